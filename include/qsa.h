@@ -1,0 +1,183 @@
+/*
+ * qsa.h -- C ABI of the packed QSA (Qwen sparse attention) decode library
+ * for AMD Instinct MI355X (gfx950).  Library: libqsa.so.
+ *
+ * The operation (page "fix(qsa): restore SM121 correctness with Humanize and
+ * Kernel Design Agent", section "Changes"): every packed row b holds exactly
+ * one bf16 query of Hq heads, head dim 256, with 12 query heads per KV head
+ * (24 Q / 2 KV, or 12 Q / 1 KV).  Row b attends over the pool rows listed in
+ * sel_indices[cu_seqlens[b] .. cu_seqlens[b+1]) -- at most 2055 entries, read
+ * in list order, a repeated slot counted every time it is listed (page
+ * "[Kernel][WIP] Integrate native FlashInfer SM70 batch GDN and QSA
+ * probes").  For Q head h, with g = h / 12:
+ *
+ *     s_j    = (q[b,h,:] . K[sel_j, g, :]) / 16
+ *     out    = sum_j softmax(s)_j * V[sel_j, g, :]          (bf16, RNE)
+ *     lse    = log(sum_j exp(s_j))                           (fp32, natural log)
+ *
+ * A zero-length row gives out = 0 and lse = -inf.
+ *
+ * Quantized pools (page "feat(qsa): quantized KV pools with dequant-on-gather
+ * (fp8/int8/int4)", part 4 "Modifications") are dequantized while the rows
+ * are gathered: element d of a row is code(d) * scale[d / group_size].
+ *
+ * Conventions for every entry point:
+ *   - Pointers inside qsa_tensor are device pointers owned by the caller.
+ *     The library never frees them and keeps none of them after returning.
+ *   - Strides are in elements of the tensor's dtype (for QSA_DTYPE_U4X2 an
+ *     element is one byte holding two codes).  The last dimension must be
+ *     contiguous (stride 1).
+ *   - Validation is done on the host from shapes/dtypes/strides only; the
+ *     host never reads device data.  A failed check returns a status and
+ *     sets the thread-local message returned by qsa_last_error().  Nothing
+ *     is launched in that case.
+ *   - A successful qsa_decode enqueues exactly one kernel on `stream` and
+ *     returns without synchronising.
+ *   - Errors that only the device can see (a row longer than 2055 or a
+ *     cu_seqlens entry outside [0, n_sel], a slot id outside [0, slots))
+ *     never fault: the offending row's out/lse are written as NaN and a bit
+ *     is set in a sticky device error word (qsa_debug_device_error).
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as in the HIP runtime headers. */
+typedef struct ihipStream_t *hipStream_t;
+
+#define QSA_ABI_VERSION 1
+#define QSA_HEAD_DIM 256
+#define QSA_GQA 12
+#define QSA_MAX_SEL 2055
+#define QSA_MAX_BS 128
+
+typedef enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_CONTRACT = 1,  /* a shape / dtype / layout outside the contract   */
+  QSA_ERR_ARG = 2,       /* a null pointer or an unknown option             */
+  QSA_ERR_WORKSPACE = 3, /* no (or too small a) workspace while capturing   */
+  QSA_ERR_HIP = 4        /* a HIP runtime call failed                       */
+} qsa_status;
+
+typedef enum qsa_dtype {
+  QSA_DTYPE_BF16 = 1,
+  QSA_DTYPE_F16 = 2,
+  QSA_DTYPE_F32 = 3,
+  QSA_DTYPE_I32 = 4,
+  QSA_DTYPE_FP8_E4M3FN = 5, /* OCP e4m3fn, one code per byte                  */
+  QSA_DTYPE_I8 = 6,         /* signed 8-bit codes                             */
+  QSA_DTYPE_U4X2 = 7        /* two 4-bit codes per byte: channel 2i in the low
+                               nibble, 2i+1 in the high nibble, value = nibble-8 */
+} qsa_dtype;
+
+/* A strided device tensor of up to 4 dimensions. */
+typedef struct qsa_tensor {
+  void *data;
+  int32_t dtype;       /* qsa_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];   /* in elements */
+} qsa_tensor;
+
+/* Scales of a quantized pool pair: k_scale / v_scale are
+ * [slots, Hkv, 256 / group_size] of QSA_DTYPE_F32.  group_size is 256 (one
+ * scale per row), 64 or 32 (int4 requires 32 or 64). */
+typedef struct qsa_kv_scales {
+  qsa_tensor k_scale;
+  qsa_tensor v_scale;
+  int32_t group_size;
+} qsa_kv_scales;
+
+/*
+ * qsa_decode -- one packed QSA decode step (one kernel launch).
+ *
+ *   q           [bs, Hq, 256] bf16.  1 <= bs <= 128; (Hq, Hkv) is (24, 2) or
+ *               (12, 1).
+ *   k_pool      [slots, Hkv, 256] bf16 | fp8_e4m3fn | i8, or
+ *               [slots, Hkv, 128] u4x2.  v_pool: same dtype and shape.
+ *               Rows must start on 16-byte boundaries.
+ *   kv_scales   NULL for bf16 pools, required for quantized pools.
+ *   sel_indices [n_sel] int32 slot ids, contiguous.  Only the entries named
+ *               by cu_seqlens are read.
+ *   cu_seqlens  [bs + 1] int32, contiguous, read on the device only: row b
+ *               is sel_indices[cu[b] .. cu[b+1]).  Changing it between graph
+ *               replays needs no host involvement.
+ *   out         [bs, Hq, 256] bf16, fully overwritten.
+ *   lse         [bs, Hq] fp32, fully overwritten.
+ *   stream      HIP stream the kernel is enqueued on (NULL = default).
+ *
+ * Uses the calling device's workspace (split partials + counters); it is
+ * created on first use outside stream capture.  Under capture a workspace
+ * reserved beforehand is required (QSA_ERR_WORKSPACE otherwise).  Calls
+ * that share a device's workspace must not run concurrently on different
+ * streams.
+ */
+qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
+                      const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
+                      const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                      qsa_tensor *out, qsa_tensor *lse, hipStream_t stream);
+
+/* Create (or grow) the current device's workspace for calls with up to
+ * max_bs rows and the given head layout, and zero its counters.  Call it
+ * before capturing a graph that contains qsa_decode.  Synchronises the
+ * device when it has to replace an existing workspace. */
+qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream);
+
+/* Re-zero the split counters and the device error word of the current
+ * device's workspace (one small kernel on `stream`). */
+qsa_status qsa_workspace_reset(hipStream_t stream);
+
+/* Free the workspaces of all devices (synchronises each device). */
+qsa_status qsa_workspace_release(void);
+
+/* Bytes of split scratch + counters the current device's workspace holds. */
+int64_t qsa_workspace_bytes(void);
+
+/* Thread-local message describing the last failed call ("" if none). */
+const char *qsa_last_error(void);
+
+/* Split plan qsa_decode uses for (bs, hkv): number of splits per (row, KV
+ * head) and the launch's workgroup count. */
+qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
+
+/* Tuning knobs (bench and tests only):
+ *   "split_target"   target workgroups per launch used to pick the split
+ *                    count (default 1024)
+ *   "max_splits"     upper bound on splits per (row, KV head) (default 16)
+ *   "min_split_keys" fewest list entries a split is given before another
+ *                    split is used (default 256)
+ * Changing them affects later launches and later reservations. */
+qsa_status qsa_set_option(const char *name, int64_t value);
+qsa_status qsa_get_option(const char *name, int64_t *value);
+
+/* Device pointer and count of the current device's split counters (uint32,
+ * zero between calls), for audits after a launch. */
+qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n);
+
+/* Copy the first n split counters of the current device to host memory
+ * (synchronises `stream`). */
+qsa_status qsa_debug_read_counters(uint32_t *host, int n, hipStream_t stream);
+
+/* Enqueue one small kernel on `stream` that adds the sum of all split
+ * counters of the current device to *dev_accum (a device uint32).  Safe to
+ * use between graph replays; *dev_accum stays 0 while every launch leaves
+ * its counters at rest. */
+qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream);
+
+/* Copy the sticky device error word to *host_word (synchronises `stream`).
+ * Bit 0: a row's cu_seqlens were out of range or longer than 2055.
+ * Bit 1: a slot id was outside [0, slots). */
+qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream);
+
+int qsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -1,0 +1,35 @@
+"""Packed QSA decode for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libqsa.so`` (built from ``csrc/`` by
+``build.py``).  Every step of the decode runs in the library's HIP kernel;
+this module only turns torch tensors into ``qsa_tensor`` descriptors and
+passes torch's current HIP stream.  If the library is missing the import of
+``decode`` fails loudly -- there is no fallback.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    ABI_VERSION,
+    QsaError,
+    abi_version,
+    debug_audit_counters,
+    debug_counters,
+    debug_device_error,
+    decode,
+    get_option,
+    lib_path,
+    load_library,
+    plan,
+    set_option,
+    workspace_bytes,
+    workspace_release,
+    workspace_reserve,
+    workspace_reset,
+)
+
+__all__ = [
+    "decode", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
+    "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
+    "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
+    "ABI_VERSION",
+]

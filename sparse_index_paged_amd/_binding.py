@@ -1,0 +1,223 @@
+"""ctypes marshalling for libqsa.so (see include/qsa.h for the contract)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libqsa.so")
+
+ABI_VERSION = 1
+
+# qsa_dtype
+BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2 = 1, 2, 3, 4, 5, 6, 7
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORKSPACE",
+          4: "QSA_ERR_HIP"}
+
+EXPORTS = (
+    "qsa_decode", "qsa_workspace_reserve", "qsa_workspace_reset", "qsa_workspace_release",
+    "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
+    "qsa_debug_counters", "qsa_debug_read_counters", "qsa_debug_audit_counters",
+    "qsa_debug_device_error", "qsa_abi_version",
+)
+
+
+class QsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class QsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class QsaKvScales(ctypes.Structure):
+    _fields_ = [("k_scale", QsaTensor), ("v_scale", QsaTensor), ("group_size", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libqsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m sparse_index_paged_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER
+    T = P(QsaTensor)
+    lib.qsa_decode.restype = ctypes.c_int
+    lib.qsa_decode.argtypes = [T, T, T, P(QsaKvScales), T, T, T, T, ctypes.c_void_p]
+    lib.qsa_workspace_reserve.restype = ctypes.c_int
+    lib.qsa_workspace_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.qsa_workspace_reset.restype = ctypes.c_int
+    lib.qsa_workspace_reset.argtypes = [ctypes.c_void_p]
+    lib.qsa_workspace_release.restype = ctypes.c_int
+    lib.qsa_workspace_release.argtypes = []
+    lib.qsa_workspace_bytes.restype = ctypes.c_int64
+    lib.qsa_workspace_bytes.argtypes = []
+    lib.qsa_last_error.restype = ctypes.c_char_p
+    lib.qsa_last_error.argtypes = []
+    lib.qsa_plan.restype = ctypes.c_int
+    lib.qsa_plan.argtypes = [ctypes.c_int, ctypes.c_int, P(ctypes.c_int), P(ctypes.c_int)]
+    lib.qsa_set_option.restype = ctypes.c_int
+    lib.qsa_set_option.argtypes = [ctypes.c_char_p, ctypes.c_int64]
+    lib.qsa_get_option.restype = ctypes.c_int
+    lib.qsa_get_option.argtypes = [ctypes.c_char_p, P(ctypes.c_int64)]
+    lib.qsa_debug_counters.restype = ctypes.c_int
+    lib.qsa_debug_counters.argtypes = [P(ctypes.c_void_p), P(ctypes.c_int)]
+    lib.qsa_debug_read_counters.restype = ctypes.c_int
+    lib.qsa_debug_read_counters.argtypes = [P(ctypes.c_uint32), ctypes.c_int, ctypes.c_void_p]
+    lib.qsa_debug_audit_counters.restype = ctypes.c_int
+    lib.qsa_debug_audit_counters.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.qsa_debug_device_error.restype = ctypes.c_int
+    lib.qsa_debug_device_error.argtypes = [P(ctypes.c_uint32), ctypes.c_void_p]
+    lib.qsa_abi_version.restype = ctypes.c_int
+    lib.qsa_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().qsa_last_error().decode()
+        raise QsaError(status, msg)
+
+
+def _torch_dtype_code(t, kv_format: str | None = None) -> int:
+    import torch
+    if kv_format is not None:
+        return {"bf16": BF16, "fp8": FP8_E4M3FN, "int8": I8, "int4": U4X2}[kv_format]
+    m = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32,
+         torch.int8: I8}
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    if fp8 is not None:
+        m[fp8] = FP8_E4M3FN
+    if t.dtype not in m:
+        raise TypeError(f"no qsa dtype for {t.dtype}")
+    return m[t.dtype]
+
+
+def describe(t, kv_format: str | None = None, dtype_code: int | None = None) -> QsaTensor:
+    """qsa_tensor for a torch tensor (strides in elements)."""
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = QsaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else (t.data_ptr() or 16)
+    d.dtype = dtype_code if dtype_code is not None else _torch_dtype_code(t, kv_format)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode(q, k_pool, v_pool, sel, cu_seqlens, *, out=None, lse=None, kv_format: str = "bf16",
+           k_scale=None, v_scale=None, group_size: int | None = None, stream=None):
+    """Packed QSA decode (one kernel launch on `stream`, default torch's
+    current stream).  Returns (out [bs, Hq, 256] bf16, lse [bs, Hq] fp32).
+
+    kv_format: "bf16" | "fp8" (e4m3fn bytes, torch.uint8 or float8_e4m3fn)
+    | "int8" (torch.int8) | "int4" (torch.uint8 [slots, Hkv, 128]).
+    Quantized formats take k_scale / v_scale [slots, Hkv, 256 // group_size]
+    float32."""
+    import torch
+    lib = load_library()
+    bs, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((bs, hq, 256), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((bs, hq), dtype=torch.float32, device=q.device)
+    qd, od, ld = describe(q), describe(out), describe(lse)
+    kd = describe(k_pool, kv_format)
+    vd = describe(v_pool, kv_format)
+    sd, cd = describe(sel), describe(cu_seqlens)
+    scales = None
+    if kv_format != "bf16":
+        if k_scale is None or v_scale is None:
+            raise ValueError(f"{kv_format} pools need k_scale and v_scale")
+        g = group_size if group_size is not None else 256 // k_scale.shape[-1]
+        scales = QsaKvScales(describe(k_scale), describe(v_scale), g)
+    st = lib.qsa_decode(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                        ctypes.byref(scales) if scales is not None else None,
+                        ctypes.byref(sd), ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
+                        _stream_handle(stream))
+    _check(st)
+    return out, lse
+
+
+def workspace_reserve(max_bs: int, hq: int, hkv: int, stream=None):
+    _check(load_library().qsa_workspace_reserve(max_bs, hq, hkv, _stream_handle(stream)))
+
+
+def workspace_reset(stream=None):
+    _check(load_library().qsa_workspace_reset(_stream_handle(stream)))
+
+
+def workspace_release():
+    _check(load_library().qsa_workspace_release())
+
+
+def workspace_bytes() -> int:
+    return int(load_library().qsa_workspace_bytes())
+
+
+def plan(bs: int, hkv: int) -> tuple[int, int]:
+    s, w = ctypes.c_int(), ctypes.c_int()
+    _check(load_library().qsa_plan(bs, hkv, ctypes.byref(s), ctypes.byref(w)))
+    return s.value, w.value
+
+
+def set_option(name: str, value: int):
+    _check(load_library().qsa_set_option(name.encode(), int(value)))
+
+
+def get_option(name: str) -> int:
+    v = ctypes.c_int64()
+    _check(load_library().qsa_get_option(name.encode(), ctypes.byref(v)))
+    return v.value
+
+
+def debug_counters(stream=None) -> list[int]:
+    """Current values of the device's split counters (synchronises); they
+    read zero between calls."""
+    ptr, n = ctypes.c_void_p(), ctypes.c_int()
+    lib = load_library()
+    _check(lib.qsa_debug_counters(ctypes.byref(ptr), ctypes.byref(n)))
+    buf = (ctypes.c_uint32 * n.value)()
+    _check(lib.qsa_debug_read_counters(buf, n.value, _stream_handle(stream)))
+    return list(buf)
+
+
+def debug_audit_counters(accum, stream=None):
+    """Enqueue: accum[0] += sum(counters).  accum is a 1-element int32 /
+    uint32 device tensor."""
+    _check(load_library().qsa_debug_audit_counters(ctypes.c_void_p(accum.data_ptr()),
+                                                   _stream_handle(stream)))
+
+
+def debug_device_error(stream=None) -> int:
+    w = ctypes.c_uint32()
+    _check(load_library().qsa_debug_device_error(ctypes.byref(w), _stream_handle(stream)))
+    return w.value
+
+
+def abi_version() -> int:
+    return int(load_library().qsa_abi_version())

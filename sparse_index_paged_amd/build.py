@@ -1,0 +1,48 @@
+"""Build libqsa.so (HIP, gfx950 only) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, "qsa_decode.hip"), os.path.join(CSRC, "qsa_api.hip")]
+LIB = os.path.join(PKG, "libqsa.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++20",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # no packed-fp32 VALU forms anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libqsa.so")
+    # hipcc's host pass does not know the packed-fp32 feature; that warning
+    # is expected, anything else is shown
+    noise = [ln for ln in res.stderr.splitlines()
+             if ln.strip() and "packed-fp32-ops" not in ln and "warning generated" not in ln]
+    if verbose and noise:
+        sys.stderr.write("\n".join(noise) + "\n")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

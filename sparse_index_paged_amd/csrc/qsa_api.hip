@@ -1,0 +1,471 @@
+// qsa_api.hip -- host side of libqsa.so: contract validation, split plan,
+// per-device workspace and the single launch of qsa_decode.
+//
+// The contract (page "fix(qsa): restore SM121 correctness with Humanize and
+// Kernel Design Agent", sections "Changes" and the integration update): bf16,
+// head dim 256, 12:1 GQA as 24 Q / 2 KV or 12 Q / 1 KV heads, one query per
+// row, 1 <= bs <= 128, at most 2055 selected entries per row; calls outside
+// it fail with a descriptive error and nothing is launched.  Lengths are only
+// read on the device, so a captured graph replays correctly when cu_seqlens
+// changes.  Counters are kept across calls and are zero at rest.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qsa_status fail(qsa_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+qsa_status fail(qsa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+qsa_status ok() {
+  g_last_error.clear();
+  return QSA_OK;
+}
+
+// ---- options ---------------------------------------------------------------
+std::atomic<int64_t> g_split_target{1024};
+std::atomic<int64_t> g_max_splits{16};
+std::atomic<int64_t> g_min_split_keys{256};
+
+int plan_splits(int bs, int hkv) {
+  const int64_t npairs8 = ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8;
+  int64_t s = (g_split_target.load() + npairs8 - 1) / npairs8;
+  const int64_t smax = g_max_splits.load();
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+int64_t plan_workgroups(int bs, int hkv, int splits) {
+  return ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8 * splits;
+}
+
+// ---- workspace -------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+
+struct Workspace {
+  float *part = nullptr;
+  int64_t part_floats = 0;
+  uint32_t *words = nullptr;  // [kMaxBs * 2 counters][1 error word]
+  int64_t n_ctr = 0;
+};
+
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxDevices];
+
+constexpr int64_t kCtrWords = static_cast<int64_t>(qsa::kMaxBs) * 2;
+
+int64_t part_floats_needed(int max_bs, int hkv) {
+  int64_t worst = 0;
+  for (int bs = 1; bs <= max_bs; ++bs) {
+    const int64_t n = static_cast<int64_t>(bs) * hkv * plan_splits(bs, hkv);
+    if (n > worst) worst = n;
+  }
+  return worst * qsa::kPartFloats;
+}
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// Ensure the current device's workspace holds `floats` partial floats.
+qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
+                            Workspace **out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace &ws = g_ws[dev];
+  if (ws.words != nullptr && ws.part_floats >= floats) {
+    *out = &ws;
+    return QSA_OK;
+  }
+  if (!allow_alloc)
+    return fail(QSA_ERR_WORKSPACE,
+                "qsa_decode: the stream is capturing and the device %d workspace holds %lld "
+                "partial floats, %lld needed; call qsa_workspace_reserve before capture",
+                dev, static_cast<long long>(ws.part_floats), static_cast<long long>(floats));
+  if (ws.words != nullptr) {
+    if (hipDeviceSynchronize() != hipSuccess)
+      return fail(QSA_ERR_HIP, "workspace: hipDeviceSynchronize failed");
+    (void)hipFree(ws.part);
+    (void)hipFree(ws.words);
+    ws = Workspace{};
+  }
+  void *part = nullptr, *words = nullptr;
+  if (hipMalloc(&part, static_cast<size_t>(floats) * sizeof(float)) != hipSuccess)
+    return fail(QSA_ERR_HIP, "workspace: hipMalloc of %lld bytes failed",
+                static_cast<long long>(floats * 4));
+  if (hipMalloc(&words, static_cast<size_t>(kCtrWords + 1) * sizeof(uint32_t)) != hipSuccess) {
+    (void)hipFree(part);
+    return fail(QSA_ERR_HIP, "workspace: hipMalloc of the counters failed");
+  }
+  ws.part = static_cast<float *>(part);
+  ws.part_floats = floats;
+  ws.words = static_cast<uint32_t *>(words);
+  ws.n_ctr = kCtrWords;
+  if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "workspace: zeroing the counters failed");
+  *out = &ws;
+  return QSA_OK;
+}
+
+// ---- descriptor checks -----------------------------------------------------
+const char *dtype_name(int32_t dt) {
+  switch (dt) {
+    case QSA_DTYPE_BF16: return "bf16";
+    case QSA_DTYPE_F16: return "f16";
+    case QSA_DTYPE_F32: return "f32";
+    case QSA_DTYPE_I32: return "i32";
+    case QSA_DTYPE_FP8_E4M3FN: return "fp8_e4m3fn";
+    case QSA_DTYPE_I8: return "i8";
+    case QSA_DTYPE_U4X2: return "u4x2";
+    default: return "unknown";
+  }
+}
+
+int64_t dtype_bytes(int32_t dt) {
+  switch (dt) {
+    case QSA_DTYPE_BF16:
+    case QSA_DTYPE_F16: return 2;
+    case QSA_DTYPE_F32:
+    case QSA_DTYPE_I32: return 4;
+    case QSA_DTYPE_FP8_E4M3FN:
+    case QSA_DTYPE_I8:
+    case QSA_DTYPE_U4X2: return 1;
+    default: return 0;
+  }
+}
+
+qsa_status check_tensor(const qsa_tensor *t, const char *name, int32_t dtype, int ndim) {
+  if (t == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s is NULL", name);
+  if (t->data == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s.data is NULL", name);
+  if (t->dtype != dtype)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must be %s, got %s", name, dtype_name(dtype),
+                dtype_name(t->dtype));
+  if (t->ndim != ndim)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must have %d dimensions, got %d", name, ndim,
+                t->ndim);
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.shape[%d] < 0", name, i);
+    if (t->stride[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.stride[%d] < 0", name, i);
+  }
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must be contiguous in its last dimension", name);
+  return QSA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_last_error(void) { return g_last_error.c_str(); }
+
+qsa_status qsa_set_option(const char *name, int64_t value) {
+  if (name == nullptr) return fail(QSA_ERR_ARG, "qsa_set_option: name is NULL");
+  if (value < 1) return fail(QSA_ERR_ARG, "qsa_set_option: %s must be >= 1", name);
+  if (!strcmp(name, "split_target")) {
+    g_split_target = value;
+  } else if (!strcmp(name, "max_splits")) {
+    if (value > 64) return fail(QSA_ERR_ARG, "qsa_set_option: max_splits must be <= 64");
+    g_max_splits = value;
+  } else if (!strcmp(name, "min_split_keys")) {
+    g_min_split_keys = value;
+  } else {
+    return fail(QSA_ERR_ARG, "qsa_set_option: unknown option '%s'", name);
+  }
+  return ok();
+}
+
+qsa_status qsa_get_option(const char *name, int64_t *value) {
+  if (name == nullptr || value == nullptr) return fail(QSA_ERR_ARG, "qsa_get_option: NULL argument");
+  if (!strcmp(name, "split_target")) *value = g_split_target;
+  else if (!strcmp(name, "max_splits")) *value = g_max_splits;
+  else if (!strcmp(name, "min_split_keys")) *value = g_min_split_keys;
+  else return fail(QSA_ERR_ARG, "qsa_get_option: unknown option '%s'", name);
+  return ok();
+}
+
+qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups) {
+  if (bs < 1 || bs > QSA_MAX_BS) return fail(QSA_ERR_CONTRACT, "qsa_plan: bs must be in [1, 128]");
+  if (hkv != 1 && hkv != 2) return fail(QSA_ERR_CONTRACT, "qsa_plan: Hkv must be 1 or 2");
+  const int s = plan_splits(bs, hkv);
+  if (splits) *splits = s;
+  if (workgroups) *workgroups = static_cast<int>(plan_workgroups(bs, hkv, s));
+  return ok();
+}
+
+qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_tensor *v_pool,
+                      const qsa_kv_scales *kv_scales, const qsa_tensor *sel_indices,
+                      const qsa_tensor *cu_seqlens, qsa_tensor *out, qsa_tensor *lse,
+                      hipStream_t stream) {
+  qsa_status st;
+  // -- query / outputs
+  if ((st = check_tensor(q, "q", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
+  const int64_t bs = q->shape[0], hq = q->shape[1];
+  if (q->shape[2] != QSA_HEAD_DIM)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: head dim must be 256, q.shape[2] = %lld",
+                static_cast<long long>(q->shape[2]));
+  if (bs < 1 || bs > QSA_MAX_BS)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: bs must be in [1, 128], got %lld",
+                static_cast<long long>(bs));
+  if (k_pool == nullptr || v_pool == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: a pool is NULL");
+  const int32_t pdt = k_pool->dtype;
+  if (pdt != QSA_DTYPE_BF16 && pdt != QSA_DTYPE_FP8_E4M3FN && pdt != QSA_DTYPE_I8 &&
+      pdt != QSA_DTYPE_U4X2)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool dtype %s is not bf16, fp8_e4m3fn, i8 or u4x2",
+                dtype_name(pdt));
+  if (v_pool->dtype != pdt)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool (%s) and v_pool (%s) must share a format",
+                dtype_name(pdt), dtype_name(v_pool->dtype));
+  if ((st = check_tensor(k_pool, "k_pool", pdt, 3)) != QSA_OK) return st;
+  if ((st = check_tensor(v_pool, "v_pool", pdt, 3)) != QSA_OK) return st;
+  const int64_t slots = k_pool->shape[0], hkv = k_pool->shape[1];
+  const int64_t row_elems = (pdt == QSA_DTYPE_U4X2) ? QSA_HEAD_DIM / 2 : QSA_HEAD_DIM;
+  if (!((hq == 24 && hkv == 2) || (hq == 12 && hkv == 1)))
+    return fail(QSA_ERR_CONTRACT,
+                "qsa_decode: (Hq, Hkv) must be (24, 2) or (12, 1) (12:1 GQA), got (%lld, %lld)",
+                static_cast<long long>(hq), static_cast<long long>(hkv));
+  if (k_pool->shape[2] != row_elems || v_pool->shape[2] != row_elems)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: pool rows must hold %lld %s elements (head dim 256)",
+                static_cast<long long>(row_elems), dtype_name(pdt));
+  if (v_pool->shape[0] != slots || v_pool->shape[1] != hkv)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool and v_pool shapes differ");
+  if (slots < 1) return fail(QSA_ERR_CONTRACT, "qsa_decode: the pools hold no slots");
+  if (slots > 0x7FFFFFFFLL)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: more than 2^31-1 slots cannot be named by int32 ids");
+  const int64_t eb = dtype_bytes(pdt);
+  if (!aligned16(k_pool->data) || !aligned16(v_pool->data) || (k_pool->stride[0] * eb) % 16 ||
+      (k_pool->stride[1] * eb) % 16 || (v_pool->stride[0] * eb) % 16 || (v_pool->stride[1] * eb) % 16)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: pool rows must start on 16-byte boundaries");
+  if (!aligned16(q->data) || q->stride[0] % 8 || q->stride[1] % 8)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: q rows must start on 16-byte boundaries");
+
+  if ((st = check_tensor(out, "out", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
+  if (out->shape[0] != bs || out->shape[1] != hq || out->shape[2] != QSA_HEAD_DIM)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: out must be [bs, Hq, 256] like q");
+  if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2)) != QSA_OK) return st;
+  if (lse->shape[0] != bs || lse->shape[1] != hq)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: lse must be [bs, Hq]");
+
+  // -- index lists
+  if ((st = check_tensor(sel_indices, "sel_indices", QSA_DTYPE_I32, 1)) != QSA_OK) return st;
+  if ((st = check_tensor(cu_seqlens, "cu_seqlens", QSA_DTYPE_I32, 1)) != QSA_OK) return st;
+  if (cu_seqlens->shape[0] != bs + 1)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: cu_seqlens must have bs + 1 = %lld entries, got %lld",
+                static_cast<long long>(bs + 1), static_cast<long long>(cu_seqlens->shape[0]));
+
+  // -- scales
+  int fmt = qsa::kFmtBF16, group = QSA_HEAD_DIM;
+  const float *ks = nullptr, *vs = nullptr;
+  int64_t ks_ss = 0, ks_sh = 0, vs_ss = 0, vs_sh = 0;
+  if (pdt == QSA_DTYPE_BF16) {
+    if (kv_scales != nullptr)
+      return fail(QSA_ERR_CONTRACT, "qsa_decode: bf16 pools take no scales (kv_scales must be NULL)");
+  } else {
+    fmt = pdt == QSA_DTYPE_FP8_E4M3FN ? qsa::kFmtFP8 : pdt == QSA_DTYPE_I8 ? qsa::kFmtINT8 : qsa::kFmtINT4;
+    if (kv_scales == nullptr)
+      return fail(QSA_ERR_CONTRACT, "qsa_decode: %s pools need kv_scales", dtype_name(pdt));
+    group = kv_scales->group_size;
+    const bool g_ok = (fmt == qsa::kFmtINT4) ? (group == 32 || group == 64)
+                                             : (group == 32 || group == 64 || group == 256);
+    if (!g_ok)
+      return fail(QSA_ERR_CONTRACT, "qsa_decode: group_size %d is not supported for %s pools "
+                  "(fp8/i8: 32, 64, 256; u4x2: 32, 64)", group, dtype_name(pdt));
+    const int64_t ng = QSA_HEAD_DIM / group;
+    if ((st = check_tensor(&kv_scales->k_scale, "k_scale", QSA_DTYPE_F32, 3)) != QSA_OK) return st;
+    if ((st = check_tensor(&kv_scales->v_scale, "v_scale", QSA_DTYPE_F32, 3)) != QSA_OK) return st;
+    for (const qsa_tensor *t : {&kv_scales->k_scale, &kv_scales->v_scale})
+      if (t->shape[0] != slots || t->shape[1] != hkv || t->shape[2] != ng)
+        return fail(QSA_ERR_CONTRACT, "qsa_decode: scales must be [slots, Hkv, 256/group] = "
+                    "[%lld, %lld, %lld]", static_cast<long long>(slots),
+                    static_cast<long long>(hkv), static_cast<long long>(ng));
+    ks = static_cast<const float *>(kv_scales->k_scale.data);
+    vs = static_cast<const float *>(kv_scales->v_scale.data);
+    ks_ss = kv_scales->k_scale.stride[0];
+    ks_sh = kv_scales->k_scale.stride[1];
+    vs_ss = kv_scales->v_scale.stride[0];
+    vs_sh = kv_scales->v_scale.stride[1];
+  }
+
+  // -- device, workspace, launch
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "qsa_decode: no HIP device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "qsa_decode: device id out of range");
+  const int splits = plan_splits(static_cast<int>(bs), static_cast<int>(hkv));
+  const int64_t need = bs * hkv * splits * static_cast<int64_t>(qsa::kPartFloats);
+  Workspace *ws = nullptr;
+  if ((st = ensure_workspace(dev, need, stream, !stream_capturing(stream), &ws)) != QSA_OK) return st;
+
+  qsa::Params p{};
+  p.q = static_cast<const __bf16 *>(q->data);
+  p.q_sb = q->stride[0];
+  p.q_sh = q->stride[1];
+  p.k = static_cast<const uint8_t *>(k_pool->data);
+  p.v = static_cast<const uint8_t *>(v_pool->data);
+  p.k_ss = k_pool->stride[0] * eb;
+  p.k_sh = k_pool->stride[1] * eb;
+  p.v_ss = v_pool->stride[0] * eb;
+  p.v_sh = v_pool->stride[1] * eb;
+  p.ks = ks;
+  p.vs = vs;
+  p.ks_ss = ks_ss;
+  p.ks_sh = ks_sh;
+  p.vs_ss = vs_ss;
+  p.vs_sh = vs_sh;
+  p.sel = static_cast<const int32_t *>(sel_indices->data);
+  p.n_sel = sel_indices->shape[0];
+  p.cu = static_cast<const int32_t *>(cu_seqlens->data);
+  p.out = static_cast<__bf16 *>(out->data);
+  p.o_sb = out->stride[0];
+  p.o_sh = out->stride[1];
+  p.lse = static_cast<float *>(lse->data);
+  p.l_sb = lse->stride[0];
+  p.l_sh = lse->stride[1];
+  p.slots = slots;
+  p.bs = static_cast<int>(bs);
+  p.hkv = static_cast<int>(hkv);
+  p.nsplit = splits;
+  p.min_split_keys = static_cast<int>(g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load());
+  p.part = ws->part;
+  p.ctr = ws->words;
+  p.err = ws->words + kCtrWords;
+  const hipError_t e = qsa::launch_decode(p, fmt, group, stream);
+  if (e != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_decode: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream) {
+  if (max_bs < 1 || max_bs > QSA_MAX_BS)
+    return fail(QSA_ERR_CONTRACT, "qsa_workspace_reserve: max_bs must be in [1, 128]");
+  if (!((hq == 24 && hkv == 2) || (hq == 12 && hkv == 1)))
+    return fail(QSA_ERR_CONTRACT, "qsa_workspace_reserve: (Hq, Hkv) must be (24, 2) or (12, 1)");
+  if (stream_capturing(stream))
+    return fail(QSA_ERR_WORKSPACE, "qsa_workspace_reserve: called while the stream is capturing");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "qsa_workspace_reserve: no HIP device");
+  Workspace *ws = nullptr;
+  qsa_status st = ensure_workspace(dev, part_floats_needed(max_bs, hkv), stream, true, &ws);
+  if (st != QSA_OK) return st;
+  if (qsa::launch_fill_u32(ws->words, kCtrWords + 1, 0u, stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_workspace_reserve: zeroing the counters failed");
+  return ok();
+}
+
+qsa_status qsa_workspace_reset(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "qsa_workspace_reset: no HIP device");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace &ws = g_ws[dev];
+  if (ws.words == nullptr) return ok();
+  if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_workspace_reset: zeroing the counters failed");
+  return ok();
+}
+
+qsa_status qsa_workspace_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = -1;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    Workspace &ws = g_ws[dev];
+    if (ws.words == nullptr) continue;
+    if (hipSetDevice(dev) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
+      (void)hipFree(ws.part);
+      (void)hipFree(ws.words);
+    }
+    ws = Workspace{};
+  }
+  if (cur >= 0) (void)hipSetDevice(cur);
+  return ok();
+}
+
+int64_t qsa_workspace_bytes(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const Workspace &ws = g_ws[dev];
+  if (ws.words == nullptr) return 0;
+  return ws.part_floats * 4 + (kCtrWords + 1) * 4;
+}
+
+qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n) {
+  if (dev_ptr == nullptr || n == nullptr) return fail(QSA_ERR_ARG, "qsa_debug_counters: NULL argument");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "qsa_debug_counters: no HIP device");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const Workspace &ws = g_ws[dev];
+  if (ws.words == nullptr) return fail(QSA_ERR_WORKSPACE, "qsa_debug_counters: no workspace yet");
+  *dev_ptr = ws.words;
+  *n = static_cast<int>(ws.n_ctr);
+  return ok();
+}
+
+qsa_status qsa_debug_read_counters(uint32_t *host, int n, hipStream_t stream) {
+  const uint32_t *ctr = nullptr;
+  int total = 0;
+  qsa_status st = qsa_debug_counters(&ctr, &total);
+  if (st != QSA_OK) return st;
+  if (host == nullptr || n < 0 || n > total)
+    return fail(QSA_ERR_ARG, "qsa_debug_read_counters: n must be in [0, %d]", total);
+  if (hipMemcpyAsync(host, ctr, sizeof(uint32_t) * n, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_debug_read_counters: copy failed");
+  return ok();
+}
+
+qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream) {
+  const uint32_t *ctr = nullptr;
+  int total = 0;
+  qsa_status st = qsa_debug_counters(&ctr, &total);
+  if (st != QSA_OK) return st;
+  if (dev_accum == nullptr) return fail(QSA_ERR_ARG, "qsa_debug_audit_counters: NULL accumulator");
+  if (qsa::launch_audit(ctr, total, dev_accum, stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_debug_audit_counters: launch failed");
+  return ok();
+}
+
+qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream) {
+  if (host_word == nullptr) return fail(QSA_ERR_ARG, "qsa_debug_device_error: NULL argument");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "qsa_debug_device_error: no HIP device");
+  uint32_t *word = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (g_ws[dev].words == nullptr) {
+      *host_word = 0;
+      return ok();
+    }
+    word = g_ws[dev].words + kCtrWords;
+  }
+  if (hipMemcpyAsync(host_word, word, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(QSA_ERR_HIP, "qsa_debug_device_error: copy failed");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,596 @@
+// qsa_decode.hip -- packed QSA decode kernel for gfx950 (MI355X).
+//
+// What it computes is stated in include/qsa.h.  The design follows the
+// page "fix(qsa): restore SM121 correctness with Humanize and Kernel Design
+// Agent", section "Optimized kernel": the 12 Q heads that share a KV head
+// live in one workgroup so every gathered K/V row is read once for all of
+// them; QK and PV run as bf16 matrix products with fp32 online-softmax state;
+// long lists are split across workgroups, and the last split to finish merges
+// the fp32 partials in a fixed order and resets its counter in the same
+// launch.  Dequantization of fp8 / int8 / int4 pools happens in the gather
+// itself (page "feat(qsa): quantized KV pools with dequant-on-gather
+// (fp8/int8/int4)", part 4 "Motivation").
+//
+// Mapping onto CDNA4:
+//   * workgroup = 4 waves = one (row b, KV head g, split s).  Each wave owns
+//     a contiguous slice of the list and runs its own online softmax over
+//     16-entry tiles; the 4 wave states are merged through LDS at the end.
+//   * QK as S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: the A operand is 16
+//     K rows, loaded by each lane straight from the pool (row = lane % 16,
+//     8 channels per lane per MFMA), the B operand is Q (heads 12..15 zero).
+//     The result holds, in lane l, head l % 16 for list entries
+//     4*(l/16) + 0..3 -- exactly the B-operand layout of the PV product, so
+//     P never moves between lanes.
+//   * PV as O^T = V^T . P^T with v_mfma_f32_16x16x16_bf16: V^T needs the
+//     transpose of the gathered rows, so the V tile goes through a
+//     wave-private, XOR-swizzled LDS tile.  The accumulator O^T keeps head
+//     l % 16 in lane l, the same lane that owns that head's running max and
+//     sum, so the rescale by exp(m_old - m_new) needs no shuffle.
+//   * P enters the PV product as a hi + lo bf16 pair (two MFMAs), so the
+//     product sees P to ~16 bits instead of bf16's 8.  Quantized codes are
+//     converted exactly to bf16; their fp32 scales are applied outside the
+//     MFMA (K scales on the QK partial of each channel group, V scales folded
+//     into P).
+//   * All splits of one (row, KV head) are given workgroup ids congruent mod
+//     8, so they are dispatched to the same XCD and their partials stay in
+//     one L2.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kScaleLog2 = kLog2e / 16.0f;  // softmax scale 1/16 in log2 units
+
+// ---- per-format gather geometry --------------------------------------------
+// A lane loads, for each of the 8 QK MFMAs kk, the 8 channels
+// 32*kk + 8*(lane/16) .. +7 of its row.  Raw is the storage of those 8 codes.
+template <int FMT> struct Fmt;
+template <> struct Fmt<kFmtBF16> { using Raw = uint4;    static constexpr int kElemBits = 16; };
+template <> struct Fmt<kFmtFP8>  { using Raw = uint2;    static constexpr int kElemBits = 8; };
+template <> struct Fmt<kFmtINT8> { using Raw = uint2;    static constexpr int kElemBits = 8; };
+template <> struct Fmt<kFmtINT4> { using Raw = uint32_t; static constexpr int kElemBits = 4; };
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// OCP e4m3fn byte -> bf16 bits (exact: every e4m3fn value is a bf16 value).
+__device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t c) {
+  const uint32_t sign = (c & 0x80u) << 8;
+  const uint32_t em = c & 0x7Fu;
+  const uint32_t e = em >> 3, m = em & 7u;
+  uint32_t mag;
+  if (e != 0u)
+    mag = ((e + 120u) << 7) | (m << 4);                       // 2^(e-7) (1 + m/8)
+  else
+    mag = __float_as_uint(static_cast<float>(m) * 0x1p-9f) >> 16;  // m 2^-9
+  if (em == 0x7Fu) mag = 0x7FC0u;                             // S.1111.111 = NaN
+  return sign | mag;
+}
+
+__device__ __forceinline__ uint32_t int_to_bf16(int x) {
+  return __float_as_uint(static_cast<float>(x)) >> 16;  // exact for |x| <= 256
+}
+
+// 8 codes -> 8 bf16 values packed in a uint4 (element e in half e%2 of word e/2)
+template <int FMT> __device__ __forceinline__ uint4 to_bf16x8(typename Fmt<FMT>::Raw r);
+
+template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtBF16>(uint4 r) { return r; }
+
+template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtFP8>(uint2 r) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t src = (i < 2) ? r.x : r.y;
+    const int sh = (i & 1) * 16;
+    w[i] = fp8_to_bf16((src >> sh) & 0xFFu) | (fp8_to_bf16((src >> (sh + 8)) & 0xFFu) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT8>(uint2 r) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t src = (i < 2) ? r.x : r.y;
+    const int sh = (i & 1) * 16;
+    const int a = static_cast<int8_t>((src >> sh) & 0xFFu);
+    const int b = static_cast<int8_t>((src >> (sh + 8)) & 0xFFu);
+    w[i] = int_to_bf16(a) | (int_to_bf16(b) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT4>(uint32_t r) {
+  // byte i holds channel 2i (low nibble) and 2i+1 (high nibble), code = nibble - 8
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lo = static_cast<int>((r >> (8 * i)) & 0xFu) - 8;
+    const int hi = static_cast<int>((r >> (8 * i + 4)) & 0xFu) - 8;
+    w[i] = int_to_bf16(lo) | (int_to_bf16(hi) << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// LDS rows of the V and Q tiles are padded from 512 to 528 bytes: the
+// 16-byte row-wise writes of 8 consecutive rows then fall into 8 different
+// bank groups, and every LDS address stays base + immediate.
+constexpr int kLdsRow = kHeadDim * 2 + 16;
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS: during the loop each wave owns a V tile [16][512 B] plus its scales;
+// afterwards the region is reused to merge the four wave states.
+constexpr int kVTileBytes = kTile * kLdsRow;
+constexpr int kScaleFloats = kTile * 8;  // up to 8 groups per row
+constexpr int kWaveLdsBytes = kVTileBytes + 2 * kScaleFloats * 4;
+constexpr int kLoopLdsBytes = kWaves * kWaveLdsBytes;
+constexpr int kQLdsBytes = 16 * kLdsRow;
+constexpr int kMergeLdsBytes = (2 * kWaves * 16 + kWaves * kGqa * kHeadDim) * 4;
+constexpr int kLdsBytes = (kLoopLdsBytes + kQLdsBytes) > kMergeLdsBytes ? (kLoopLdsBytes + kQLdsBytes)
+                                                                        : kMergeLdsBytes;
+
+__device__ void write_nan_rows(const Params &p, int b, int g, int tid) {
+  const __bf16 nan = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x7FC0u));
+  for (int h = 0; h < kGqa; ++h)
+    p.out[b * p.o_sb + (g * kGqa + h) * p.o_sh + tid] = nan;
+  if (tid < kGqa) p.lse[b * p.l_sb + (g * kGqa + tid) * p.l_sh] = __builtin_nanf("");
+}
+
+template <int FMT, int G>
+__global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p) {
+  using Raw = typename Fmt<FMT>::Raw;
+  constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
+  constexpr int NGL = (NG == 0) ? 0 : (NG >= 4 ? NG / 4 : 1); // scale loads per lane
+  constexpr int kChunkBytes = 8 * Fmt<FMT>::kElemBits / 8;    // bytes of 8 codes
+
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;  // load row / head
+  const int qg = lane >> 4;   // lane group 0..3
+
+  // ---- workgroup -> (pair, split); splits of a pair share blockIdx % 8
+  const int npairs = p.bs * p.hkv;
+  const int wg = blockIdx.x;
+  const int local = wg >> 3;
+  const int pp = local / p.nsplit;
+  const int split = local - pp * p.nsplit;
+  const int pair = pp * 8 + (wg & 7);
+  if (pair >= npairs) return;
+  const int b = pair / p.hkv;
+  const int g = pair - b * p.hkv;
+
+  // ---- live row length from device cu_seqlens
+  const int c0 = p.cu[b];
+  const int c1 = p.cu[b + 1];
+  const int L = c1 - c0;
+  if (c0 < 0 || L < 0 || L > kMaxSel || static_cast<int64_t>(c1) > p.n_sel) {
+    if (split == 0) {
+      write_nan_rows(p, b, g, tid);
+      if (tid == 0) atomicOr(p.err, kErrRowRange);
+    }
+    return;
+  }
+  int n_active = (L + p.min_split_keys - 1) / p.min_split_keys;
+  n_active = n_active < 1 ? 1 : (n_active > p.nsplit ? p.nsplit : n_active);
+  if (split >= n_active) return;
+
+  // ---- this wave's contiguous slice of the list
+  const int nw = n_active * kWaves;
+  const int wi = split * kWaves + wave;
+  const int k0 = (L * wi) / nw;
+  const int nkeys = (L * (wi + 1)) / nw - k0;
+  const int ntile = (nkeys + kTile - 1) / kTile;
+
+  // ---- Q of the 12 heads of KV head g -> LDS [16 heads][528 B] (heads
+  // 12..15 zero); each QK MFMA reads its B operand from there.
+  unsigned char *qlds = smem + kLoopLdsBytes;
+  {
+    const int h = tid >> 4;        // 16 threads per head, 2 chunks each
+    const int c = (tid & 15) * 2;
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+    if (h < kGqa) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + (g * kGqa + h) * p.q_sh) + c;
+      v0 = src[0];
+      v1 = src[1];
+    }
+    *reinterpret_cast<uint4 *>(qlds + h * kLdsRow + c * 16) = v0;
+    *reinterpret_cast<uint4 *>(qlds + h * kLdsRow + c * 16 + 16) = v1;
+  }
+  __syncthreads();
+  auto qfrag = [&](int kk) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
+  };
+
+  unsigned char *wlds = smem + wave * kWaveLdsBytes;
+  unsigned char *vt = wlds;                                          // [16][528 B]
+  float *ksc = reinterpret_cast<float *>(wlds + kVTileBytes);        // [16][NG]
+  float *vsc = ksc + kScaleFloats;                                   // [16][NG]
+
+  const uint8_t *kbase = p.k + g * p.k_sh + (kChunkBytes * qg);
+  const uint8_t *vbase = p.v + g * p.v_sh + (kChunkBytes * qg);
+  const float *ksbase = (NG > 0) ? p.ks + g * p.ks_sh : nullptr;
+  const float *vsbase = (NG > 0) ? p.vs + g * p.vs_sh : nullptr;
+  const int32_t *selw = p.sel + c0 + k0;
+  const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
+
+  // per-lane online-softmax state for head r16 (replicated over lane groups)
+  float m_run = -INFINITY;
+  float l_run = 0.0f;  // partial sum over this lane's 4 entries per tile
+  f32x4 acc[16];
+#pragma unroll
+  for (int mt = 0; mt < 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad_slot = false;
+
+  // LDS read offsets of the transposed V operand: entry j = 4*qg + e,
+  // channel 16*mt + r16 at byte j*528 + 2*(16*mt + r16).
+  const unsigned char *vcol = vt + (4 * qg) * kLdsRow + 2 * r16;
+
+  // K rows of the current and the next tile stay in registers (QK reads
+  // them there); the V rows and scales of the next tile share one register
+  // set that is emptied into LDS at the start of each step.
+  Raw kraw[2][8], vraw[8];
+  float ksr[NGL > 0 ? NGL : 1], vsr[NGL > 0 ? NGL : 1];
+
+  auto fetch_slot = [&](int t) -> int32_t {
+    int j = kTile * t + r16;
+    j = j < nkeys ? j : nkeys - 1;
+    return selw[j];
+  };
+  auto checked = [&](int32_t s) -> uint32_t {
+    if (static_cast<uint32_t>(s) >= slots) { bad_slot = true; return 0u; }
+    return static_cast<uint32_t>(s);
+  };
+  auto issue = [&](int kbuf, uint32_t slot) {
+    const uint8_t *kp = kbase + static_cast<int64_t>(slot) * p.k_ss;
+    const uint8_t *vp = vbase + static_cast<int64_t>(slot) * p.v_ss;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      kraw[kbuf][kk] = *reinterpret_cast<const Raw *>(kp + kk * 4 * kChunkBytes);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      vraw[kk] = *reinterpret_cast<const Raw *>(vp + kk * 4 * kChunkBytes);
+    if constexpr (NG > 0) {
+      const float *kr = ksbase + static_cast<int64_t>(slot) * p.ks_ss;
+      const float *vr = vsbase + static_cast<int64_t>(slot) * p.vs_ss;
+#pragma unroll
+      for (int i = 0; i < NGL; ++i) {
+        const int gi = qg + 4 * i;
+        ksr[i] = (gi < NG) ? kr[gi] : 0.0f;
+        vsr[i] = (gi < NG) ? vr[gi] : 0.0f;
+      }
+    }
+  };
+
+  // 1. dequantized V rows (and both scale rows) of the current tile into
+  // the wave's LDS tile
+  auto stage_v = [&]() {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      *reinterpret_cast<uint4 *>(vt + r16 * kLdsRow + (4 * kk + qg) * 16) = to_bf16x8<FMT>(vraw[kk]);
+    }
+    if constexpr (NG > 0) {
+#pragma unroll
+      for (int i = 0; i < NGL; ++i) {
+        const int gi = qg + 4 * i;
+        if (gi < NG) {
+          ksc[r16 * NG + gi] = ksr[i];
+          vsc[r16 * NG + gi] = vsr[i];
+        }
+      }
+    }
+  };
+
+  auto process = [&](int buf, int t) {
+
+    // 2. S^T = K . Q^T  (lane: head r16, entries 4*qg + e)
+    f32x4 s;
+    if constexpr (NG <= 1) {
+      s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(to_bf16x8<FMT>(kraw[buf][kk])),
+                                                    qfrag(kk), s, 0, 0, 0);
+    }
+    wave_lds_fence();
+    if constexpr (NG == 1) {
+      const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ksc + 4 * qg);
+      s *= k4;
+    } else if constexpr (NG > 1) {
+      constexpr int KPG = G / 32;  // QK MFMAs per scale group
+      s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KPG; ++u) {
+          const int kk = gi * KPG + u;
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_bf16x8(to_bf16x8<FMT>(kraw[buf][kk])), qfrag(kk), part, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] += ksc[(4 * qg + e) * NG + gi] * part[e];
+      }
+    }
+
+    // 3. online softmax in log2 units
+    const int jbase = kTile * t + 4 * qg;
+    float s2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s2[e] = (jbase + e < nkeys) ? s[e] * kScaleLog2 : -INFINITY;
+    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(s2[e] - m_new);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
+
+    // 4. O^T += V^T . P^T with P as hi + lo bf16
+    auto split_p = [&](const float (&pv)[4], i16x4 &hi, i16x4 &lo) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hb = f32_to_bf16_rne(pv[e]);
+        const float rest = pv[e] - __uint_as_float(hb << 16);
+        hi[e] = static_cast<short>(hb);
+        lo[e] = static_cast<short>(f32_to_bf16_rne(rest));
+      }
+    };
+    auto pv_mfma = [&](int mt, const i16x4 &hi, const i16x4 &lo) {
+      i16x4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a[e] = *reinterpret_cast<const short *>(vcol + e * kLdsRow + 32 * mt);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[mt], 0, 0, 0);
+    };
+    if constexpr (NG <= 1) {
+      float pv[4];
+      if constexpr (NG == 1) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(vsc + 4 * qg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = pr[e] * v4[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = pr[e];
+      }
+      i16x4 hi, lo;
+      split_p(pv, hi, lo);
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) pv_mfma(mt, hi, lo);
+    } else {
+      constexpr int MPG = G / 16;  // PV MFMAs per scale group
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = pr[e] * vsc[(4 * qg + e) * NG + gi];
+        i16x4 hi, lo;
+        split_p(pv, hi, lo);
+#pragma unroll
+        for (int u = 0; u < MPG; ++u) pv_mfma(gi * MPG + u, hi, lo);
+      }
+    }
+    wave_lds_fence();  // reads of this tile finish before the next tile's writes
+  };
+
+  // ---- software pipeline: the rows of tile t+1 are in flight while tile t
+  // is processed.  Step t: V(t) -> LDS, issue K/V(t+1), fetch the slot of
+  // t+2, then QK / softmax / PV of tile t.
+  if (ntile > 0) {
+    issue(0, checked(fetch_slot(0)));
+    int32_t slot_next = (ntile > 1) ? fetch_slot(1) : 0;
+    for (int t = 0; t < ntile; t += 2) {
+      {
+        stage_v();
+        if (t + 1 < ntile) issue(1, checked(slot_next));
+        slot_next = (t + 2 < ntile) ? fetch_slot(t + 2) : 0;
+        process(0, t);
+      }
+      if (t + 1 < ntile) {
+        stage_v();
+        if (t + 2 < ntile) issue(0, checked(slot_next));
+        slot_next = (t + 3 < ntile) ? fetch_slot(t + 3) : 0;
+        process(1, t + 1);
+      }
+    }
+  }
+
+  // ---- wave result: full sum per head over the 4 lane groups
+  float l_w = l_run + __shfl_xor(l_run, 16);
+  l_w += __shfl_xor(l_w, 32);
+  const bool wave_bad = __any(bad_slot);
+  if (wave_bad) {
+    l_w = __builtin_nanf("");
+    if (lane == 0) atomicOr(p.err, kErrSlot);
+  }
+
+  // ---- merge the 4 wave states of this workgroup through LDS
+  __syncthreads();
+  float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
+  float *red_l = red_m + kWaves * 16;               // [4][16]
+  float *red_acc = red_l + kWaves * 16;             // [4][12][256]
+  if (qg == 0) {
+    red_m[wave * 16 + r16] = m_run;
+    red_l[wave * 16 + r16] = l_w;
+  }
+  if (r16 < kGqa) {
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+      *reinterpret_cast<f32x4 *>(red_acc + (wave * kGqa + r16) * kHeadDim + 16 * mt + 4 * qg) = acc[mt];
+  }
+  __syncthreads();
+
+  const int d = tid;  // one channel per thread
+  float o_un[kGqa], m_h[kGqa], l_h[kGqa];
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 16 + h]);
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_m[w * 16 + h];
+      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      lsum += f * red_l[w * 16 + h];
+      o += f * red_acc[(w * kGqa + h) * kHeadDim + d];
+    }
+    o_un[h] = o;
+    m_h[h] = M;
+    l_h[h] = lsum;
+  }
+
+  __bf16 *orow = p.out + b * p.o_sb + (g * kGqa) * p.o_sh + d;
+  float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
+
+  if (n_active == 1) {
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      const float o = (l_h[h] > 0.f || l_h[h] != l_h[h]) ? o_un[h] / l_h[h] : 0.f;
+      orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o)));
+    }
+    if (tid < kGqa) {
+      float lse_v = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h)
+        if (h == tid) lse_v = (l_h[h] > 0.f || l_h[h] != l_h[h]) ? (m_h[h] + __log2f(l_h[h])) * kLn2 : -INFINITY;
+      lrow[tid * p.l_sh] = lse_v;
+    }
+    return;
+  }
+
+  // ---- split partial, then the last arriver merges all splits in order
+  float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) part[32 + h * kHeadDim + d] = o_un[h];
+  if (tid < kGqa) {
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h)
+      if (h == tid) {
+        part[h] = m_h[h];
+        part[16 + h] = l_h[h];
+      }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == static_cast<uint32_t>(n_active - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
+  float lse_mine = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    float M = -INFINITY;
+    for (int s = 0; s < n_active; ++s) M = fmaxf(M, pbase[s * kPartFloats + h]);
+    float lsum = 0.f, o = 0.f;
+    for (int s = 0; s < n_active; ++s) {
+      const float *ps = pbase + s * kPartFloats;
+      const float ms = ps[h];
+      const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      lsum += f * ps[16 + h];
+      o += f * ps[32 + h * kHeadDim + d];
+    }
+    const float ov = (lsum > 0.f || lsum != lsum) ? o / lsum : 0.f;
+    orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(ov)));
+    if (h == tid) lse_mine = (lsum > 0.f || lsum != lsum) ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  }
+  if (tid < kGqa) lrow[tid * p.l_sh] = lse_mine;
+  if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void fill_u32_kernel(uint32_t *dst, int64_t n, uint32_t value) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = value;
+}
+
+__global__ void audit_kernel(const uint32_t *ctr, int n, uint32_t *accum) {
+  __shared__ uint32_t part[256];
+  uint32_t s = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s += ctr[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x); ++i) t += part[i];
+    atomicAdd(accum, t);
+  }
+}
+
+template <int FMT, int G>
+hipError_t launch_one(const Params &p, hipStream_t stream) {
+  const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
+  const dim3 grid(npairs8 * p.nsplit);
+  hipLaunchKernelGGL((qsa_decode_kernel<FMT, G>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream) {
+  switch (fmt) {
+    case kFmtBF16: return launch_one<kFmtBF16, 256>(p, stream);
+    case kFmtFP8:
+      if (group == 256) return launch_one<kFmtFP8, 256>(p, stream);
+      if (group == 64) return launch_one<kFmtFP8, 64>(p, stream);
+      if (group == 32) return launch_one<kFmtFP8, 32>(p, stream);
+      break;
+    case kFmtINT8:
+      if (group == 256) return launch_one<kFmtINT8, 256>(p, stream);
+      if (group == 64) return launch_one<kFmtINT8, 64>(p, stream);
+      if (group == 32) return launch_one<kFmtINT8, 32>(p, stream);
+      break;
+    case kFmtINT4:
+      if (group == 64) return launch_one<kFmtINT4, 64>(p, stream);
+      if (group == 32) return launch_one<kFmtINT4, 32>(p, stream);
+      break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_audit(const uint32_t *ctr, int n, uint32_t *accum, hipStream_t stream) {
+  hipLaunchKernelGGL(audit_kernel, dim3(1), dim3(256), 0, stream, ctr, n, accum);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream,
+                     dst, n, value);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,62 @@
+// qsa_internal.h -- types shared by the decode kernel and the host API of
+// libqsa.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+constexpr int kHeadDim = 256;
+constexpr int kGqa = 12;          // Q heads per KV head
+constexpr int kMaxSel = 2055;     // list entries per row
+constexpr int kMaxBs = 128;
+constexpr int kWaves = 4;         // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;         // list entries per wave iteration
+
+// One split partial: m[16] and l[16] (log2 domain, 12 used) then the
+// unnormalised accumulator [12][256].
+constexpr int kPartFloats = 32 + kGqa * kHeadDim;
+
+enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3 };
+
+// Device-side error bits (sticky, OR-ed into Params::err).
+constexpr uint32_t kErrRowRange = 1u;   // cu_seqlens out of range / row > 2055
+constexpr uint32_t kErrSlot = 2u;       // a slot id outside [0, slots)
+
+struct Params {
+  const __bf16 *q;          // [bs, hq, 256]
+  int64_t q_sb, q_sh;       // element strides
+  const uint8_t *k, *v;     // pools (byte pointers)
+  int64_t k_ss, k_sh;       // byte strides (slot, kv head)
+  int64_t v_ss, v_sh;
+  const float *ks, *vs;     // scales [slots, hkv, 256/G] or null
+  int64_t ks_ss, ks_sh;     // element strides
+  int64_t vs_ss, vs_sh;
+  const int32_t *sel;
+  int64_t n_sel;
+  const int32_t *cu;
+  __bf16 *out;
+  int64_t o_sb, o_sh;
+  float *lse;
+  int64_t l_sb, l_sh;
+  int64_t slots;
+  int bs, hkv;
+  int nsplit;               // splits per (row, kv head) in the grid
+  int min_split_keys;       // entries per split before another is used
+  float *part;              // [npairs][nsplit][kPartFloats]
+  uint32_t *ctr;            // [npairs], zero at rest
+  uint32_t *err;            // sticky error word
+};
+
+// Launch the decode kernel for one call (grid = 8 * ceil(npairs/8) * nsplit).
+hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream);
+
+// Zero n words at dst with a small kernel (no memset node in captured graphs).
+hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream);
+
+// *accum += sum of ctr[0..n) (one workgroup).
+hipError_t launch_audit(const uint32_t *ctr, int n, uint32_t *accum, hipStream_t stream);
+
+}  // namespace qsa

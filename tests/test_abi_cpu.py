@@ -1,0 +1,156 @@
+"""libqsa.so loads, exports what include/qsa.h declares, and rejects calls
+outside the packed-decode contract on the host (no GPU needed: validation
+reads descriptors only and runs before any HIP call).
+
+Contract: page "fix(qsa): restore SM121 correctness with Humanize and Kernel
+Design Agent", section "Changes" -- bf16, head dim 256, 12:1 GQA as
+24Q/2KV or 12Q/1KV, 1 <= bs <= 128, unsupported calls fail with a
+descriptive error.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_index_paged_amd as qsa
+from sparse_index_paged_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = qsa.load_library()
+    declared = _declared_functions()
+    assert "qsa_decode" in declared and len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in qsa.h but not exported"
+    assert set(declared) == set(B.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", qsa.lib_path()], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qsa_\w+)", nm))
+    assert exported == set(declared)
+
+
+def test_header_compiles_as_c():
+    src = "#include \"qsa.h\"\nint main(void) { return qsa_abi_version() != QSA_ABI_VERSION; }\n"
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I",
+                          os.path.join(ROOT, "include"), "-x", "c", "-"], input=src, text=True,
+                         capture_output=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_abi_version():
+    assert qsa.abi_version() == B.ABI_VERSION == 1
+
+
+def test_plan_and_options():
+    assert qsa.get_option("split_target") == 1024
+    s, w = qsa.plan(128, 2)
+    assert s == 4 and w == 1024
+    s, w = qsa.plan(1, 2)
+    assert w == 8 * s and 1 <= s <= qsa.get_option("max_splits")
+    with pytest.raises(qsa.QsaError, match="unknown option"):
+        qsa.set_option("nope", 3)
+    with pytest.raises(qsa.QsaError, match="bs must be"):
+        qsa.plan(0, 2)
+    qsa.set_option("split_target", 2048)
+    try:
+        assert qsa.plan(128, 2)[0] == 8
+    finally:
+        qsa.set_option("split_target", 1024)
+
+
+# ---- contract rejection with fake (never dereferenced) device pointers ----
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced on the host
+
+
+def _t(shape, dtype, strides=None, data=FAKE):
+    d = B.QsaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    for i, (n, s) in enumerate(zip(shape, strides)):
+        d.shape[i] = n
+        d.stride[i] = s
+    return d
+
+
+def _call(bs=4, hq=24, hkv=2, d=256, slots=64, pool_dtype=B.BF16, v_dtype=None, scales=None,
+          q_dtype=B.BF16, cu_len=None, pool_data=FAKE, q_strides=None, out_shape=None,
+          lse_shape=None, sel_dtype=B.I32, pool_strides=None):
+    lib = qsa.load_library()
+    row = d if pool_dtype != B.U4X2 else d // 2
+    q = _t((bs, hq, d), q_dtype, q_strides)
+    k = _t((slots, hkv, row), pool_dtype, pool_strides, data=pool_data)
+    v = _t((slots, hkv, row), v_dtype or pool_dtype, pool_strides)
+    sel = _t((100,), sel_dtype)
+    cu = _t(((cu_len if cu_len is not None else bs + 1),), B.I32)
+    out = _t(out_shape or (bs, hq, d), B.BF16)
+    lse = _t(lse_shape or (bs, hq), B.F32)
+    st = lib.qsa_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                        ctypes.byref(scales) if scales is not None else None, ctypes.byref(sel),
+                        ctypes.byref(cu), ctypes.byref(out), ctypes.byref(lse), None)
+    return st, lib.qsa_last_error().decode()
+
+
+def _scales(slots=64, hkv=2, group=256, dtype=B.F32):
+    return B.QsaKvScales(_t((slots, hkv, 256 // group), dtype), _t((slots, hkv, 256 // group), dtype),
+                         group)
+
+
+@pytest.mark.parametrize("kwargs,match", [
+    (dict(d=128), "head dim must be 256"),
+    (dict(bs=129), r"bs must be in \[1, 128\]"),
+    (dict(hq=16), r"\(Hq, Hkv\) must be \(24, 2\) or \(12, 1\)"),
+    (dict(hq=12, hkv=2), r"\(Hq, Hkv\)"),
+    (dict(hq=24, hkv=1), r"\(Hq, Hkv\)"),
+    (dict(q_dtype=B.F16), "q must be bf16"),
+    (dict(pool_dtype=B.F32), "is not bf16, fp8_e4m3fn, i8 or u4x2"),
+    (dict(pool_dtype=B.I8, v_dtype=B.FP8_E4M3FN, scales=None), "must share a format"),
+    (dict(pool_dtype=B.I8), "pools need kv_scales"),
+    (dict(scales="bf16"), "take no scales"),
+    (dict(pool_dtype=B.I8, scales="g48"), "group_size 48 is not supported"),
+    (dict(pool_dtype=B.U4X2, scales="g256"), "group_size 256 is not supported"),
+    (dict(pool_dtype=B.I8, scales="f16"), "k_scale must be f32"),
+    (dict(cu_len=3), "cu_seqlens must have bs \\+ 1"),
+    (dict(pool_data=FAKE + 8), "16-byte boundaries"),
+    (dict(q_strides=(24 * 256, 256, 2)), "contiguous in its last dimension"),
+    (dict(out_shape=(4, 24, 128)), "out must be"),
+    (dict(lse_shape=(4, 12)), "lse must be"),
+    (dict(sel_dtype=B.F32), "sel_indices must be i32"),
+])
+def test_contract_rejections(kwargs, match):
+    sc = kwargs.pop("scales", None)
+    if sc == "bf16":
+        kwargs["scales"] = _scales()
+    elif sc == "g48":
+        kwargs["scales"] = B.QsaKvScales(_t((64, 2, 5), B.F32), _t((64, 2, 5), B.F32), 48)
+    elif sc == "g256":
+        kwargs["scales"] = _scales(group=256)
+    elif sc == "f16":
+        kwargs["scales"] = _scales(dtype=B.F16)
+    st, msg = _call(**kwargs)
+    assert st == 1, (st, msg)
+    assert re.search(match, msg), msg
+
+
+def test_null_arguments_are_arg_errors():
+    lib = qsa.load_library()
+    st = lib.qsa_decode(None, None, None, None, None, None, None, None, None)
+    assert st == 2
+    assert "q is NULL" in lib.qsa_last_error().decode()

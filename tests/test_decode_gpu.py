@@ -1,0 +1,220 @@
+"""Parity of the HIP decode path with the oracle, through the C ABI.
+
+Workloads follow the packed decode contract of the page "fix(qsa): restore
+SM121 correctness with Humanize and Kernel Design Agent" (section
+"Changes"); quantized pools follow the page "feat(qsa): quantized KV pools
+with dequant-on-gather (fp8/int8/int4)" (part 4 "Modifications").
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import quant
+from qsa_testlib import compare, oracle_rows, run_and_compare, say, to_device
+
+import sparse_index_paged_amd as qsa
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _default_options():
+    yield
+    qsa.set_option("split_target", 1024)
+    qsa.set_option("max_splits", 16)
+    qsa.set_option("min_split_keys", 256)
+
+
+def test_bs1_tp1_l128():
+    run_and_compare(synth.case_bs1_tp1(), "bs1 tp1 L128")
+
+
+def test_bs16_tp2_mixed_lengths():
+    run_and_compare(synth.case_bs16_tp2_mixed(), "bs16 tp2 mixed")
+
+
+def test_bs128_tp1_saturated_all_rows_small_pool():
+    case = synth.case_bs128_tp1_saturated(seed=1031, slots=16384)
+    run_and_compare(case, "bs128 tp1 sat2055 (16k-slot pool, all rows)")
+
+
+def test_bs128_tp1_saturated_full_size_sampled_rows():
+    """Full-size pools [262144, 2, 256] with 5% peaked keys, in the launch
+    configuration the benchmark times; the oracle checks 16 sampled rows."""
+    case = synth.case_bs128_tp1_saturated()
+    rows = sorted(np.random.default_rng(7).choice(128, size=16, replace=False).tolist())
+    out, lse, _ = run_and_compare(case, "bs128 tp1 sat2055 full size", rows=rows)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert all(v == 0 for v in qsa.debug_counters())
+
+
+@pytest.mark.parametrize("fmt,group,seed", [("fp8", 256, 1041), ("int8", 256, 1042),
+                                            ("int4", 32, 1043)])
+def test_bs64_tp1_quantized_full_size(fmt, group, seed):
+    case = synth.case_bs64_tp1_quantsrc(seed)
+    kc, ks = quant.quantize(case.k_pool, fmt, group)
+    vc, vs = quant.quantize(case.v_pool, fmt, group)
+    run_and_compare(case, f"bs64 tp1 {fmt} g{group}", quant=(fmt, group, kc, ks, vc, vs))
+
+
+@pytest.mark.parametrize("fmt,group", [("fp8", 64), ("fp8", 32), ("int8", 64), ("int8", 32),
+                                       ("int4", 64)])
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_quantized_group_sizes(fmt, group, hkv):
+    lens = [1, 17, 300, 2055, 64, 0, 1000]
+    case = synth.make_case(lengths=lens, slots=4096, hkv=hkv, seed=2000 + group + hkv,
+                           dup_prob=0.05)
+    kc, ks = quant.quantize(case.k_pool, fmt, group)
+    vc, vs = quant.quantize(case.v_pool, fmt, group)
+    run_and_compare(case, f"{fmt} g{group} hkv{hkv}", quant=(fmt, group, kc, ks, vc, vs))
+
+
+EDGE_LENGTHS = [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 2054, 2055, 0, 3, 511]
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+@pytest.mark.parametrize("opts", [dict(), dict(split_target=1), dict(split_target=100000),
+                                  dict(split_target=100000, min_split_keys=1),
+                                  dict(split_target=100000, max_splits=64, min_split_keys=1)])
+def test_edge_lengths_and_split_plans(hkv, opts):
+    for k, v in opts.items():
+        qsa.set_option(k, v)
+    case = synth.make_case(lengths=EDGE_LENGTHS, slots=8192, hkv=hkv, seed=77 + hkv,
+                           dup_prob=0.1)
+    run_and_compare(case, f"edge lengths hkv{hkv} {opts} plan={qsa.plan(case.bs, hkv)}")
+    assert all(v == 0 for v in qsa.debug_counters())
+
+
+@pytest.mark.parametrize("bs", [1, 2, 7, 17, 33, 64, 127, 128])
+def test_batch_sizes_tp2_tp1(bs):
+    rng = np.random.default_rng(bs)
+    for hkv in (1, 2):
+        lens = rng.integers(0, 2056, size=bs).tolist()
+        case = synth.make_case(lengths=lens, slots=8192, hkv=hkv, seed=500 + bs, dup_prob=0.1)
+        run_and_compare(case, f"bs{bs} hkv{hkv}")
+
+
+def test_repeated_single_slot_is_exact():
+    """A list of one slot repeated 2055 times: every weight is 1/2055 exactly
+    and the output is that V row bit for bit; lse = s + ln 2055."""
+    case = synth.make_case(lengths=[5], slots=64, hkv=2, seed=9)
+    sel = np.full(2055, 11, np.int32)
+    cu = np.array([0, 2055], np.int32)
+    d = to_device(case)
+    out, lse = qsa.decode(d["q"], d["k"], d["v"], torch.from_numpy(sel).cuda(),
+                          torch.from_numpy(cu).cuda())
+    torch.cuda.synchronize()
+    for h in range(24):
+        assert torch.equal(out[0, h].cpu(), case.v_pool[11, h // 12])
+    s = (case.q[0].double() @ case.k_pool[11].double().repeat_interleave(12, 0).T).diagonal() / 16
+    assert torch.allclose(lse[0].cpu().double(), s + np.log(2055), atol=1e-4)
+
+
+def test_strided_views():
+    """q / pools / out / lse as strided views of larger buffers."""
+    case = synth.make_case(lengths=[40, 2055, 7], slots=3000, hkv=2, seed=31)
+    big_q = torch.zeros(3, 40, 256, dtype=torch.bfloat16)
+    big_q[:, 8:32] = case.q
+    big_k = torch.zeros(3000, 4, 256, dtype=torch.bfloat16)
+    big_v = torch.zeros(3000, 3, 256, dtype=torch.bfloat16)
+    big_k[:, 1:3] = case.k_pool
+    big_v[:, 0:2] = case.v_pool
+    q = big_q.cuda()[:, 8:32]
+    k = big_k.cuda()[:, 1:3]
+    v = big_v.cuda()[:, 0:2]
+    out_big = torch.full((3, 30, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse_big = torch.full((3, 48), 7.0, dtype=torch.float32, device="cuda")
+    out = out_big[:, 3:27]
+    lse = lse_big[:, ::2]
+    sel = torch.from_numpy(case.sel).cuda()
+    cu = torch.from_numpy(case.cu).cuda()
+    qsa.decode(q, k, v, sel, cu, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_rows(case.q, case.k_pool, case.v_pool, case.sel, case.cu)
+    compare(out, lse, o_ref, l_ref, case.lengths, label="strided views")
+    assert torch.all(out_big[:, :3] == 7.0) and torch.all(out_big[:, 27:] == 7.0)
+    assert torch.all(lse_big[:, 1::2] == 7.0)
+
+
+def test_bitwise_deterministic_and_plan_independent():
+    case = synth.make_case(lengths=[2055] * 8 + [700] * 8, slots=20000, hkv=2, seed=41,
+                           dup_prob=0.1)
+    d = to_device(case)
+    o1, l1 = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+    o2, l2 = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    qsa.set_option("split_target", 1)
+    o3, l3 = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    diff = (o3.float() - o1.float()).norm() / o1.float().norm()
+    assert diff < 2e-3 and (l3 - l1).abs().max() < 1e-4
+
+
+def test_controls_k_zero_v_zero():
+    """K := 0 gives uniform weights (mean of the listed V rows, lse = ln L);
+    V := 0 gives exactly zero."""
+    case = synth.make_case(lengths=[2055, 100, 1], slots=5000, hkv=2, seed=51)
+    d = to_device(case)
+    zk = torch.zeros_like(d["k"])
+    out, lse = qsa.decode(d["q"], zk, d["v"], d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    for b in range(case.bs):
+        idx = torch.from_numpy(case.sel[case.cu[b]:case.cu[b + 1]].astype(np.int64))
+        for g in range(2):
+            mean = case.v_pool[idx, g].double().mean(0)
+            got = out[b, 12 * g:12 * g + 12].cpu().double()
+            rel = (got - mean).norm() / (mean.norm() * np.sqrt(12))
+            assert rel < 2e-3
+        assert torch.allclose(lse[b].cpu().double(),
+                              torch.full((24,), float(np.log(case.lengths[b])), dtype=torch.float64),
+                              atol=1e-5)
+    out, _ = qsa.decode(d["q"], d["k"], torch.zeros_like(d["v"]), d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    assert not out.float().any()
+
+
+def test_device_errors_are_reported_and_isolated():
+    """Rows whose lengths or slot ids are outside the contract come back as
+    NaN with a device error bit; the other rows are unaffected."""
+    case = synth.make_case(lengths=[30, 2056, 30, 30], slots=1000, hkv=1, seed=61)
+    sel = case.sel.copy()
+    sel[case.cu[2] + 5] = 1000          # slot id == slots: out of range
+    qsa.workspace_reset()
+    d = to_device(case)
+    out, lse = qsa.decode(d["q"], d["k"], d["v"], torch.from_numpy(sel).cuda(), d["cu"])
+    word = qsa.debug_device_error()
+    assert word == 3, word
+    assert torch.isnan(out[1].float()).all() and torch.isnan(lse[1]).all()
+    assert torch.isnan(out[2].float()).all() and torch.isnan(lse[2]).all()
+    good = [0, 3]
+    o_ref, l_ref = oracle_rows(case.q, case.k_pool, case.v_pool, case.sel, case.cu, good)
+    compare(out[good], lse[good], o_ref, l_ref, case.lengths[good], label="good rows")
+    # cu beyond the end of sel
+    cu_bad = torch.tensor([0, 30, 70000], dtype=torch.int32, device="cuda")
+    q2 = d["q"][:2].contiguous()
+    out2, lse2 = qsa.decode(q2, d["k"], d["v"], d["sel"], cu_bad)
+    torch.cuda.synchronize()
+    assert torch.isnan(out2[1].float()).all() and not torch.isnan(out2[0].float()).any()
+    assert all(v == 0 for v in qsa.debug_counters())
+    qsa.workspace_reset()
+    assert qsa.debug_device_error() == 0
+
+
+def test_one_launch_per_call_and_counters_at_rest():
+    """torch's profiler sees exactly one kernel per qsa_decode call."""
+    case = synth.make_case(lengths=[2055] * 4, slots=4096, hkv=2, seed=71)
+    d = to_device(case)
+    qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    from torch.profiler import ProfilerActivity, profile
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(3):
+            qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+        torch.cuda.synchronize()
+    kernels = [e for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA
+               and "qsa_decode_kernel" in e.name]
+    say(f"  decode kernels seen: {len(kernels)}")
+    assert len(kernels) == 3
+    assert all(v == 0 for v in qsa.debug_counters())
