@@ -26,7 +26,7 @@
  *     The library never frees them and keeps none of them after returning.
  *   - Strides are in elements of the tensor's dtype (for QSA_DTYPE_U4X2 an
  *     element is one byte holding two codes).  The last dimension must be
- *     contiguous (stride 1).
+ *     contiguous (stride 1), except for lse, which may have any strides.
  *   - Validation is done on the host from shapes/dtypes/strides only; the
  *     host never reads device data.  A failed check returns a status and
  *     sets the thread-local message returned by qsa_last_error().  Nothing

@@ -152,7 +152,8 @@ int64_t dtype_bytes(int32_t dt) {
   }
 }
 
-qsa_status check_tensor(const qsa_tensor *t, const char *name, int32_t dtype, int ndim) {
+qsa_status check_tensor(const qsa_tensor *t, const char *name, int32_t dtype, int ndim,
+                        bool last_dim_contiguous = true) {
   if (t == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s is NULL", name);
   if (t->data == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s.data is NULL", name);
   if (t->dtype != dtype)
@@ -165,7 +166,7 @@ qsa_status check_tensor(const qsa_tensor *t, const char *name, int32_t dtype, in
     if (t->shape[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.shape[%d] < 0", name, i);
     if (t->stride[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.stride[%d] < 0", name, i);
   }
-  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
+  if (last_dim_contiguous && t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must be contiguous in its last dimension", name);
   return QSA_OK;
 }
@@ -263,7 +264,8 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   if ((st = check_tensor(out, "out", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
   if (out->shape[0] != bs || out->shape[1] != hq || out->shape[2] != QSA_HEAD_DIM)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: out must be [bs, Hq, 256] like q");
-  if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2)) != QSA_OK) return st;
+  // lse is written one float at a time: any strides
+  if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2, false)) != QSA_OK) return st;
   if (lse->shape[0] != bs || lse->shape[1] != hq)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: lse must be [bs, Hq]");
 
