@@ -96,12 +96,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--banks", type=int, default=4)
     ap.add_argument("--bs", type=int, default=128)
+    ap.add_argument("--hkv", type=int, default=2, choices=[1, 2])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["decode", "copy"], default="decode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--split-target", type=int, default=None)
     ap.add_argument("--min-split-keys", type=int, default=None)
+    ap.add_argument("--waves", type=int, default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -124,10 +126,12 @@ def main():
         qsa.set_option("split_target", args.split_target)
     if args.min_split_keys:
         qsa.set_option("min_split_keys", args.min_split_keys)
+    if args.waves:
+        qsa.set_option("waves_per_workgroup", args.waves)
 
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    case = synth.case_bs128_tp1_saturated(bs=args.bs)
+    case = synth.case_bs128_tp1_saturated(bs=args.bs, hkv=args.hkv)
     bank_sels = [case.sel]
     for i in range(1, args.banks):
         rng = np.random.default_rng(103_000 + i)
@@ -182,8 +186,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"packed QSA decode bs={case.bs} TP1 (24Q/2KV, D=256) bf16 pools "
-                        f"[262144,2,256], 2055 selected slots per row, 5% keys x8",
+            "workload": f"packed QSA decode bs={case.bs} "
+                        f"{'TP1 (24Q/2KV' if case.hkv == 2 else 'TP2 (12Q/1KV'}, D=256) bf16 pools "
+                        f"[262144,{case.hkv},256], 2055 selected slots per row, 5% keys x8",
             "bs": case.bs, "hq": case.hq, "hkv": case.hkv, "head_dim": 256,
             "sel_per_row": int(case.lengths.max()), "pool_slots": int(case.k_pool.shape[0]),
             "index_banks": len(sels), "splits": splits, "workgroups": wgs,

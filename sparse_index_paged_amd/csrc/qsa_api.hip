@@ -42,6 +42,7 @@ qsa_status ok() {
 std::atomic<int64_t> g_split_target{1024};
 std::atomic<int64_t> g_max_splits{16};
 std::atomic<int64_t> g_min_split_keys{256};
+std::atomic<int64_t> g_waves{4};
 
 int plan_splits(int bs, int hkv) {
   const int64_t npairs8 = ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8;
@@ -191,6 +192,9 @@ qsa_status qsa_set_option(const char *name, int64_t value) {
     g_max_splits = value;
   } else if (!strcmp(name, "min_split_keys")) {
     g_min_split_keys = value;
+  } else if (!strcmp(name, "waves_per_workgroup")) {
+    if (value != 4 && value != 8) return fail(QSA_ERR_ARG, "qsa_set_option: waves_per_workgroup must be 4 or 8");
+    g_waves = value;
   } else {
     return fail(QSA_ERR_ARG, "qsa_set_option: unknown option '%s'", name);
   }
@@ -202,6 +206,7 @@ qsa_status qsa_get_option(const char *name, int64_t *value) {
   if (!strcmp(name, "split_target")) *value = g_split_target;
   else if (!strcmp(name, "max_splits")) *value = g_max_splits;
   else if (!strcmp(name, "min_split_keys")) *value = g_min_split_keys;
+  else if (!strcmp(name, "waves_per_workgroup")) *value = g_waves;
   else return fail(QSA_ERR_ARG, "qsa_get_option: unknown option '%s'", name);
   return ok();
 }
@@ -347,6 +352,7 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.bs = static_cast<int>(bs);
   p.hkv = static_cast<int>(hkv);
   p.nsplit = splits;
+  p.waves = static_cast<int>(g_waves.load());
   p.min_split_keys = static_cast<int>(g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load());
   p.part = ws->part;
   p.ctr = ws->words;

@@ -135,32 +135,44 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// LDS: during the loop each wave owns a V tile [16][512 B] plus its scales;
-// afterwards the region is reused to merge the four wave states.
-constexpr int kVTileBytes = kTile * kLdsRow;
-constexpr int kScaleFloats = kTile * 8;  // up to 8 groups per row
-constexpr int kWaveLdsBytes = kVTileBytes + 2 * kScaleFloats * 4;
-constexpr int kLoopLdsBytes = kWaves * kWaveLdsBytes;
-constexpr int kQLdsBytes = 16 * kLdsRow;
-constexpr int kMergeLdsBytes = (2 * kWaves * 16 + kWaves * kGqa * kHeadDim) * 4;
-constexpr int kLdsBytes = (kLoopLdsBytes + kQLdsBytes) > kMergeLdsBytes ? (kLoopLdsBytes + kQLdsBytes)
-                                                                        : kMergeLdsBytes;
+// LDS layout for a workgroup of W waves.  During the loop each wave owns a
+// V tile [16][528 B] plus its scale rows, and all waves share Q [16][528 B];
+// afterwards the same bytes are reused to merge the wave states.
+template <int W> struct Lds {
+  static constexpr int kVTile = kTile * kLdsRow;
+  static constexpr int kScaleFloats = kTile * 8;               // up to 8 groups per row
+  static constexpr int kWave = kVTile + 2 * kScaleFloats * 4;
+  static constexpr int kLoop = W * kWave;
+  static constexpr int kQ = 16 * kLdsRow;
+  // merge of 4 wave states: m, l [4][16] and acc [4][12][256]; a workgroup of
+  // 8 waves first folds waves 4..7 into 0..3 through [4][16 f32x4][64 lanes]
+  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim) * 4;
+  static constexpr int kFold = (W > 4) ? 4 * (16 * 64 * 16 + 2 * 64 * 4) : 0;
+  static constexpr int kMerge = kMerge4 > kFold ? kMerge4 : kFold;
+  static constexpr int kBytes = (kLoop + kQ) > kMerge ? (kLoop + kQ) : kMerge;
+};
 
-__device__ void write_nan_rows(const Params &p, int b, int g, int tid) {
+__device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthreads) {
   const __bf16 nan = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x7FC0u));
-  for (int h = 0; h < kGqa; ++h)
-    p.out[b * p.o_sb + (g * kGqa + h) * p.o_sh + tid] = nan;
+  for (int i = tid; i < kGqa * kHeadDim; i += nthreads)
+    p.out[b * p.o_sb + (g * kGqa + i / kHeadDim) * p.o_sh + (i % kHeadDim)] = nan;
   if (tid < kGqa) p.lse[b * p.l_sb + (g * kGqa + tid) * p.l_sh] = __builtin_nanf("");
 }
 
-template <int FMT, int G>
-__global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p) {
+template <int FMT, int G, int W>
+__global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params p) {
   using Raw = typename Fmt<FMT>::Raw;
+  using LDS = Lds<W>;
+  constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NGL = (NG == 0) ? 0 : (NG >= 4 ? NG / 4 : 1); // scale loads per lane
   constexpr int kChunkBytes = 8 * Fmt<FMT>::kElemBits / 8;    // bytes of 8 codes
+  // after the merge each thread owns channel d = tid % 256 of heads
+  // h0, h0 + HS, ... (HS = threads / 256)
+  constexpr int HS = kThr / kHeadDim;
+  constexpr int NH = kGqa / HS;
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -186,7 +198,7 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
   const int L = c1 - c0;
   if (c0 < 0 || L < 0 || L > kMaxSel || static_cast<int64_t>(c1) > p.n_sel) {
     if (split == 0) {
-      write_nan_rows(p, b, g, tid);
+      write_nan_rows(p, b, g, tid, kThr);
       if (tid == 0) atomicOr(p.err, kErrRowRange);
     }
     return;
@@ -196,36 +208,17 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
   if (split >= n_active) return;
 
   // ---- this wave's contiguous slice of the list
-  const int nw = n_active * kWaves;
-  const int wi = split * kWaves + wave;
+  const int nw = n_active * W;
+  const int wi = split * W + wave;
   const int k0 = (L * wi) / nw;
   const int nkeys = (L * (wi + 1)) / nw - k0;
   const int ntile = (nkeys + kTile - 1) / kTile;
 
-  // ---- Q of the 12 heads of KV head g -> LDS [16 heads][528 B] (heads
-  // 12..15 zero); each QK MFMA reads its B operand from there.
-  unsigned char *qlds = smem + kLoopLdsBytes;
-  {
-    const int h = tid >> 4;        // 16 threads per head, 2 chunks each
-    const int c = (tid & 15) * 2;
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (h < kGqa) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + (g * kGqa + h) * p.q_sh) + c;
-      v0 = src[0];
-      v1 = src[1];
-    }
-    *reinterpret_cast<uint4 *>(qlds + h * kLdsRow + c * 16) = v0;
-    *reinterpret_cast<uint4 *>(qlds + h * kLdsRow + c * 16 + 16) = v1;
-  }
-  __syncthreads();
-  auto qfrag = [&](int kk) -> bf16x8 {
-    return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
-  };
-
-  unsigned char *wlds = smem + wave * kWaveLdsBytes;
+  unsigned char *qlds = smem + LDS::kLoop;
+  unsigned char *wlds = smem + wave * LDS::kWave;
   unsigned char *vt = wlds;                                          // [16][528 B]
-  float *ksc = reinterpret_cast<float *>(wlds + kVTileBytes);        // [16][NG]
-  float *vsc = ksc + kScaleFloats;                                   // [16][NG]
+  float *ksc = reinterpret_cast<float *>(wlds + LDS::kVTile);        // [16][NG]
+  float *vsc = ksc + LDS::kScaleFloats;                              // [16][NG]
 
   const uint8_t *kbase = p.k + g * p.k_sh + (kChunkBytes * qg);
   const uint8_t *vbase = p.v + g * p.v_sh + (kChunkBytes * qg);
@@ -282,13 +275,41 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
     }
   };
 
+  // ---- prologue: the first two slot ids and Q are in flight together; Q
+  // of the 12 heads of KV head g goes to LDS [16 heads][528 B] (heads
+  // 12..15 zero), where each QK MFMA reads its B operand.
+  int32_t slot0 = 0, slot_next = 0;
+  if (ntile > 0) slot0 = fetch_slot(0);
+  if (ntile > 1) slot_next = fetch_slot(1);
+  {
+    constexpr int CPT = 512 / kThr;  // 16-byte Q chunks per thread
+    uint4 qv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid * CPT + i;
+      const int h = idx >> 5, c = idx & 31;
+      qv[i] = make_uint4(0, 0, 0, 0);
+      if (h < kGqa)
+        qv[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + (g * kGqa + h) * p.q_sh)[c];
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid * CPT + i;
+      *reinterpret_cast<uint4 *>(qlds + (idx >> 5) * kLdsRow + (idx & 31) * 16) = qv[i];
+    }
+  }
+  if (ntile > 0) issue(0, checked(slot0));
+  __syncthreads();
+  auto qfrag = [&](int kk) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
+  };
+
   // 1. dequantized V rows (and both scale rows) of the current tile into
   // the wave's LDS tile
   auto stage_v = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+    for (int kk = 0; kk < 8; ++kk)
       *reinterpret_cast<uint4 *>(vt + r16 * kLdsRow + (4 * kk + qg) * 16) = to_bf16x8<FMT>(vraw[kk]);
-    }
     if constexpr (NG > 0) {
 #pragma unroll
       for (int i = 0; i < NGL; ++i) {
@@ -302,7 +323,6 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
   };
 
   auto process = [&](int buf, int t) {
-
     // 2. S^T = K . Q^T  (lane: head r16, entries 4*qg + e)
     f32x4 s;
     if constexpr (NG <= 1) {
@@ -403,8 +423,6 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
   // is processed.  Step t: V(t) -> LDS, issue K/V(t+1), fetch the slot of
   // t+2, then QK / softmax / PV of tile t.
   if (ntile > 0) {
-    issue(0, checked(fetch_slot(0)));
-    int32_t slot_next = (ntile > 1) ? fetch_slot(1) : 0;
     for (int t = 0; t < ntile; t += 2) {
       {
         stage_v();
@@ -424,108 +442,173 @@ __global__ void __launch_bounds__(kThreads, 2) qsa_decode_kernel(const Params p)
   // ---- wave result: full sum per head over the 4 lane groups
   float l_w = l_run + __shfl_xor(l_run, 16);
   l_w += __shfl_xor(l_w, 32);
-  const bool wave_bad = __any(bad_slot);
-  if (wave_bad) {
+  if (__any(bad_slot)) {
     l_w = __builtin_nanf("");
     if (lane == 0) atomicOr(p.err, kErrSlot);
   }
 
-  // ---- merge the 4 wave states of this workgroup through LDS
+  // ---- 8-wave workgroups: fold waves 4..7 into waves 0..3 (same lane
+  // layout, so the fold is element-wise per lane)
   __syncthreads();
-  float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
-  float *red_l = red_m + kWaves * 16;               // [4][16]
-  float *red_acc = red_l + kWaves * 16;             // [4][12][256]
-  if (qg == 0) {
-    red_m[wave * 16 + r16] = m_run;
-    red_l[wave * 16 + r16] = l_w;
-  }
-  if (r16 < kGqa) {
+  if constexpr (W > 4) {
+    f32x4 *fold = reinterpret_cast<f32x4 *>(smem);               // [4][16][64]
+    float *fold_ml = reinterpret_cast<float *>(smem + 4 * 16 * 64 * 16);  // [4][2][64]
+    if (wave >= 4) {
+      const int slot = wave - 4;
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt)
-      *reinterpret_cast<f32x4 *>(red_acc + (wave * kGqa + r16) * kHeadDim + 16 * mt + 4 * qg) = acc[mt];
+      for (int mt = 0; mt < 16; ++mt) fold[(slot * 16 + mt) * 64 + lane] = acc[mt];
+      fold_ml[(slot * 2 + 0) * 64 + lane] = m_run;
+      fold_ml[(slot * 2 + 1) * 64 + lane] = l_w;
+    }
+    __syncthreads();
+    if (wave < 4) {
+      const float m2 = fold_ml[(wave * 2 + 0) * 64 + lane];
+      const float l2 = fold_ml[(wave * 2 + 1) * 64 + lane];
+      const float M = fmaxf(m_run, m2);
+      const float f1 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float f2 = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) acc[mt] = acc[mt] * f1 + fold[(wave * 16 + mt) * 64 + lane] * f2;
+      l_w = l_w * f1 + l2 * f2;
+      m_run = M;
+    }
+    __syncthreads();
+  }
+
+  // ---- merge the (up to) 4 wave states of this workgroup through LDS
+  float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
+  float *red_l = red_m + 4 * 16;                    // [4][16]
+  float *red_acc = red_l + 4 * 16;                  // [4][12][256]
+  if (wave < 4) {
+    if (qg == 0) {
+      red_m[wave * 16 + r16] = m_run;
+      red_l[wave * 16 + r16] = l_w;
+    }
+    if (r16 < kGqa) {
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt)
+        *reinterpret_cast<f32x4 *>(red_acc + (wave * kGqa + r16) * kHeadDim + 16 * mt + 4 * qg) = acc[mt];
+    }
   }
   __syncthreads();
 
-  const int d = tid;  // one channel per thread
-  float o_un[kGqa], m_h[kGqa], l_h[kGqa];
+  const int d = tid & (kHeadDim - 1);  // one channel per thread
+  const int h0 = tid >> 8;             // first head of this thread
+  float o_un[NH], m_h[NH], l_h[NH];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
+  for (int i = 0; i < NH; ++i) {
+    const int h = h0 + i * HS;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_m[w * 16 + h]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + h]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < 4; ++w) {
       const float mw = red_m[w * 16 + h];
-      const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       lsum += f * red_l[w * 16 + h];
       o += f * red_acc[(w * kGqa + h) * kHeadDim + d];
     }
-    o_un[h] = o;
-    m_h[h] = M;
-    l_h[h] = lsum;
+    o_un[i] = o;
+    m_h[i] = M;
+    l_h[i] = lsum;
   }
 
   __bf16 *orow = p.out + b * p.o_sb + (g * kGqa) * p.o_sh + d;
   float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
+  auto finish = [&](int h, float o, float M, float lsum) {
+    const bool any = lsum > 0.f || lsum != lsum;
+    orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(any ? o / lsum : 0.f)));
+    if (d == 0) lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+  };
 
   if (n_active == 1) {
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      const float o = (l_h[h] > 0.f || l_h[h] != l_h[h]) ? o_un[h] / l_h[h] : 0.f;
-      orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o)));
-    }
-    if (tid < kGqa) {
-      float lse_v = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < kGqa; ++h)
-        if (h == tid) lse_v = (l_h[h] > 0.f || l_h[h] != l_h[h]) ? (m_h[h] + __log2f(l_h[h])) * kLn2 : -INFINITY;
-      lrow[tid * p.l_sh] = lse_v;
-    }
+    for (int i = 0; i < NH; ++i) finish(h0 + i * HS, o_un[i], m_h[i], l_h[i]);
     return;
   }
 
-  // ---- split partial, then the last arriver merges all splits in order
+  // ---- split partial, then the last arriver merges all splits in order.
+  // Partials are written and read with device-scope (sc1) accesses, which
+  // are coherent across XCDs without writing back or invalidating whole L2
+  // caches; each wave waits for its stores to be acknowledged before the
+  // workgroup barrier, and one device-scope atomic per workgroup counts the
+  // arrivals.  The split that sees count n_active - 1 is the last one.
   float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) part[32 + h * kHeadDim + d] = o_un[h];
-  if (tid < kGqa) {
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h)
-      if (h == tid) {
-        part[h] = m_h[h];
-        part[16 + h] = l_h[h];
-      }
+  for (int i = 0; i < NH; ++i) {
+    const int h = h0 + i * HS;
+    __hip_atomic_store(part + 32 + h * kHeadDim + d, o_un[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(part + h, m_h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(part + 16 + h, l_h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<uint32_t>(n_active - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
+  // (a) m and l of every split -> LDS in one round of loads
+  auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
-  float lse_mine = -INFINITY;
-#pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
+  float *sm_ml = reinterpret_cast<float *>(smem);            // [n_active][32]
+  float *sm_w = sm_ml + 64 * 32;                             // [n_active][16]
+  float *sm_lsum = sm_w + 64 * 16;                           // [16]
+  for (int i = tid; i < n_active * 32; i += kThr) sm_ml[i] = ld(pbase + (i >> 5) * kPartFloats + (i & 31));
+  __syncthreads();
+  // (b) per head: merged max, normaliser, each split's weight, lse
+  if (tid < kGqa) {
+    const int h = tid;
     float M = -INFINITY;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, pbase[s * kPartFloats + h]);
-    float lsum = 0.f, o = 0.f;
+    for (int s = 0; s < n_active; ++s) M = fmaxf(M, sm_ml[s * 32 + h]);
+    float lsum = 0.f;
     for (int s = 0; s < n_active; ++s) {
-      const float *ps = pbase + s * kPartFloats;
-      const float ms = ps[h];
+      const float ms = sm_ml[s * 32 + h];
       const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      lsum += f * ps[16 + h];
-      o += f * ps[32 + h * kHeadDim + d];
+      sm_w[s * 16 + h] = f;
+      lsum += f * sm_ml[s * 32 + 16 + h];
     }
-    const float ov = (lsum > 0.f || lsum != lsum) ? o / lsum : 0.f;
-    orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(ov)));
-    if (h == tid) lse_mine = (lsum > 0.f || lsum != lsum) ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+    const bool any = lsum > 0.f || lsum != lsum;
+    sm_lsum[h] = lsum;
+    lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
-  if (tid < kGqa) lrow[tid * p.l_sh] = lse_mine;
+  __syncthreads();
+  // (c) out = (sum_s w_s acc_s) / l, splits in index order, loads issued 4
+  // splits at a time
+  float o[NH];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) o[i] = 0.f;
+  int s = 0;
+  for (; s + 4 <= n_active; s += 4) {
+    float a[4][NH];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NH; ++i) a[u][i] = ld(pbase + (s + u) * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NH; ++i) o[i] += sm_w[(s + u) * 16 + h0 + i * HS] * a[u][i];
+  }
+  for (; s < n_active; ++s) {
+    float a[NH];
+#pragma unroll
+    for (int i = 0; i < NH; ++i) a[i] = ld(pbase + s * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d);
+#pragma unroll
+    for (int i = 0; i < NH; ++i) o[i] += sm_w[s * 16 + h0 + i * HS] * a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const float lsum = sm_lsum[h0 + i * HS];
+    const bool any = lsum > 0.f || lsum != lsum;
+    orow[(h0 + i * HS) * p.o_sh] =
+        __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(any ? o[i] / lsum : 0.f)));
+  }
   if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -551,7 +634,10 @@ template <int FMT, int G>
 hipError_t launch_one(const Params &p, hipStream_t stream) {
   const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
   const dim3 grid(npairs8 * p.nsplit);
-  hipLaunchKernelGGL((qsa_decode_kernel<FMT, G>), grid, dim3(kThreads), 0, stream, p);
+  if (p.waves == 8)
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -11,8 +11,6 @@ constexpr int kHeadDim = 256;
 constexpr int kGqa = 12;          // Q heads per KV head
 constexpr int kMaxSel = 2055;     // list entries per row
 constexpr int kMaxBs = 128;
-constexpr int kWaves = 4;         // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;         // list entries per wave iteration
 
 // One split partial: m[16] and l[16] (log2 domain, 12 used) then the
@@ -44,6 +42,7 @@ struct Params {
   int64_t slots;
   int bs, hkv;
   int nsplit;               // splits per (row, kv head) in the grid
+  int waves;                // waves per workgroup: 4 or 8
   int min_split_keys;       // entries per split before another is used
   float *part;              // [npairs][nsplit][kPartFloats]
   uint32_t *ctr;            // [npairs], zero at rest

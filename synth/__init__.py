@@ -143,11 +143,13 @@ def case_bs16_tp2_mixed(seed: int = 102, slots: int = 65536) -> QsaCase:
     return make_case(lengths=lens, slots=slots, hkv=1, seed=seed, name="bs16_tp2_mixed")
 
 
-def case_bs128_tp1_saturated(seed: int = 103, slots: int = 262144, bs: int = 128) -> QsaCase:
+def case_bs128_tp1_saturated(seed: int = 103, slots: int = 262144, bs: int = 128,
+                             hkv: int = 2) -> QsaCase:
     """bs=128, 24Q/2KV, pools [262144, 2, 256], all rows at 2055, 5% of the
-    (slot, kv-head) key rows scaled x8 (peaked softmax)."""
-    return make_case(lengths=[CAPACITY] * bs, slots=slots, hkv=2, seed=seed,
-                     peaked_frac=0.05, name=f"bs{bs}_tp1_sat2055_peaked")
+    (slot, kv-head) key rows scaled x8 (peaked softmax).  bs and the KV head
+    count can be changed for sweeps."""
+    return make_case(lengths=[CAPACITY] * bs, slots=slots, hkv=hkv, seed=seed,
+                     peaked_frac=0.05, name=f"bs{bs}_hkv{hkv}_sat2055_peaked")
 
 
 def quant_lengths_bs64(rng: np.random.Generator, bs: int = 64) -> list[int]:

@@ -24,6 +24,7 @@ def _default_options():
     qsa.set_option("split_target", 1024)
     qsa.set_option("max_splits", 16)
     qsa.set_option("min_split_keys", 256)
+    qsa.set_option("waves_per_workgroup", 4)
 
 
 def test_bs1_tp1_l128():
@@ -76,7 +77,11 @@ EDGE_LENGTHS = [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 2054, 2055
 @pytest.mark.parametrize("hkv", [1, 2])
 @pytest.mark.parametrize("opts", [dict(), dict(split_target=1), dict(split_target=100000),
                                   dict(split_target=100000, min_split_keys=1),
-                                  dict(split_target=100000, max_splits=64, min_split_keys=1)])
+                                  dict(split_target=100000, max_splits=64, min_split_keys=1),
+                                  dict(waves_per_workgroup=8),
+                                  dict(waves_per_workgroup=8, split_target=1),
+                                  dict(waves_per_workgroup=8, split_target=100000,
+                                       min_split_keys=1)])
 def test_edge_lengths_and_split_plans(hkv, opts):
     for k, v in opts.items():
         qsa.set_option(k, v)
