@@ -147,7 +147,7 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
 
 /* Tuning knobs (bench and tests only):
  *   "split_target"   target workgroups per launch used to pick the split
- *                    count (default 1024)
+ *                    count (default 256)
  *   "max_splits"     upper bound on splits per (row, KV head) (default 16)
  *   "min_split_keys" fewest list entries a split is given before another
  *                    split is used (default 256)

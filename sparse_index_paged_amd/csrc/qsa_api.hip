@@ -39,7 +39,7 @@ qsa_status ok() {
 }
 
 // ---- options ---------------------------------------------------------------
-std::atomic<int64_t> g_split_target{1024};
+std::atomic<int64_t> g_split_target{256};
 std::atomic<int64_t> g_max_splits{16};
 std::atomic<int64_t> g_min_split_keys{256};
 std::atomic<int64_t> g_waves{4};

@@ -48,13 +48,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScaleLog2 = kLog2e / 16.0f;  // softmax scale 1/16 in log2 units
 
 // ---- per-format gather geometry --------------------------------------------
-// A lane loads, for each of the 8 QK MFMAs kk, the 8 channels
-// 32*kk + 8*(lane/16) .. +7 of its row.  Raw is the storage of those 8 codes.
+// Rows are gathered with fully coalesced 16-byte loads: one wave instruction
+// covers 1 KB = kRPI whole rows (kLPR lanes per row), and a 16-row tile takes
+// kNI instructions.  Lane l serves rows (l / kLPR) * kNI + i, i < kNI, so its
+// slot ids are contiguous in the list.  Part is the storage of 8 codes.
 template <int FMT> struct Fmt;
-template <> struct Fmt<kFmtBF16> { using Raw = uint4;    static constexpr int kElemBits = 16; };
-template <> struct Fmt<kFmtFP8>  { using Raw = uint2;    static constexpr int kElemBits = 8; };
-template <> struct Fmt<kFmtINT8> { using Raw = uint2;    static constexpr int kElemBits = 8; };
-template <> struct Fmt<kFmtINT4> { using Raw = uint32_t; static constexpr int kElemBits = 4; };
+template <> struct Fmt<kFmtBF16> { using Part = uint4;    static constexpr int kRowBytes = 512; };
+template <> struct Fmt<kFmtFP8>  { using Part = uint2;    static constexpr int kRowBytes = 256; };
+template <> struct Fmt<kFmtINT8> { using Part = uint2;    static constexpr int kRowBytes = 256; };
+template <> struct Fmt<kFmtINT4> { using Part = uint32_t; static constexpr int kRowBytes = 128; };
+template <int FMT> struct Geo {
+  static constexpr int kLPR = Fmt<FMT>::kRowBytes / 16;  // lanes per row
+  static constexpr int kRPI = 64 / kLPR;                 // rows per instruction
+  static constexpr int kNI = 16 / kRPI;                  // instructions per tile
+  static constexpr int kParts = 16 / sizeof(typename Fmt<FMT>::Part);  // 8-code parts per lane
+};
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -82,7 +90,7 @@ __device__ __forceinline__ uint32_t int_to_bf16(int x) {
 }
 
 // 8 codes -> 8 bf16 values packed in a uint4 (element e in half e%2 of word e/2)
-template <int FMT> __device__ __forceinline__ uint4 to_bf16x8(typename Fmt<FMT>::Raw r);
+template <int FMT> __device__ __forceinline__ uint4 to_bf16x8(typename Fmt<FMT>::Part r);
 
 template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtBF16>(uint4 r) { return r; }
 
@@ -136,12 +144,13 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 // LDS layout for a workgroup of W waves.  During the loop each wave owns a
-// V tile [16][528 B] plus its scale rows, and all waves share Q [16][528 B];
+// K tile and a V tile [16][528 B] (dequantized to bf16) plus their scale
+// rows, and all waves share Q [16][528 B];
 // afterwards the same bytes are reused to merge the wave states.
 template <int W> struct Lds {
-  static constexpr int kVTile = kTile * kLdsRow;
+  static constexpr int kTileB = kTile * kLdsRow;               // one bf16 tile [16][528 B]
   static constexpr int kScaleFloats = kTile * 8;               // up to 8 groups per row
-  static constexpr int kWave = kVTile + 2 * kScaleFloats * 4;
+  static constexpr int kWave = 2 * kTileB + 2 * kScaleFloats * 4;
   static constexpr int kLoop = W * kWave;
   static constexpr int kQ = 16 * kLdsRow;
   // merge of 4 wave states: m, l [4][16] and acc [4][12][256]; a workgroup of
@@ -161,12 +170,12 @@ __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthre
 
 template <int FMT, int G, int W>
 __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params p) {
-  using Raw = typename Fmt<FMT>::Raw;
+  using Part = typename Fmt<FMT>::Part;
+  using GEO = Geo<FMT>;
   using LDS = Lds<W>;
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
-  constexpr int NGL = (NG == 0) ? 0 : (NG >= 4 ? NG / 4 : 1); // scale loads per lane
-  constexpr int kChunkBytes = 8 * Fmt<FMT>::kElemBits / 8;    // bytes of 8 codes
+  constexpr int NI = GEO::kNI;
   // after the merge each thread owns channel d = tid % 256 of heads
   // h0, h0 + HS, ... (HS = threads / 256)
   constexpr int HS = kThr / kHeadDim;
@@ -178,8 +187,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int r16 = lane & 15;  // load row / head
+  const int r16 = lane & 15;  // MFMA row / head
   const int qg = lane >> 4;   // lane group 0..3
+  const int ldrow = (lane / GEO::kLPR) * NI;  // first tile row this lane loads
+  const int lchunk = lane % GEO::kLPR;       // its 16-byte chunk of each row
 
   // ---- workgroup -> (pair, split); splits of a pair share blockIdx % 8
   const int npairs = p.bs * p.hkv;
@@ -216,14 +227,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 
   unsigned char *qlds = smem + LDS::kLoop;
   unsigned char *wlds = smem + wave * LDS::kWave;
-  unsigned char *vt = wlds;                                          // [16][528 B]
-  float *ksc = reinterpret_cast<float *>(wlds + LDS::kVTile);        // [16][NG]
+  unsigned char *kt = wlds;                                          // [16][528 B]
+  unsigned char *vt = wlds + LDS::kTileB;                            // [16][528 B]
+  float *ksc = reinterpret_cast<float *>(wlds + 2 * LDS::kTileB);    // [16][NG]
   float *vsc = ksc + LDS::kScaleFloats;                              // [16][NG]
 
-  const uint8_t *kbase = p.k + g * p.k_sh + (kChunkBytes * qg);
-  const uint8_t *vbase = p.v + g * p.v_sh + (kChunkBytes * qg);
-  const float *ksbase = (NG > 0) ? p.ks + g * p.ks_sh : nullptr;
-  const float *vsbase = (NG > 0) ? p.vs + g * p.vs_sh : nullptr;
+  const uint8_t *kbase = p.k + g * p.k_sh + 16 * lchunk;
+  const uint8_t *vbase = p.v + g * p.v_sh + 16 * lchunk;
+  const float *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + lchunk : nullptr;
+  const float *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + lchunk : nullptr;
   const int32_t *selw = p.sel + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
 
@@ -239,49 +251,50 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // channel 16*mt + r16 at byte j*528 + 2*(16*mt + r16).
   const unsigned char *vcol = vt + (4 * qg) * kLdsRow + 2 * r16;
 
-  // K rows of the current and the next tile stay in registers (QK reads
-  // them there); the V rows and scales of the next tile share one register
-  // set that is emptied into LDS at the start of each step.
-  Raw kraw[2][8], vraw[8];
-  float ksr[NGL > 0 ? NGL : 1], vsr[NGL > 0 ? NGL : 1];
+  // The K / V rows (and scales) of the next tile are in flight in one
+  // register set that is emptied into the LDS tiles at the start of a step.
+  uint4 kraw[NI], vraw[NI];
+  float ksr[NI], vsr[NI];
 
-  auto fetch_slot = [&](int t) -> int32_t {
-    int j = kTile * t + r16;
-    j = j < nkeys ? j : nkeys - 1;
-    return selw[j];
+  auto fetch_slots = [&](int t, int32_t (&sl)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int j = kTile * t + ldrow + i;
+      j = j < nkeys ? j : nkeys - 1;
+      sl[i] = selw[j];
+    }
   };
   auto checked = [&](int32_t s) -> uint32_t {
     if (static_cast<uint32_t>(s) >= slots) { bad_slot = true; return 0u; }
     return static_cast<uint32_t>(s);
   };
-  auto issue = [&](int kbuf, uint32_t slot) {
-    const uint8_t *kp = kbase + static_cast<int64_t>(slot) * p.k_ss;
-    const uint8_t *vp = vbase + static_cast<int64_t>(slot) * p.v_ss;
+  auto issue = [&](const int32_t (&sl)[NI]) {
+    uint32_t slot[NI];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      kraw[kbuf][kk] = *reinterpret_cast<const Raw *>(kp + kk * 4 * kChunkBytes);
+    for (int i = 0; i < NI; ++i) slot[i] = checked(sl[i]);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      vraw[kk] = *reinterpret_cast<const Raw *>(vp + kk * 4 * kChunkBytes);
+    for (int i = 0; i < NI; ++i)
+      kraw[i] = *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(slot[i]) * p.k_ss);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      vraw[i] = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(slot[i]) * p.v_ss);
     if constexpr (NG > 0) {
-      const float *kr = ksbase + static_cast<int64_t>(slot) * p.ks_ss;
-      const float *vr = vsbase + static_cast<int64_t>(slot) * p.vs_ss;
 #pragma unroll
-      for (int i = 0; i < NGL; ++i) {
-        const int gi = qg + 4 * i;
-        ksr[i] = (gi < NG) ? kr[gi] : 0.0f;
-        vsr[i] = (gi < NG) ? vr[gi] : 0.0f;
+      for (int i = 0; i < NI; ++i) {
+        ksr[i] = (lchunk < NG) ? ksbase[static_cast<int64_t>(slot[i]) * p.ks_ss] : 0.0f;
+        vsr[i] = (lchunk < NG) ? vsbase[static_cast<int64_t>(slot[i]) * p.vs_ss] : 0.0f;
       }
     }
   };
 
-  // ---- prologue: the first two slot ids and Q are in flight together; Q
-  // of the 12 heads of KV head g goes to LDS [16 heads][528 B] (heads
-  // 12..15 zero), where each QK MFMA reads its B operand.
-  int32_t slot0 = 0, slot_next = 0;
-  if (ntile > 0) slot0 = fetch_slot(0);
-  if (ntile > 1) slot_next = fetch_slot(1);
+  // ---- prologue: the first two tiles' slot ids and Q are in flight
+  // together; Q of the 12 heads of KV head g goes to LDS [16 heads][528 B]
+  // (heads 12..15 zero), where each QK MFMA reads its B operand.
+  int32_t snext[NI];
   {
+    int32_t s0[NI];
+    if (ntile > 0) fetch_slots(0, s0);
+    if (ntile > 1) fetch_slots(1, snext);
     constexpr int CPT = 512 / kThr;  // 16-byte Q chunks per thread
     uint4 qv[CPT];
 #pragma unroll
@@ -297,42 +310,51 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       const int idx = tid * CPT + i;
       *reinterpret_cast<uint4 *>(qlds + (idx >> 5) * kLdsRow + (idx & 31) * 16) = qv[i];
     }
+    if (ntile > 0) issue(s0);
   }
-  if (ntile > 0) issue(0, checked(slot0));
   __syncthreads();
   auto qfrag = [&](int kk) -> bf16x8 {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
   };
+  auto kfrag = [&](int kk) -> bf16x8 {
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(kt + r16 * kLdsRow + (4 * kk + qg) * 16));
+  };
 
-  // 1. dequantized V rows (and both scale rows) of the current tile into
-  // the wave's LDS tile
-  auto stage_v = [&]() {
+  // 1. the current tile's K and V rows, dequantized to bf16, and their
+  // scale rows into the wave's LDS tiles
+  auto stage = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      *reinterpret_cast<uint4 *>(vt + r16 * kLdsRow + (4 * kk + qg) * 16) = to_bf16x8<FMT>(vraw[kk]);
+    for (int i = 0; i < NI; ++i) {
+      const int off = (ldrow + i) * kLdsRow + lchunk * 16 * GEO::kParts;
+#pragma unroll
+      for (int u = 0; u < GEO::kParts; ++u) {
+        const Part kp = reinterpret_cast<const Part *>(&kraw[i])[u];
+        const Part vp = reinterpret_cast<const Part *>(&vraw[i])[u];
+        *reinterpret_cast<uint4 *>(kt + off + 16 * u) = to_bf16x8<FMT>(kp);
+        *reinterpret_cast<uint4 *>(vt + off + 16 * u) = to_bf16x8<FMT>(vp);
+      }
+    }
     if constexpr (NG > 0) {
+      if (lchunk < NG) {
 #pragma unroll
-      for (int i = 0; i < NGL; ++i) {
-        const int gi = qg + 4 * i;
-        if (gi < NG) {
-          ksc[r16 * NG + gi] = ksr[i];
-          vsc[r16 * NG + gi] = vsr[i];
+        for (int i = 0; i < NI; ++i) {
+          ksc[(ldrow + i) * NG + lchunk] = ksr[i];
+          vsc[(ldrow + i) * NG + lchunk] = vsr[i];
         }
       }
     }
   };
 
-  auto process = [&](int buf, int t) {
+  auto process = [&](int t) {
     // 2. S^T = K . Q^T  (lane: head r16, entries 4*qg + e)
+    wave_lds_fence();
     f32x4 s;
     if constexpr (NG <= 1) {
       s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(to_bf16x8<FMT>(kraw[buf][kk])),
-                                                    qfrag(kk), s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk), qfrag(kk), s, 0, 0, 0);
     }
-    wave_lds_fence();
     if constexpr (NG == 1) {
       const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ksc + 4 * qg);
       s *= k4;
@@ -345,8 +367,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 #pragma unroll
         for (int u = 0; u < KPG; ++u) {
           const int kk = gi * KPG + u;
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(to_bf16x8<FMT>(kraw[buf][kk])), qfrag(kk), part, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk), qfrag(kk), part, 0, 0, 0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[e] += ksc[(4 * qg + e) * NG + gi] * part[e];
@@ -420,23 +441,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   };
 
   // ---- software pipeline: the rows of tile t+1 are in flight while tile t
-  // is processed.  Step t: V(t) -> LDS, issue K/V(t+1), fetch the slot of
-  // t+2, then QK / softmax / PV of tile t.
-  if (ntile > 0) {
-    for (int t = 0; t < ntile; t += 2) {
-      {
-        stage_v();
-        if (t + 1 < ntile) issue(1, checked(slot_next));
-        slot_next = (t + 2 < ntile) ? fetch_slot(t + 2) : 0;
-        process(0, t);
-      }
-      if (t + 1 < ntile) {
-        stage_v();
-        if (t + 2 < ntile) issue(0, checked(slot_next));
-        slot_next = (t + 3 < ntile) ? fetch_slot(t + 3) : 0;
-        process(1, t + 1);
-      }
-    }
+  // is processed.  Step t: K/V(t) -> LDS, issue K/V(t+1), fetch the slot ids
+  // of t+2, then QK / softmax / PV of tile t.
+  for (int t = 0; t < ntile; ++t) {
+    stage();
+    if (t + 1 < ntile) issue(snext);
+    if (t + 2 < ntile) fetch_slots(t + 2, snext);
+    process(t);
   }
 
   // ---- wave result: full sum per head over the 4 lane groups

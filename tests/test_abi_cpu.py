@@ -53,9 +53,11 @@ def test_abi_version():
 
 
 def test_plan_and_options():
-    assert qsa.get_option("split_target") == 1024
+    assert qsa.get_option("split_target") == 256
     s, w = qsa.plan(128, 2)
-    assert s == 4 and w == 1024
+    assert s == 1 and w == 256
+    s, w = qsa.plan(16, 1)
+    assert s == 16 and w == 256
     s, w = qsa.plan(1, 2)
     assert w == 8 * s and 1 <= s <= qsa.get_option("max_splits")
     with pytest.raises(qsa.QsaError, match="unknown option"):
@@ -66,7 +68,7 @@ def test_plan_and_options():
     try:
         assert qsa.plan(128, 2)[0] == 8
     finally:
-        qsa.set_option("split_target", 1024)
+        qsa.set_option("split_target", 256)
 
 
 # ---- contract rejection with fake (never dereferenced) device pointers ----
