@@ -155,7 +155,7 @@ template <int W> struct Lds {
   static constexpr int kQ = 16 * kLdsRow;
   // merge of 4 wave states: m, l [4][16] and acc [4][12][256]; a workgroup of
   // 8 waves first folds waves 4..7 into 0..3 through [4][16 f32x4][64 lanes]
-  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim) * 4;
+  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim + 16 * 4 + 16) * 4;
   static constexpr int kFold = (W > 4) ? 4 * (16 * 64 * 16 + 2 * 64 * 4) : 0;
   static constexpr int kMerge = kMerge4 > kFold ? kMerge4 : kFold;
   static constexpr int kBytes = (kLoop + kQ) > kMerge ? (kLoop + kQ) : kMerge;
@@ -486,10 +486,14 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     __syncthreads();
   }
 
-  // ---- merge the (up to) 4 wave states of this workgroup through LDS
+  // ---- merge the (up to) 4 wave states of this workgroup through LDS.
+  // One thread per head computes the wave weights 2^(m_w - M), the merged
+  // max M and sum l once; every thread then combines its channel.
   float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
   float *red_l = red_m + 4 * 16;                    // [4][16]
   float *red_acc = red_l + 4 * 16;                  // [4][12][256]
+  f32x4 *red_f = reinterpret_cast<f32x4 *>(red_acc + 4 * kGqa * kHeadDim);  // [16] weights of waves 0..3
+  float *red_inv = reinterpret_cast<float *>(red_f + 16);                   // [16] 1 / l
   if (wave < 4) {
     if (qg == 0) {
       red_m[wave * 16 + r16] = m_run;
@@ -505,37 +509,50 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 
   const int d = tid & (kHeadDim - 1);  // one channel per thread
   const int h0 = tid >> 8;             // first head of this thread
-  float o_un[NH], m_h[NH], l_h[NH];
-#pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    const int h = h0 + i * HS;
+  __bf16 *orow = p.out + b * p.o_sb + (g * kGqa) * p.o_sh + d;
+  float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
+  float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
+  if (tid < kGqa) {
+    const int h = tid;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + h]);
-    float lsum = 0.f, o = 0.f;
+    f32x4 f;
+    float lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = red_m[w * 16 + h];
-      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lsum += f * red_l[w * 16 + h];
-      o += f * red_acc[(w * kGqa + h) * kHeadDim + d];
+      f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      lsum += f[w] * red_l[w * 16 + h];
     }
-    o_un[i] = o;
-    m_h[i] = M;
-    l_h[i] = lsum;
-  }
-
-  __bf16 *orow = p.out + b * p.o_sb + (g * kGqa) * p.o_sh + d;
-  float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
-  auto finish = [&](int h, float o, float M, float lsum) {
+    red_f[h] = f;
     const bool any = lsum > 0.f || lsum != lsum;
-    orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(any ? o / lsum : 0.f)));
-    if (d == 0) lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
-  };
+    red_inv[h] = any ? 1.0f / lsum : 0.f;
+    if (n_active == 1) {
+      lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
+    } else {
+      __hip_atomic_store(part + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(part + 16 + h, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  float o_un[NH];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int h = h0 + i * HS;
+    const f32x4 f = red_f[h];
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o += f[w] * red_acc[(w * kGqa + h) * kHeadDim + d];
+    o_un[i] = o;
+  }
 
   if (n_active == 1) {
 #pragma unroll
-    for (int i = 0; i < NH; ++i) finish(h0 + i * HS, o_un[i], m_h[i], l_h[i]);
+    for (int i = 0; i < NH; ++i) {
+      const int h = h0 + i * HS;
+      orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o_un[i] * red_inv[h])));
+    }
     return;
   }
 
@@ -545,16 +562,11 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // caches; each wave waits for its stores to be acknowledged before the
   // workgroup barrier, and one device-scope atomic per workgroup counts the
   // arrivals.  The split that sees count n_active - 1 is the last one.
-  float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
+  // (m and l of each head were stored above by the thread owning the head.)
 #pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    const int h = h0 + i * HS;
-    __hip_atomic_store(part + 32 + h * kHeadDim + d, o_un[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == 0) {
-      __hip_atomic_store(part + h, m_h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(part + 16 + h, l_h[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  for (int i = 0; i < NH; ++i)
+    __hip_atomic_store(part + 32 + (h0 + i * HS) * kHeadDim + d, o_un[i], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
@@ -564,12 +576,20 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   __syncthreads();
   if (!s_last) return;
 
-  // (a) m and l of every split -> LDS in one round of loads
+  // (a) one round of loads: the accumulators of the first (up to) 4 splits
+  // into registers and m, l of every split into LDS
   auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
   float *sm_ml = reinterpret_cast<float *>(smem);            // [n_active][32]
   float *sm_w = sm_ml + 64 * 32;                             // [n_active][16]
-  float *sm_lsum = sm_w + 64 * 16;                           // [16]
+  float *sm_inv = sm_w + 64 * 16;                            // [16] 1 / l
+  auto acc_ptr = [&](int sp, int i) { return pbase + sp * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d; };
+  const int nfirst = n_active < 4 ? n_active : 4;
+  float a0[4][NH];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < NH; ++i) a0[u][i] = (u < nfirst) ? ld(acc_ptr(u, i)) : 0.f;
   for (int i = tid; i < n_active * 32; i += kThr) sm_ml[i] = ld(pbase + (i >> 5) * kPartFloats + (i & 31));
   __syncthreads();
   // (b) per head: merged max, normaliser, each split's weight, lse
@@ -580,27 +600,33 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     float lsum = 0.f;
     for (int s = 0; s < n_active; ++s) {
       const float ms = sm_ml[s * 32 + h];
-      const float f = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
       sm_w[s * 16 + h] = f;
       lsum += f * sm_ml[s * 32 + 16 + h];
     }
     const bool any = lsum > 0.f || lsum != lsum;
-    sm_lsum[h] = lsum;
+    sm_inv[h] = any ? 1.0f / lsum : 0.f;
     lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  // (c) out = (sum_s w_s acc_s) / l, splits in index order, loads issued 4
-  // splits at a time
+  // (c) out = (sum_s w_s acc_s) / l, splits in index order; splits past the
+  // first four are loaded 4 at a time
   float o[NH];
 #pragma unroll
   for (int i = 0; i < NH; ++i) o[i] = 0.f;
-  int s = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (u < nfirst) {
+#pragma unroll
+      for (int i = 0; i < NH; ++i) o[i] += sm_w[u * 16 + h0 + i * HS] * a0[u][i];
+    }
+  int s = nfirst;
   for (; s + 4 <= n_active; s += 4) {
     float a[4][NH];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < NH; ++i) a[u][i] = ld(pbase + (s + u) * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d);
+      for (int i = 0; i < NH; ++i) a[u][i] = ld(acc_ptr(s + u, i));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -609,17 +635,14 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   for (; s < n_active; ++s) {
     float a[NH];
 #pragma unroll
-    for (int i = 0; i < NH; ++i) a[i] = ld(pbase + s * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d);
+    for (int i = 0; i < NH; ++i) a[i] = ld(acc_ptr(s, i));
 #pragma unroll
     for (int i = 0; i < NH; ++i) o[i] += sm_w[s * 16 + h0 + i * HS] * a[i];
   }
 #pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    const float lsum = sm_lsum[h0 + i * HS];
-    const bool any = lsum > 0.f || lsum != lsum;
+  for (int i = 0; i < NH; ++i)
     orow[(h0 + i * HS) * p.o_sh] =
-        __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(any ? o[i] / lsum : 0.f)));
-  }
+        __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o[i] * sm_inv[h0 + i * HS])));
   if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
