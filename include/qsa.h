@@ -142,12 +142,13 @@ int64_t qsa_workspace_bytes(void);
 const char *qsa_last_error(void);
 
 /* Split plan qsa_decode uses for (bs, hkv): number of splits per (row, KV
- * head) and the launch's workgroup count. */
+ * head) and the launch's workgroup count.  It depends on (bs, hkv) and the
+ * options only, never on live lengths. */
 qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
 
 /* Tuning knobs (bench and tests only):
- *   "split_target"   target workgroups per launch used to pick the split
- *                    count (default 256)
+ *   "split_target"   0 (default): splits from a cost model of a launch with
+ *                    every list full; > 0: about this many workgroups
  *   "max_splits"     upper bound on splits per (row, KV head) (default 16)
  *   "min_split_keys" fewest list entries a split is given before another
  *                    split is used (default 256)

@@ -39,18 +39,46 @@ qsa_status ok() {
 }
 
 // ---- options ---------------------------------------------------------------
-std::atomic<int64_t> g_split_target{256};
+std::atomic<int64_t> g_split_target{0};  // 0: cost model below
 std::atomic<int64_t> g_max_splits{16};
 std::atomic<int64_t> g_min_split_keys{256};
 std::atomic<int64_t> g_waves{4};
 
+// Splits per (row, KV head) pair.  The plan depends on (bs, hkv) and the
+// options only -- never on live lengths -- so captured graphs stay valid.
+//
+// Default: a cost model of one launch with every list at full capacity on
+// a 256-CU MI355X, fitted to measured per-workgroup timelines.  With n
+// splits the pairs' P*n workgroups are dealt round-robin over the CUs (two
+// resident per CU); the busiest CU gathers ceil(P*n/256) * ceil(2055/n)
+// entries at ~30 entries/us, a split pair adds ~6 us of merge latency, and
+// each workgroup per CU beyond the two resident ones adds ~20 us (it starts
+// only when a resident one has finished, and pays its own start-up and
+// merge).
+// split_target > 0 replaces the model by "about split_target workgroups".
 int plan_splits(int bs, int hkv) {
-  const int64_t npairs8 = ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8;
-  int64_t s = (g_split_target.load() + npairs8 - 1) / npairs8;
+  const int64_t npairs = static_cast<int64_t>(bs) * hkv;
   const int64_t smax = g_max_splits.load();
-  if (s > smax) s = smax;
-  if (s < 1) s = 1;
-  return static_cast<int>(s);
+  const int64_t target = g_split_target.load();
+  if (target > 0) {
+    const int64_t npairs8 = ((npairs + 7) / 8) * 8;
+    int64_t s = (target + npairs8 - 1) / npairs8;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    return static_cast<int>(s);
+  }
+  int best = 1;
+  double best_cost = 1e30;
+  for (int n = 1; n <= smax; ++n) {
+    const int64_t per_cu = (npairs * n + 255) / 256;
+    const double cost = static_cast<double>(per_cu) * ((qsa::kMaxSel + n - 1) / n) / 30.0 +
+                        (n > 1 ? 6.0 : 0.0) + 20.0 * static_cast<double>(per_cu > 2 ? per_cu - 2 : 0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = n;
+    }
+  }
+  return best;
 }
 
 int64_t plan_workgroups(int bs, int hkv, int splits) {
@@ -184,9 +212,10 @@ const char *qsa_last_error(void) { return g_last_error.c_str(); }
 
 qsa_status qsa_set_option(const char *name, int64_t value) {
   if (name == nullptr) return fail(QSA_ERR_ARG, "qsa_set_option: name is NULL");
-  if (value < 1) return fail(QSA_ERR_ARG, "qsa_set_option: %s must be >= 1", name);
+  if (value < 0 || (value == 0 && strcmp(name, "split_target") != 0))
+    return fail(QSA_ERR_ARG, "qsa_set_option: %s must be >= 1", name);
   if (!strcmp(name, "split_target")) {
-    g_split_target = value;
+    g_split_target = value;  // 0 restores the cost model
   } else if (!strcmp(name, "max_splits")) {
     if (value > 64) return fail(QSA_ERR_ARG, "qsa_set_option: max_splits must be <= 64");
     g_max_splits = value;

@@ -53,13 +53,20 @@ def test_abi_version():
 
 
 def test_plan_and_options():
-    assert qsa.get_option("split_target") == 256
-    s, w = qsa.plan(128, 2)
-    assert s == 1 and w == 256
-    s, w = qsa.plan(16, 1)
-    assert s == 16 and w == 256
-    s, w = qsa.plan(1, 2)
-    assert w == 8 * s and 1 <= s <= qsa.get_option("max_splits")
+    assert qsa.get_option("split_target") == 0          # cost model
+    # one workgroup per CU when the pairs fill the chip; fractional fills
+    # pick the split count that balances the busiest CU
+    assert qsa.plan(128, 2) == (1, 256)
+    assert qsa.plan(64, 2) == (2, 256)
+    assert qsa.plan(32, 2) == (4, 256)
+    assert qsa.plan(16, 1) == (16, 256)
+    assert qsa.plan(48, 2) == (5, 480)
+    assert qsa.plan(96, 2) == (1, 192)        # a third workgroup per CU costs more
+    assert qsa.plan(96, 1) == (5, 480)
+    for bs in range(1, 129):
+        for hkv in (1, 2):
+            s, w = qsa.plan(bs, hkv)
+            assert 1 <= s <= 16 and w == ((bs * hkv + 7) // 8) * 8 * s
     with pytest.raises(qsa.QsaError, match="unknown option"):
         qsa.set_option("nope", 3)
     with pytest.raises(qsa.QsaError, match="bs must be"):
@@ -68,7 +75,7 @@ def test_plan_and_options():
     try:
         assert qsa.plan(128, 2)[0] == 8
     finally:
-        qsa.set_option("split_target", 256)
+        qsa.set_option("split_target", 0)
 
 
 # ---- contract rejection with fake (never dereferenced) device pointers ----

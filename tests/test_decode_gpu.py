@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _default_options():
     yield
-    qsa.set_option("split_target", 256)
+    qsa.set_option("split_target", 0)
     qsa.set_option("max_splits", 16)
     qsa.set_option("min_split_keys", 256)
     qsa.set_option("waves_per_workgroup", 4)

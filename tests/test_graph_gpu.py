@@ -113,6 +113,6 @@ def test_capture_without_reserved_workspace_is_rejected(pools):
             with torch.cuda.graph(g):
                 qsa.decode(q, kd, vd, sel, cu)
     finally:
-        qsa.set_option("split_target", 256)
+        qsa.set_option("split_target", 0)
         qsa.set_option("max_splits", 16)
     torch.cuda.synchronize()
