@@ -97,7 +97,7 @@ typedef struct qsa_kv_scales {
  * qsa_decode -- one packed QSA decode step (one kernel launch).
  *
  *   q           [bs, Hq, 256] bf16.  1 <= bs <= 128; (Hq, Hkv) is (24, 2) or
- *               (12, 1).
+ *               (12, 1).  Rows must start on 16-byte boundaries.
  *   k_pool      [slots, Hkv, 256] bf16 | fp8_e4m3fn | i8, or
  *               [slots, Hkv, 128] u4x2.  v_pool: same dtype and shape.
  *               Rows must start on 16-byte boundaries.
@@ -107,7 +107,8 @@ typedef struct qsa_kv_scales {
  *   cu_seqlens  [bs + 1] int32, contiguous, read on the device only: row b
  *               is sel_indices[cu[b] .. cu[b+1]).  Changing it between graph
  *               replays needs no host involvement.
- *   out         [bs, Hq, 256] bf16, fully overwritten.
+ *   out         [bs, Hq, 256] bf16, fully overwritten.  Rows must start on
+ *               16-byte boundaries.
  *   lse         [bs, Hq] fp32, fully overwritten.
  *   stream      HIP stream the kernel is enqueued on (NULL = default).
  *

@@ -298,6 +298,8 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   if ((st = check_tensor(out, "out", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
   if (out->shape[0] != bs || out->shape[1] != hq || out->shape[2] != QSA_HEAD_DIM)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: out must be [bs, Hq, 256] like q");
+  if (!aligned16(out->data) || out->stride[0] % 8 || out->stride[1] % 8)
+    return fail(QSA_ERR_CONTRACT, "qsa_decode: out rows must start on 16-byte boundaries");
   // lse is written one float at a time: any strides
   if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2, false)) != QSA_OK) return st;
   if (lse->shape[0] != bs || lse->shape[1] != hq)

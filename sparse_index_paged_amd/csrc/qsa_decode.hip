@@ -15,15 +15,20 @@
 //   * workgroup = 4 waves = one (row b, KV head g, split s).  Each wave owns
 //     a contiguous slice of the list and runs its own online softmax over
 //     16-entry tiles; the 4 wave states are merged through LDS at the end.
+//   * Gather: each wave instruction loads 1 KB of whole K (or V) rows with
+//     16-byte loads, so the rows of a 16-entry tile arrive fully coalesced;
+//     they are dequantized to bf16 into the wave's LDS tiles while the next
+//     tile's rows are in flight.
 //   * QK as S^T = K . Q^T with v_mfma_f32_16x16x32_bf16: the A operand is 16
-//     K rows, loaded by each lane straight from the pool (row = lane % 16,
-//     8 channels per lane per MFMA), the B operand is Q (heads 12..15 zero).
+//     K rows read from the LDS tile (row = lane % 16, 8 channels per lane
+//     per MFMA), the B operand is Q from a tile shared by the workgroup
+//     (heads 12..15 zero).
 //     The result holds, in lane l, head l % 16 for list entries
 //     4*(l/16) + 0..3 -- exactly the B-operand layout of the PV product, so
 //     P never moves between lanes.
 //   * PV as O^T = V^T . P^T with v_mfma_f32_16x16x16_bf16: V^T needs the
-//     transpose of the gathered rows, so the V tile goes through a
-//     wave-private, XOR-swizzled LDS tile.  The accumulator O^T keeps head
+//     transpose of the gathered rows, which the wave reads column-wise from
+//     its LDS copy of the V tile.  The accumulator O^T keeps head
 //     l % 16 in lane l, the same lane that owns that head's running max and
 //     sum, so the rescale by exp(m_old - m_new) needs no shuffle.
 //   * P enters the PV product as a hi + lo bf16 pair (two MFMAs), so the
@@ -153,9 +158,12 @@ template <int W> struct Lds {
   static constexpr int kWave = 2 * kTileB + 2 * kScaleFloats * 4;
   static constexpr int kLoop = W * kWave;
   static constexpr int kQ = 16 * kLdsRow;
-  // merge of 4 wave states: m, l [4][16] and acc [4][12][256]; a workgroup of
-  // 8 waves first folds waves 4..7 into 0..3 through [4][16 f32x4][64 lanes]
-  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim + 16 * 4 + 16) * 4;
+  // merge of 4 wave states: m, l [4][16] and acc [4][12][256] (the split
+  // merge's per-wave weight tables [4][64][16] fit in the same bytes); a
+  // workgroup of 8 waves first folds waves 4..7 into 0..3 through
+  // [4][16 f32x4][64 lanes]
+  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim) * 4;
+  static_assert(kMerge4 >= 4 * 64 * 16 * 4, "split-merge weight tables exceed the merge area");
   static constexpr int kFold = (W > 4) ? 4 * (16 * 64 * 16 + 2 * 64 * 4) : 0;
   static constexpr int kMerge = kMerge4 > kFold ? kMerge4 : kFold;
   static constexpr int kBytes = (kLoop + kQ) > kMerge ? (kLoop + kQ) : kMerge;
@@ -176,10 +184,6 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
-  // after the merge each thread owns channel d = tid % 256 of heads
-  // h0, h0 + HS, ... (HS = threads / 256)
-  constexpr int HS = kThr / kHeadDim;
-  constexpr int NH = kGqa / HS;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
@@ -486,14 +490,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     __syncthreads();
   }
 
-  // ---- merge the (up to) 4 wave states of this workgroup through LDS.
-  // One thread per head computes the wave weights 2^(m_w - M), the merged
-  // max M and sum l once; every thread then combines its channel.
+  // ---- merge the (up to) 4 wave states of this workgroup through LDS
   float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
   float *red_l = red_m + 4 * 16;                    // [4][16]
   float *red_acc = red_l + 4 * 16;                  // [4][12][256]
-  f32x4 *red_f = reinterpret_cast<f32x4 *>(red_acc + 4 * kGqa * kHeadDim);  // [16] weights of waves 0..3
-  float *red_inv = reinterpret_cast<float *>(red_f + 16);                   // [16] 1 / l
   if (wave < 4) {
     if (qg == 0) {
       red_m[wave * 16 + r16] = m_run;
@@ -507,142 +507,179 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   }
   __syncthreads();
 
-  const int d = tid & (kHeadDim - 1);  // one channel per thread
-  const int h0 = tid >> 8;             // first head of this thread
-  __bf16 *orow = p.out + b * p.o_sb + (g * kGqa) * p.o_sh + d;
+  // From here wave wv < 4 owns heads wv, wv + 4, wv + 8 and lane l owns
+  // channels 4l .. 4l + 3 of each; the waves 4..7 of an 8-wave workgroup
+  // only take part in the barriers.  Weights are computed redundantly per
+  // wave: lane j = 16 w + h holds state w of head h, so the merged max, sum
+  // and reciprocal of head h end up in lanes h, h + 16, h + 32, h + 48 and
+  // are read out with readlane (no extra barrier).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int sq = lane >> 4;  // state (wave or split) index within a group of 4
+  const int hh = lane & 15;  // head
+  auto bcast = [](float x, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+  };
+  auto weights4 = [&](float mj, float lj, float &Mj, float &sj) {
+    Mj = fmaxf(mj, __shfl_xor(mj, 16));
+    Mj = fmaxf(Mj, __shfl_xor(Mj, 32));
+    const float fj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - Mj);
+    sj = fj * lj;
+    sj += __shfl_xor(sj, 16);
+    sj += __shfl_xor(sj, 32);
+    return fj;
+  };
+  auto recip = [](float s) { return (s > 0.f || s != s) ? 1.0f / s : 0.f; };
+  auto lse_of = [](float M, float s) { return (s > 0.f || s != s) ? (M + __log2f(s)) * kLn2 : -INFINITY; };
+  auto store_out = [&](int h, const f32x4 &o, float inv) {
+    uint2 w;
+    w.x = f32_to_bf16_rne(o[0] * inv) | (f32_to_bf16_rne(o[1] * inv) << 16);
+    w.y = f32_to_bf16_rne(o[2] * inv) | (f32_to_bf16_rne(o[3] * inv) << 16);
+    *reinterpret_cast<uint2 *>(p.out + b * p.o_sb + (g * kGqa + h) * p.o_sh + 4 * lane) = w;
+  };
   float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
-  float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
-  if (tid < kGqa) {
-    const int h = tid;
-    float M = -INFINITY;
+
+  float Mw = 0.f, sw = 0.f;
+  f32x4 o[3];
+  if (wv < 4) {
+    const float fj = weights4(red_m[lane], red_l[lane], Mw, sw);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + h]);
-    f32x4 f;
-    float lsum = 0.f;
+    for (int k = 0; k < 3; ++k) {
+      const int h = 4 * k + wv;
+      o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = red_m[w * 16 + h];
-      f[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      lsum += f[w] * red_l[w * 16 + h];
+      for (int w = 0; w < 4; ++w)
+        o[k] += bcast(fj, 16 * w + h) *
+                *reinterpret_cast<const f32x4 *>(red_acc + (w * kGqa + h) * kHeadDim + 4 * lane);
     }
-    red_f[h] = f;
-    const bool any = lsum > 0.f || lsum != lsum;
-    red_inv[h] = any ? 1.0f / lsum : 0.f;
-    if (n_active == 1) {
-      lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
-    } else {
-      __hip_atomic_store(part + h, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(part + 16 + h, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-  float o_un[NH];
-#pragma unroll
-  for (int i = 0; i < NH; ++i) {
-    const int h = h0 + i * HS;
-    const f32x4 f = red_f[h];
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o += f[w] * red_acc[(w * kGqa + h) * kHeadDim + d];
-    o_un[i] = o;
   }
 
   if (n_active == 1) {
+    if (wv < 4) {
+      const float invj = recip(sw);
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int h = h0 + i * HS;
-      orow[h * p.o_sh] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o_un[i] * red_inv[h])));
+      for (int k = 0; k < 3; ++k) store_out(4 * k + wv, o[k], bcast(invj, 4 * k + wv));
+      if (wv == 0 && lane < kGqa) lrow[lane * p.l_sh] = lse_of(Mw, sw);
     }
     return;
   }
 
   // ---- split partial, then the last arriver merges all splits in order.
-  // Partials are written and read with device-scope (sc1) accesses, which
-  // are coherent across XCDs without writing back or invalidating whole L2
-  // caches; each wave waits for its stores to be acknowledged before the
-  // workgroup barrier, and one device-scope atomic per workgroup counts the
-  // arrivals.  The split that sees count n_active - 1 is the last one.
-  // (m and l of each head were stored above by the thread owning the head.)
+  // A partial is m[16], l[16] (log2 domain) and the unnormalised
+  // accumulator laid out [head][4][64 lanes], so every store and load of a
+  // wave covers 256 contiguous bytes.  Partials are written and read with
+  // device-scope (sc1) accesses, which are coherent across XCDs without
+  // writing back or invalidating whole L2 caches; each wave waits for its
+  // stores to be acknowledged before the workgroup barrier, and one
+  // device-scope atomic per workgroup counts the arrivals.  The split that
+  // sees count n_active - 1 is the last one.
+  auto st = [](float *ptr, float x) { __hip_atomic_store(ptr, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
+  if (wv < 4) {
+    float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
+    if (wv == 0 && lane < 16) {
+      st(part + lane, Mw);
+      st(part + 16 + lane, sw);
+    }
 #pragma unroll
-  for (int i = 0; i < NH; ++i)
-    __hip_atomic_store(part + 32 + (h0 + i * HS) * kHeadDim + d, o_un[i], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st(part + 32 + ((4 * k + wv) * 4 + i) * 64 + lane, o[k][i]);
+  }
+  // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained); as a builtin, the
+  // compiler's own wait tracking knows that no load is outstanding after it
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (tid == 0) {
     const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<uint32_t>(n_active - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last || wv >= 4) return;
 
-  // (a) one round of loads: the accumulators of the first (up to) 4 splits
-  // into registers and m, l of every split into LDS
-  auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
-  float *sm_ml = reinterpret_cast<float *>(smem);            // [n_active][32]
-  float *sm_w = sm_ml + 64 * 32;                             // [n_active][16]
-  float *sm_inv = sm_w + 64 * 16;                            // [16] 1 / l
-  auto acc_ptr = [&](int sp, int i) { return pbase + sp * kPartFloats + 32 + (h0 + i * HS) * kHeadDim + d; };
-  const int nfirst = n_active < 4 ? n_active : 4;
-  float a0[4][NH];
+  // (a) m and l of every split: lane j = 16 s' + h of round r holds split
+  // 4r + s' (at most 64 splits = 16 rounds), issued together with the
+  // accumulators of the first 8 splits
+  constexpr int kBatch = 8;
+  const int nround = (n_active + 3) >> 2;
+  // (rounds past the last split re-read the last split and are masked)
+  float mr[16], lr[16];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int i = 0; i < NH; ++i) a0[u][i] = (u < nfirst) ? ld(acc_ptr(u, i)) : 0.f;
-  for (int i = tid; i < n_active * 32; i += kThr) sm_ml[i] = ld(pbase + (i >> 5) * kPartFloats + (i & 31));
-  __syncthreads();
-  // (b) per head: merged max, normaliser, each split's weight, lse
-  if (tid < kGqa) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < n_active; ++s) M = fmaxf(M, sm_ml[s * 32 + h]);
-    float lsum = 0.f;
-    for (int s = 0; s < n_active; ++s) {
-      const float ms = sm_ml[s * 32 + h];
-      const float f = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      sm_w[s * 16 + h] = f;
-      lsum += f * sm_ml[s * 32 + 16 + h];
+  for (int r = 0; r < 16; ++r) {
+    if (r < nround) {
+      const int s = min(4 * r + sq, n_active - 1);
+      mr[r] = ld(pbase + s * kPartFloats + hh);
+      lr[r] = ld(pbase + s * kPartFloats + 16 + hh);
     }
-    const bool any = lsum > 0.f || lsum != lsum;
-    sm_inv[h] = any ? 1.0f / lsum : 0.f;
-    lrow[h * p.l_sh] = any ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
-  __syncthreads();
-  // (c) out = (sum_s w_s acc_s) / l, splits in index order; splits past the
-  // first four are loaded 4 at a time
-  float o[NH];
+  auto acc_ld = [&](int s, int k, int i) { return ld(pbase + s * kPartFloats + 32 + ((4 * k + wv) * 4 + i) * 64 + lane); };
+  // (a split's registers are only written and read when the split exists)
+  f32x4 a[kBatch][3];
 #pragma unroll
-  for (int i = 0; i < NH; ++i) o[i] = 0.f;
+  for (int u = 0; u < kBatch; ++u)
+    if (u < n_active) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (u < nfirst) {
+      for (int k = 0; k < 3; ++k)
 #pragma unroll
-      for (int i = 0; i < NH; ++i) o[i] += sm_w[u * 16 + h0 + i * HS] * a0[u][i];
+        for (int i = 0; i < 4; ++i) a[u][k][i] = acc_ld(u, k, i);
     }
-  int s = nfirst;
-  for (; s + 4 <= n_active; s += 4) {
-    float a[4][NH];
+
+  // (b) per head: merged max, each split's weight (into this wave's LDS
+  // table wf[split][16]), sum and reciprocal
+  float M = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < NH; ++i) a[u][i] = ld(acc_ptr(s + u, i));
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < NH; ++i) o[i] += sm_w[(s + u) * 16 + h0 + i * HS] * a[u][i];
+  for (int r = 0; r < 16; ++r) {
+    if (r < nround) {
+      if (4 * r + sq >= n_active) mr[r] = -INFINITY;
+      M = fmaxf(M, mr[r]);
+    }
   }
-  for (; s < n_active; ++s) {
-    float a[NH];
+  M = fmaxf(M, __shfl_xor(M, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  float *wf = reinterpret_cast<float *>(smem) + wv * 64 * 16;
+  float ssum = 0.f;
 #pragma unroll
-    for (int i = 0; i < NH; ++i) a[i] = ld(acc_ptr(s, i));
-#pragma unroll
-    for (int i = 0; i < NH; ++i) o[i] += sm_w[s * 16 + h0 + i * HS] * a[i];
+  for (int r = 0; r < 16; ++r) {
+    if (r < nround) {
+      const float f = (mr[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr[r] - M);
+      wf[r * 64 + lane] = f;
+      ssum += f * lr[r];
+    }
   }
+  ssum += __shfl_xor(ssum, 16);
+  ssum += __shfl_xor(ssum, 32);
+  wave_lds_fence();
+
+  // (c) out = (sum_s w_s acc_s) / l with the splits in index order
+  f32x4 acc_o[3];
 #pragma unroll
-  for (int i = 0; i < NH; ++i)
-    orow[(h0 + i * HS) * p.o_sh] =
-        __builtin_bit_cast(__bf16, static_cast<uint16_t>(f32_to_bf16_rne(o[i] * sm_inv[h0 + i * HS])));
+  for (int k = 0; k < 3; ++k) acc_o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    if (u < n_active) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) acc_o[k] += wf[u * 16 + 4 * k + wv] * a[u][k];
+    }
+  for (int s0 = kBatch; s0 < n_active; s0 += kBatch) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < n_active) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[u][k][i] = acc_ld(s0 + u, k, i);
+      }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < n_active) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) acc_o[k] += wf[(s0 + u) * 16 + 4 * k + wv] * a[u][k];
+      }
+  }
+  const float invj = recip(ssum);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) store_out(4 * k + wv, acc_o[k], bcast(invj, 4 * k + wv));
+  if (wv == 0 && lane < kGqa) lrow[lane * p.l_sh] = lse_of(M, ssum);
   if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
