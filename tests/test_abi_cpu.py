@@ -101,7 +101,7 @@ def _t(shape, dtype, strides=None, data=FAKE):
 
 def _call(bs=4, hq=24, hkv=2, d=256, slots=64, pool_dtype=B.BF16, v_dtype=None, scales=None,
           q_dtype=B.BF16, cu_len=None, pool_data=FAKE, q_strides=None, out_shape=None,
-          lse_shape=None, sel_dtype=B.I32, pool_strides=None):
+          lse_shape=None, sel_dtype=B.I32, pool_strides=None, out_data=FAKE, out_strides=None):
     lib = qsa.load_library()
     row = d if pool_dtype != B.U4X2 else d // 2
     q = _t((bs, hq, d), q_dtype, q_strides)
@@ -109,7 +109,7 @@ def _call(bs=4, hq=24, hkv=2, d=256, slots=64, pool_dtype=B.BF16, v_dtype=None, 
     v = _t((slots, hkv, row), v_dtype or pool_dtype, pool_strides)
     sel = _t((100,), sel_dtype)
     cu = _t(((cu_len if cu_len is not None else bs + 1),), B.I32)
-    out = _t(out_shape or (bs, hq, d), B.BF16)
+    out = _t(out_shape or (bs, hq, d), B.BF16, out_strides, data=out_data)
     lse = _t(lse_shape or (bs, hq), B.F32)
     st = lib.qsa_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                         ctypes.byref(scales) if scales is not None else None, ctypes.byref(sel),
@@ -140,6 +140,8 @@ def _scales(slots=64, hkv=2, group=256, dtype=B.F32):
     (dict(pool_data=FAKE + 8), "16-byte boundaries"),
     (dict(q_strides=(24 * 256, 256, 2)), "contiguous in its last dimension"),
     (dict(out_shape=(4, 24, 128)), "out must be"),
+    (dict(out_data=FAKE + 8), "out rows must start on 16-byte boundaries"),
+    (dict(out_strides=(24 * 260, 260, 1)), "out rows must start on 16-byte boundaries"),
     (dict(lse_shape=(4, 12)), "lse must be"),
     (dict(sel_dtype=B.F32), "sel_indices must be i32"),
 ])
