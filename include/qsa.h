@@ -50,7 +50,7 @@ extern "C" {
 /* Same declaration as in the HIP runtime headers. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 #define QSA_HEAD_DIM 256
 #define QSA_GQA 12
 #define QSA_MAX_SEL 2055
@@ -71,8 +71,9 @@ typedef enum qsa_dtype {
   QSA_DTYPE_I32 = 4,
   QSA_DTYPE_FP8_E4M3FN = 5, /* OCP e4m3fn, one code per byte                  */
   QSA_DTYPE_I8 = 6,         /* signed 8-bit codes                             */
-  QSA_DTYPE_U4X2 = 7        /* two 4-bit codes per byte: channel 2i in the low
+  QSA_DTYPE_U4X2 = 7,       /* two 4-bit codes per byte: channel 2i in the low
                                nibble, 2i+1 in the high nibble, value = nibble-8 */
+  QSA_DTYPE_I64 = 8
 } qsa_dtype;
 
 /* A strided device tensor of up to 4 dimensions. */
@@ -85,8 +86,9 @@ typedef struct qsa_tensor {
 } qsa_tensor;
 
 /* Scales of a quantized pool pair: k_scale / v_scale are
- * [slots, Hkv, 256 / group_size] of QSA_DTYPE_F32.  group_size is 256 (one
- * scale per row), 64 or 32 (int4 requires 32 or 64). */
+ * [slots, Hkv, 256 / group_size], both QSA_DTYPE_F32 or both QSA_DTYPE_F16
+ * (the pages store fp16 scales).  group_size is 256 (one scale per row), 64
+ * or 32 (int4 requires 32 or 64). */
 typedef struct qsa_kv_scales {
   qsa_tensor k_scale;
   qsa_tensor v_scale;
@@ -122,6 +124,39 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
                       const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
                       const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
                       qsa_tensor *out, qsa_tensor *lse, hipStream_t stream);
+
+/*
+ * qsa_kv_store -- quantize new K/V rows and scatter them into the pools
+ * (one kernel launch; page "feat(qsa): quantized KV pools with
+ * dequant-on-gather (fp8/int8/int4)", part 4 "Modifications": the write is
+ * one fused quantize + scatter launch).
+ *
+ *   k_new, v_new [n, Hkv, 256] bf16, rows on 16-byte boundaries.  n may be 0.
+ *   loc          [n] int32 or int64 slot ids, contiguous: row t of k_new /
+ *                v_new is written to pool slot loc[t] (all Hkv heads).  The
+ *                ids of one call must be distinct; with a repeated id the
+ *                slot holds an unspecified mix of the rows written to it.
+ *   k_pool, v_pool, kv_scales  as for qsa_decode; written in place.
+ *
+ * Per (token, KV head, group of group_size channels), in fp32 with ties to
+ * even:
+ *   i8     scale = absmax / 127, code = clamp(rint(x / scale), -127, 127)
+ *   u4x2   scale = absmax / 7,   q = clamp(rint(x / scale), -7, 7), stored
+ *          as the nibble q + 8
+ *   fp8    scale = absmax / 448, code = e4m3fn(clamp(x / scale, -448, 448))
+ *   bf16   the row is copied unchanged (kv_scales must be NULL)
+ * An f16 scale is min(scale, 65504) rounded to f16, and the codes are
+ * computed from the scale as stored.  A zero scale gives zero codes.
+ * Non-finite inputs are outside the contract.
+ *
+ * A slot id outside [0, slots) skips that token (nothing is written for it)
+ * and sets bit 2 of the device error word.  Uses the device workspace's
+ * error word only: outside capture it is created on first use; under
+ * capture it must exist already (QSA_ERR_WORKSPACE otherwise).
+ */
+qsa_status qsa_kv_store(const qsa_tensor *k_new, const qsa_tensor *v_new,
+                        const qsa_tensor *loc, qsa_tensor *k_pool, qsa_tensor *v_pool,
+                        const qsa_kv_scales *kv_scales, hipStream_t stream);
 
 /* Create (or grow) the current device's workspace for calls with up to
  * max_bs rows and the given head layout, and zero its counters.  Call it
@@ -174,7 +209,8 @@ qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream);
 
 /* Copy the sticky device error word to *host_word (synchronises `stream`).
  * Bit 0: a row's cu_seqlens were out of range or longer than 2055.
- * Bit 1: a slot id was outside [0, slots). */
+ * Bit 1: a slot id was outside [0, slots).
+ * Bit 2: a qsa_kv_store slot id was outside [0, slots). */
 qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream);
 
 int qsa_abi_version(void);

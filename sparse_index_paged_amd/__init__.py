@@ -1,7 +1,8 @@
 """Packed QSA decode for AMD Instinct MI355X (gfx950).
 
 Thin ctypes binding over ``libqsa.so`` (built from ``csrc/`` by
-``build.py``).  Every step of the decode runs in the library's HIP kernel;
+``build.py``).  Every step of the decode and of the quantize + scatter
+write runs in the library's HIP kernels;
 this module only turns torch tensors into ``qsa_tensor`` descriptors and
 passes torch's current HIP stream.  If the library is missing the import of
 ``decode`` fails loudly -- there is no fallback.
@@ -17,6 +18,7 @@ from ._binding import (  # noqa: F401
     debug_device_error,
     decode,
     get_option,
+    kv_store,
     lib_path,
     load_library,
     plan,
@@ -28,7 +30,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "decode", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
+    "decode", "kv_store", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
     "ABI_VERSION",

@@ -7,16 +7,16 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "libqsa.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # qsa_dtype
-BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2 = 1, 2, 3, 4, 5, 6, 7
+BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2, I64 = 1, 2, 3, 4, 5, 6, 7, 8
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORKSPACE",
           4: "QSA_ERR_HIP"}
 
 EXPORTS = (
-    "qsa_decode", "qsa_workspace_reserve", "qsa_workspace_reset", "qsa_workspace_release",
-    "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
+    "qsa_decode", "qsa_kv_store", "qsa_workspace_reserve", "qsa_workspace_reset",
+    "qsa_workspace_release", "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
     "qsa_debug_counters", "qsa_debug_read_counters", "qsa_debug_audit_counters",
     "qsa_debug_device_error", "qsa_abi_version",
 )
@@ -58,6 +58,8 @@ def load_library():
     T = P(QsaTensor)
     lib.qsa_decode.restype = ctypes.c_int
     lib.qsa_decode.argtypes = [T, T, T, P(QsaKvScales), T, T, T, T, ctypes.c_void_p]
+    lib.qsa_kv_store.restype = ctypes.c_int
+    lib.qsa_kv_store.argtypes = [T, T, T, T, T, P(QsaKvScales), ctypes.c_void_p]
     lib.qsa_workspace_reserve.restype = ctypes.c_int
     lib.qsa_workspace_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.qsa_workspace_reset.restype = ctypes.c_int
@@ -99,7 +101,7 @@ def _torch_dtype_code(t, kv_format: str | None = None) -> int:
     if kv_format is not None:
         return {"bf16": BF16, "fp8": FP8_E4M3FN, "int8": I8, "int4": U4X2}[kv_format]
     m = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32,
-         torch.int8: I8}
+         torch.int8: I8, torch.int64: I64}
     fp8 = getattr(torch, "float8_e4m3fn", None)
     if fp8 is not None:
         m[fp8] = FP8_E4M3FN
@@ -137,7 +139,7 @@ def decode(q, k_pool, v_pool, sel, cu_seqlens, *, out=None, lse=None, kv_format:
     kv_format: "bf16" | "fp8" (e4m3fn bytes, torch.uint8 or float8_e4m3fn)
     | "int8" (torch.int8) | "int4" (torch.uint8 [slots, Hkv, 128]).
     Quantized formats take k_scale / v_scale [slots, Hkv, 256 // group_size]
-    float32."""
+    float32 or float16."""
     import torch
     lib = load_library()
     bs, hq = q.shape[0], q.shape[1]
@@ -149,18 +151,38 @@ def decode(q, k_pool, v_pool, sel, cu_seqlens, *, out=None, lse=None, kv_format:
     kd = describe(k_pool, kv_format)
     vd = describe(v_pool, kv_format)
     sd, cd = describe(sel), describe(cu_seqlens)
-    scales = None
-    if kv_format != "bf16":
-        if k_scale is None or v_scale is None:
-            raise ValueError(f"{kv_format} pools need k_scale and v_scale")
-        g = group_size if group_size is not None else 256 // k_scale.shape[-1]
-        scales = QsaKvScales(describe(k_scale), describe(v_scale), g)
+    scales = _scales(kv_format, k_scale, v_scale, group_size)
     st = lib.qsa_decode(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
                         ctypes.byref(scales) if scales is not None else None,
                         ctypes.byref(sd), ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
                         _stream_handle(stream))
     _check(st)
     return out, lse
+
+
+def _scales(kv_format, k_scale, v_scale, group_size):
+    if kv_format == "bf16":
+        return None
+    if k_scale is None or v_scale is None:
+        raise ValueError(f"{kv_format} pools need k_scale and v_scale")
+    g = group_size if group_size is not None else 256 // k_scale.shape[-1]
+    return QsaKvScales(describe(k_scale), describe(v_scale), g)
+
+
+def kv_store(k_new, v_new, loc, k_pool, v_pool, *, kv_format: str = "bf16", k_scale=None,
+             v_scale=None, group_size: int | None = None, stream=None):
+    """Quantize k_new / v_new [n, Hkv, 256] bf16 and scatter row t to pool
+    slot loc[t] (int32 or int64, distinct ids), writing codes and scales in
+    place (one kernel launch on `stream`)."""
+    lib = load_library()
+    kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
+    kpd = describe(k_pool, kv_format)
+    vpd = describe(v_pool, kv_format)
+    scales = _scales(kv_format, k_scale, v_scale, group_size)
+    st = lib.qsa_kv_store(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld), ctypes.byref(kpd),
+                          ctypes.byref(vpd), ctypes.byref(scales) if scales is not None else None,
+                          _stream_handle(stream))
+    _check(st)
 
 
 def workspace_reserve(max_bs: int, hq: int, hkv: int, stream=None):

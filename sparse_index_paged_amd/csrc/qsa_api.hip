@@ -117,7 +117,7 @@ bool stream_capturing(hipStream_t stream) {
 
 // Ensure the current device's workspace holds `floats` partial floats.
 qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
-                            Workspace **out) {
+                            Workspace **out, const char *fn = "qsa_decode") {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace &ws = g_ws[dev];
   if (ws.words != nullptr && ws.part_floats >= floats) {
@@ -126,9 +126,9 @@ qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool al
   }
   if (!allow_alloc)
     return fail(QSA_ERR_WORKSPACE,
-                "qsa_decode: the stream is capturing and the device %d workspace holds %lld "
+                "%s: the stream is capturing and the device %d workspace holds %lld "
                 "partial floats, %lld needed; call qsa_workspace_reserve before capture",
-                dev, static_cast<long long>(ws.part_floats), static_cast<long long>(floats));
+                fn, dev, static_cast<long long>(ws.part_floats), static_cast<long long>(floats));
   if (ws.words != nullptr) {
     if (hipDeviceSynchronize() != hipSuccess)
       return fail(QSA_ERR_HIP, "workspace: hipDeviceSynchronize failed");
@@ -164,6 +164,7 @@ const char *dtype_name(int32_t dt) {
     case QSA_DTYPE_FP8_E4M3FN: return "fp8_e4m3fn";
     case QSA_DTYPE_I8: return "i8";
     case QSA_DTYPE_U4X2: return "u4x2";
+    case QSA_DTYPE_I64: return "i64";
     default: return "unknown";
   }
 }
@@ -174,6 +175,7 @@ int64_t dtype_bytes(int32_t dt) {
     case QSA_DTYPE_F16: return 2;
     case QSA_DTYPE_F32:
     case QSA_DTYPE_I32: return 4;
+    case QSA_DTYPE_I64: return 8;
     case QSA_DTYPE_FP8_E4M3FN:
     case QSA_DTYPE_I8:
     case QSA_DTYPE_U4X2: return 1;
@@ -182,25 +184,118 @@ int64_t dtype_bytes(int32_t dt) {
 }
 
 qsa_status check_tensor(const qsa_tensor *t, const char *name, int32_t dtype, int ndim,
-                        bool last_dim_contiguous = true) {
-  if (t == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s is NULL", name);
-  if (t->data == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: %s.data is NULL", name);
+                        bool last_dim_contiguous = true, const char *fn = "qsa_decode") {
+  if (t == nullptr) return fail(QSA_ERR_ARG, "%s: %s is NULL", fn, name);
+  if (t->data == nullptr) return fail(QSA_ERR_ARG, "%s: %s.data is NULL", fn, name);
   if (t->dtype != dtype)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must be %s, got %s", name, dtype_name(dtype),
+    return fail(QSA_ERR_CONTRACT, "%s: %s must be %s, got %s", fn, name, dtype_name(dtype),
                 dtype_name(t->dtype));
   if (t->ndim != ndim)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must have %d dimensions, got %d", name, ndim,
+    return fail(QSA_ERR_CONTRACT, "%s: %s must have %d dimensions, got %d", fn, name, ndim,
                 t->ndim);
   for (int i = 0; i < ndim; ++i) {
-    if (t->shape[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.shape[%d] < 0", name, i);
-    if (t->stride[i] < 0) return fail(QSA_ERR_CONTRACT, "qsa_decode: %s.stride[%d] < 0", name, i);
+    if (t->shape[i] < 0) return fail(QSA_ERR_CONTRACT, "%s: %s.shape[%d] < 0", fn, name, i);
+    if (t->stride[i] < 0) return fail(QSA_ERR_CONTRACT, "%s: %s.stride[%d] < 0", fn, name, i);
   }
   if (last_dim_contiguous && t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: %s must be contiguous in its last dimension", name);
+    return fail(QSA_ERR_CONTRACT, "%s: %s must be contiguous in its last dimension", fn, name);
   return QSA_OK;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A pair of K/V pools and their scales, as validated for decode and store.
+struct PoolDesc {
+  int32_t dtype = 0;
+  int fmt = qsa::kFmtBF16, group = QSA_HEAD_DIM;
+  int64_t slots = 0, hkv = 0, eb = 0;  // eb: bytes per pool element
+  const qsa_tensor *k = nullptr, *v = nullptr;
+  uint8_t *ks = nullptr, *vs = nullptr;
+  int64_t ks_ss = 0, ks_sh = 0, vs_ss = 0, vs_sh = 0;  // bytes
+  int scale_f16 = 0;
+};
+
+// Pools: bf16 | fp8_e4m3fn | i8 [slots, Hkv, 256] or u4x2 [slots, Hkv, 128],
+// one format for K and V, Hkv 1 or 2, rows on 16-byte boundaries.  Scales:
+// absent for bf16, else f32 or f16 [slots, Hkv, 256 / group] for both.
+qsa_status check_pools(const char *fn, const qsa_tensor *k_pool, const qsa_tensor *v_pool,
+                       const qsa_kv_scales *kv_scales, PoolDesc *d) {
+  qsa_status st;
+  if (k_pool == nullptr || v_pool == nullptr) return fail(QSA_ERR_ARG, "%s: a pool is NULL", fn);
+  const int32_t pdt = k_pool->dtype;
+  if (pdt != QSA_DTYPE_BF16 && pdt != QSA_DTYPE_FP8_E4M3FN && pdt != QSA_DTYPE_I8 &&
+      pdt != QSA_DTYPE_U4X2)
+    return fail(QSA_ERR_CONTRACT, "%s: k_pool dtype %s is not bf16, fp8_e4m3fn, i8 or u4x2", fn,
+                dtype_name(pdt));
+  if (v_pool->dtype != pdt)
+    return fail(QSA_ERR_CONTRACT, "%s: k_pool (%s) and v_pool (%s) must share a format", fn,
+                dtype_name(pdt), dtype_name(v_pool->dtype));
+  if ((st = check_tensor(k_pool, "k_pool", pdt, 3, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(v_pool, "v_pool", pdt, 3, true, fn)) != QSA_OK) return st;
+  const int64_t slots = k_pool->shape[0], hkv = k_pool->shape[1];
+  const int64_t row_elems = (pdt == QSA_DTYPE_U4X2) ? QSA_HEAD_DIM / 2 : QSA_HEAD_DIM;
+  if (hkv != 1 && hkv != 2)
+    return fail(QSA_ERR_CONTRACT, "%s: pools must hold 1 or 2 KV heads, got %lld", fn,
+                static_cast<long long>(hkv));
+  if (k_pool->shape[2] != row_elems || v_pool->shape[2] != row_elems)
+    return fail(QSA_ERR_CONTRACT, "%s: pool rows must hold %lld %s elements (head dim 256)", fn,
+                static_cast<long long>(row_elems), dtype_name(pdt));
+  if (v_pool->shape[0] != slots || v_pool->shape[1] != hkv)
+    return fail(QSA_ERR_CONTRACT, "%s: k_pool and v_pool shapes differ", fn);
+  if (slots < 1) return fail(QSA_ERR_CONTRACT, "%s: the pools hold no slots", fn);
+  if (slots > 0x7FFFFFFFLL)
+    return fail(QSA_ERR_CONTRACT, "%s: more than 2^31-1 slots cannot be named by int32 ids", fn);
+  const int64_t eb = dtype_bytes(pdt);
+  if (!aligned16(k_pool->data) || !aligned16(v_pool->data) || (k_pool->stride[0] * eb) % 16 ||
+      (k_pool->stride[1] * eb) % 16 || (v_pool->stride[0] * eb) % 16 || (v_pool->stride[1] * eb) % 16)
+    return fail(QSA_ERR_CONTRACT, "%s: pool rows must start on 16-byte boundaries", fn);
+
+  *d = PoolDesc{};
+  d->dtype = pdt;
+  d->slots = slots;
+  d->hkv = hkv;
+  d->eb = eb;
+  d->k = k_pool;
+  d->v = v_pool;
+  if (pdt == QSA_DTYPE_BF16) {
+    if (kv_scales != nullptr)
+      return fail(QSA_ERR_CONTRACT, "%s: bf16 pools take no scales (kv_scales must be NULL)", fn);
+    return QSA_OK;
+  }
+  d->fmt = pdt == QSA_DTYPE_FP8_E4M3FN ? qsa::kFmtFP8 : pdt == QSA_DTYPE_I8 ? qsa::kFmtINT8 : qsa::kFmtINT4;
+  if (kv_scales == nullptr) return fail(QSA_ERR_CONTRACT, "%s: %s pools need kv_scales", fn, dtype_name(pdt));
+  const int group = kv_scales->group_size;
+  const bool g_ok = (d->fmt == qsa::kFmtINT4) ? (group == 32 || group == 64)
+                                              : (group == 32 || group == 64 || group == 256);
+  if (!g_ok)
+    return fail(QSA_ERR_CONTRACT, "%s: group_size %d is not supported for %s pools "
+                "(fp8/i8: 32, 64, 256; u4x2: 32, 64)", fn, group, dtype_name(pdt));
+  d->group = group;
+  const int32_t sdt = kv_scales->k_scale.dtype;
+  if (sdt != QSA_DTYPE_F32 && sdt != QSA_DTYPE_F16)
+    return fail(QSA_ERR_CONTRACT, "%s: k_scale must be f32 or f16, got %s", fn, dtype_name(sdt));
+  if ((st = check_tensor(&kv_scales->k_scale, "k_scale", sdt, 3, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(&kv_scales->v_scale, "v_scale", sdt, 3, true, fn)) != QSA_OK) return st;
+  const int64_t ng = QSA_HEAD_DIM / group;
+  for (const qsa_tensor *t : {&kv_scales->k_scale, &kv_scales->v_scale})
+    if (t->shape[0] != slots || t->shape[1] != hkv || t->shape[2] != ng)
+      return fail(QSA_ERR_CONTRACT, "%s: scales must be [slots, Hkv, 256/group] = "
+                  "[%lld, %lld, %lld]", fn, static_cast<long long>(slots),
+                  static_cast<long long>(hkv), static_cast<long long>(ng));
+  const int64_t sb = dtype_bytes(sdt);
+  if ((reinterpret_cast<uintptr_t>(kv_scales->k_scale.data) % sb) ||
+      (reinterpret_cast<uintptr_t>(kv_scales->v_scale.data) % sb))
+    return fail(QSA_ERR_CONTRACT, "%s: scale data must be aligned to its element size", fn);
+  d->scale_f16 = sdt == QSA_DTYPE_F16;
+  d->ks = static_cast<uint8_t *>(kv_scales->k_scale.data);
+  d->vs = static_cast<uint8_t *>(kv_scales->v_scale.data);
+  d->ks_ss = kv_scales->k_scale.stride[0] * sb;
+  d->ks_sh = kv_scales->k_scale.stride[1] * sb;
+  d->vs_ss = kv_scales->v_scale.stride[0] * sb;
+  d->vs_sh = kv_scales->v_scale.stride[1] * sb;
+  return QSA_OK;
+}
+
 
 }  // namespace
 
@@ -263,35 +358,13 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   if (bs < 1 || bs > QSA_MAX_BS)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: bs must be in [1, 128], got %lld",
                 static_cast<long long>(bs));
-  if (k_pool == nullptr || v_pool == nullptr) return fail(QSA_ERR_ARG, "qsa_decode: a pool is NULL");
-  const int32_t pdt = k_pool->dtype;
-  if (pdt != QSA_DTYPE_BF16 && pdt != QSA_DTYPE_FP8_E4M3FN && pdt != QSA_DTYPE_I8 &&
-      pdt != QSA_DTYPE_U4X2)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool dtype %s is not bf16, fp8_e4m3fn, i8 or u4x2",
-                dtype_name(pdt));
-  if (v_pool->dtype != pdt)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool (%s) and v_pool (%s) must share a format",
-                dtype_name(pdt), dtype_name(v_pool->dtype));
-  if ((st = check_tensor(k_pool, "k_pool", pdt, 3)) != QSA_OK) return st;
-  if ((st = check_tensor(v_pool, "v_pool", pdt, 3)) != QSA_OK) return st;
-  const int64_t slots = k_pool->shape[0], hkv = k_pool->shape[1];
-  const int64_t row_elems = (pdt == QSA_DTYPE_U4X2) ? QSA_HEAD_DIM / 2 : QSA_HEAD_DIM;
+  PoolDesc pd;
+  if ((st = check_pools("qsa_decode", k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
+  const int64_t slots = pd.slots, hkv = pd.hkv, eb = pd.eb;
   if (!((hq == 24 && hkv == 2) || (hq == 12 && hkv == 1)))
     return fail(QSA_ERR_CONTRACT,
                 "qsa_decode: (Hq, Hkv) must be (24, 2) or (12, 1) (12:1 GQA), got (%lld, %lld)",
                 static_cast<long long>(hq), static_cast<long long>(hkv));
-  if (k_pool->shape[2] != row_elems || v_pool->shape[2] != row_elems)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: pool rows must hold %lld %s elements (head dim 256)",
-                static_cast<long long>(row_elems), dtype_name(pdt));
-  if (v_pool->shape[0] != slots || v_pool->shape[1] != hkv)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: k_pool and v_pool shapes differ");
-  if (slots < 1) return fail(QSA_ERR_CONTRACT, "qsa_decode: the pools hold no slots");
-  if (slots > 0x7FFFFFFFLL)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: more than 2^31-1 slots cannot be named by int32 ids");
-  const int64_t eb = dtype_bytes(pdt);
-  if (!aligned16(k_pool->data) || !aligned16(v_pool->data) || (k_pool->stride[0] * eb) % 16 ||
-      (k_pool->stride[1] * eb) % 16 || (v_pool->stride[0] * eb) % 16 || (v_pool->stride[1] * eb) % 16)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: pool rows must start on 16-byte boundaries");
   if (!aligned16(q->data) || q->stride[0] % 8 || q->stride[1] % 8)
     return fail(QSA_ERR_CONTRACT, "qsa_decode: q rows must start on 16-byte boundaries");
 
@@ -312,39 +385,6 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
     return fail(QSA_ERR_CONTRACT, "qsa_decode: cu_seqlens must have bs + 1 = %lld entries, got %lld",
                 static_cast<long long>(bs + 1), static_cast<long long>(cu_seqlens->shape[0]));
 
-  // -- scales
-  int fmt = qsa::kFmtBF16, group = QSA_HEAD_DIM;
-  const float *ks = nullptr, *vs = nullptr;
-  int64_t ks_ss = 0, ks_sh = 0, vs_ss = 0, vs_sh = 0;
-  if (pdt == QSA_DTYPE_BF16) {
-    if (kv_scales != nullptr)
-      return fail(QSA_ERR_CONTRACT, "qsa_decode: bf16 pools take no scales (kv_scales must be NULL)");
-  } else {
-    fmt = pdt == QSA_DTYPE_FP8_E4M3FN ? qsa::kFmtFP8 : pdt == QSA_DTYPE_I8 ? qsa::kFmtINT8 : qsa::kFmtINT4;
-    if (kv_scales == nullptr)
-      return fail(QSA_ERR_CONTRACT, "qsa_decode: %s pools need kv_scales", dtype_name(pdt));
-    group = kv_scales->group_size;
-    const bool g_ok = (fmt == qsa::kFmtINT4) ? (group == 32 || group == 64)
-                                             : (group == 32 || group == 64 || group == 256);
-    if (!g_ok)
-      return fail(QSA_ERR_CONTRACT, "qsa_decode: group_size %d is not supported for %s pools "
-                  "(fp8/i8: 32, 64, 256; u4x2: 32, 64)", group, dtype_name(pdt));
-    const int64_t ng = QSA_HEAD_DIM / group;
-    if ((st = check_tensor(&kv_scales->k_scale, "k_scale", QSA_DTYPE_F32, 3)) != QSA_OK) return st;
-    if ((st = check_tensor(&kv_scales->v_scale, "v_scale", QSA_DTYPE_F32, 3)) != QSA_OK) return st;
-    for (const qsa_tensor *t : {&kv_scales->k_scale, &kv_scales->v_scale})
-      if (t->shape[0] != slots || t->shape[1] != hkv || t->shape[2] != ng)
-        return fail(QSA_ERR_CONTRACT, "qsa_decode: scales must be [slots, Hkv, 256/group] = "
-                    "[%lld, %lld, %lld]", static_cast<long long>(slots),
-                    static_cast<long long>(hkv), static_cast<long long>(ng));
-    ks = static_cast<const float *>(kv_scales->k_scale.data);
-    vs = static_cast<const float *>(kv_scales->v_scale.data);
-    ks_ss = kv_scales->k_scale.stride[0];
-    ks_sh = kv_scales->k_scale.stride[1];
-    vs_ss = kv_scales->v_scale.stride[0];
-    vs_sh = kv_scales->v_scale.stride[1];
-  }
-
   // -- device, workspace, launch
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "qsa_decode: no HIP device");
@@ -364,12 +404,13 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.k_sh = k_pool->stride[1] * eb;
   p.v_ss = v_pool->stride[0] * eb;
   p.v_sh = v_pool->stride[1] * eb;
-  p.ks = ks;
-  p.vs = vs;
-  p.ks_ss = ks_ss;
-  p.ks_sh = ks_sh;
-  p.vs_ss = vs_ss;
-  p.vs_sh = vs_sh;
+  p.ks = pd.ks;
+  p.vs = pd.vs;
+  p.ks_ss = pd.ks_ss;
+  p.ks_sh = pd.ks_sh;
+  p.vs_ss = pd.vs_ss;
+  p.vs_sh = pd.vs_sh;
+  p.scale_f16 = pd.scale_f16;
   p.sel = static_cast<const int32_t *>(sel_indices->data);
   p.n_sel = sel_indices->shape[0];
   p.cu = static_cast<const int32_t *>(cu_seqlens->data);
@@ -388,9 +429,75 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.part = ws->part;
   p.ctr = ws->words;
   p.err = ws->words + kCtrWords;
-  const hipError_t e = qsa::launch_decode(p, fmt, group, stream);
+  const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess)
     return fail(QSA_ERR_HIP, "qsa_decode: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_kv_store(const qsa_tensor *k_new, const qsa_tensor *v_new, const qsa_tensor *loc,
+                        qsa_tensor *k_pool, qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
+                        hipStream_t stream) {
+  static const char *fn = "qsa_kv_store";
+  qsa_status st;
+  PoolDesc pd;
+  if ((st = check_pools(fn, k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
+  if ((st = check_tensor(k_new, "k_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(v_new, "v_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  const int64_t n = k_new->shape[0];
+  for (const qsa_tensor *t : {k_new, v_new}) {
+    if (t->shape[0] != n || t->shape[1] != pd.hkv || t->shape[2] != QSA_HEAD_DIM)
+      return fail(QSA_ERR_CONTRACT, "%s: k_new and v_new must be [n, Hkv, 256] = [%lld, %lld, 256]",
+                  fn, static_cast<long long>(n), static_cast<long long>(pd.hkv));
+    if (!aligned16(t->data) || t->stride[0] % 8 || t->stride[1] % 8)
+      return fail(QSA_ERR_CONTRACT, "%s: k_new / v_new rows must start on 16-byte boundaries", fn);
+  }
+  if (loc == nullptr) return fail(QSA_ERR_ARG, "%s: loc is NULL", fn);
+  if (loc->dtype != QSA_DTYPE_I32 && loc->dtype != QSA_DTYPE_I64)
+    return fail(QSA_ERR_CONTRACT, "%s: loc must be i32 or i64, got %s", fn, dtype_name(loc->dtype));
+  if ((st = check_tensor(loc, "loc", loc->dtype, 1, true, fn)) != QSA_OK) return st;
+  if (loc->shape[0] != n)
+    return fail(QSA_ERR_CONTRACT, "%s: loc must have n = %lld entries, got %lld", fn,
+                static_cast<long long>(n), static_cast<long long>(loc->shape[0]));
+  if ((n * pd.hkv + 3) / 4 > 0x7FFFFFFFLL)
+    return fail(QSA_ERR_CONTRACT, "%s: n = %lld rows is too many for one launch", fn,
+                static_cast<long long>(n));
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  Workspace *ws = nullptr;  // only its sticky error word is used
+  if ((st = ensure_workspace(dev, 0, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK) return st;
+
+  qsa::StoreParams p{};
+  p.k = static_cast<const __bf16 *>(k_new->data);
+  p.v = static_cast<const __bf16 *>(v_new->data);
+  p.k_st = k_new->stride[0];
+  p.k_sh = k_new->stride[1];
+  p.v_st = v_new->stride[0];
+  p.v_sh = v_new->stride[1];
+  p.loc = loc->data;
+  p.loc_i64 = loc->dtype == QSA_DTYPE_I64;
+  p.n = n;
+  p.kp = static_cast<uint8_t *>(k_pool->data);
+  p.vp = static_cast<uint8_t *>(v_pool->data);
+  p.kp_ss = k_pool->stride[0] * pd.eb;
+  p.kp_sh = k_pool->stride[1] * pd.eb;
+  p.vp_ss = v_pool->stride[0] * pd.eb;
+  p.vp_sh = v_pool->stride[1] * pd.eb;
+  p.ks = pd.ks;
+  p.vs = pd.vs;
+  p.ks_ss = pd.ks_ss;
+  p.ks_sh = pd.ks_sh;
+  p.vs_ss = pd.vs_ss;
+  p.vs_sh = pd.vs_sh;
+  p.scale_f16 = pd.scale_f16;
+  p.group = pd.group;
+  p.slots = pd.slots;
+  p.hkv = static_cast<int>(pd.hkv);
+  p.err = ws->words + kCtrWords;
+  const hipError_t e = qsa::launch_store(p, pd.fmt, stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 

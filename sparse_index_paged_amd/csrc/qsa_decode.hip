@@ -238,8 +238,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 
   const uint8_t *kbase = p.k + g * p.k_sh + 16 * lchunk;
   const uint8_t *vbase = p.v + g * p.v_sh + 16 * lchunk;
-  const float *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + lchunk : nullptr;
-  const float *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + lchunk : nullptr;
+  const int sbytes = p.scale_f16 ? 2 : 4;
+  const uint8_t *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + lchunk * sbytes : nullptr;
+  const uint8_t *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + lchunk * sbytes : nullptr;
   const int32_t *selw = p.sel + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
 
@@ -268,6 +269,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       sl[i] = selw[j];
     }
   };
+  auto load_scale = [&](const uint8_t *ptr) -> float {
+    if (p.scale_f16) return static_cast<float>(*reinterpret_cast<const _Float16 *>(ptr));
+    return *reinterpret_cast<const float *>(ptr);
+  };
   auto checked = [&](int32_t s) -> uint32_t {
     if (static_cast<uint32_t>(s) >= slots) { bad_slot = true; return 0u; }
     return static_cast<uint32_t>(s);
@@ -285,8 +290,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     if constexpr (NG > 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        ksr[i] = (lchunk < NG) ? ksbase[static_cast<int64_t>(slot[i]) * p.ks_ss] : 0.0f;
-        vsr[i] = (lchunk < NG) ? vsbase[static_cast<int64_t>(slot[i]) * p.vs_ss] : 0.0f;
+        ksr[i] = (lchunk < NG) ? load_scale(ksbase + static_cast<int64_t>(slot[i]) * p.ks_ss) : 0.0f;
+        vsr[i] = (lchunk < NG) ? load_scale(vsbase + static_cast<int64_t>(slot[i]) * p.vs_ss) : 0.0f;
       }
     }
   };

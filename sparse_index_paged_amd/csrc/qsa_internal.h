@@ -22,6 +22,7 @@ enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3 };
 // Device-side error bits (sticky, OR-ed into Params::err).
 constexpr uint32_t kErrRowRange = 1u;   // cu_seqlens out of range / row > 2055
 constexpr uint32_t kErrSlot = 2u;       // a slot id outside [0, slots)
+constexpr uint32_t kErrStoreSlot = 4u;  // a store's slot id outside [0, slots)
 
 struct Params {
   const __bf16 *q;          // [bs, hq, 256]
@@ -29,9 +30,10 @@ struct Params {
   const uint8_t *k, *v;     // pools (byte pointers)
   int64_t k_ss, k_sh;       // byte strides (slot, kv head)
   int64_t v_ss, v_sh;
-  const float *ks, *vs;     // scales [slots, hkv, 256/G] or null
-  int64_t ks_ss, ks_sh;     // element strides
+  const uint8_t *ks, *vs;   // scales [slots, hkv, 256/G] (f32 or f16) or null
+  int64_t ks_ss, ks_sh;     // byte strides
   int64_t vs_ss, vs_sh;
+  int scale_f16;            // scales are f16 (else f32)
   const int32_t *sel;
   int64_t n_sel;
   const int32_t *cu;
@@ -49,8 +51,32 @@ struct Params {
   uint32_t *err;            // sticky error word
 };
 
+// One quantize + scatter call: rows t of k_new / v_new go to pool slot loc[t].
+struct StoreParams {
+  const __bf16 *k, *v;      // new rows [n, hkv, 256]
+  int64_t k_st, k_sh;       // element strides (token, kv head)
+  int64_t v_st, v_sh;
+  const void *loc;          // [n] int32 or int64 slot ids
+  int loc_i64;
+  int64_t n;
+  uint8_t *kp, *vp;         // code pools (byte pointers)
+  int64_t kp_ss, kp_sh;     // byte strides (slot, kv head)
+  int64_t vp_ss, vp_sh;
+  uint8_t *ks, *vs;         // scale pools or null (bf16 pools)
+  int64_t ks_ss, ks_sh;     // byte strides
+  int64_t vs_ss, vs_sh;
+  int scale_f16;
+  int group;                // channels per scale: 32, 64 or 256
+  int64_t slots;
+  int hkv;
+  uint32_t *err;            // sticky error word
+};
+
 // Launch the decode kernel for one call (grid = 8 * ceil(npairs/8) * nsplit).
 hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream);
+
+// Launch the quantize + scatter kernel (one wave per (token, kv head)).
+hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream);
 
 // Zero n words at dst with a small kernel (no memset node in captured graphs).
 hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream);

@@ -80,9 +80,11 @@ def compare(out, lse, o_ref, l_ref, lengths, *, tol=REL_L2_TOL, lse_tol=LSE_TOL,
     return rel
 
 
-def run_and_compare(case, label, rows=None, quant=None, **decode_kw):
+def run_and_compare(case, label, rows=None, quant=None, scale_dtype=None, **decode_kw):
     """Decode a synth.QsaCase on the GPU and compare with the oracle.
-    quant = (fmt, group, kc, ks, vc, vs) for quantized pools (host arrays)."""
+    quant = (fmt, group, kc, ks, vc, vs) for quantized pools (host arrays);
+    scale_dtype = torch dtype the scales are handed to the GPU in (default
+    float32; the oracle always gets their float32 values)."""
     import torch
     import sparse_index_paged_amd as qsa
     d = to_device(case)
@@ -92,8 +94,9 @@ def run_and_compare(case, label, rows=None, quant=None, **decode_kw):
         fmt, group, kc, ks, vc, vs = quant
         d["k"] = torch.from_numpy(kc).cuda()
         d["v"] = torch.from_numpy(vc).cuda()
-        kw = dict(kv_format=fmt, k_scale=torch.from_numpy(ks).cuda(),
-                  v_scale=torch.from_numpy(vs).cuda(), group_size=group)
+        sdt = scale_dtype or torch.float32
+        kw = dict(kv_format=fmt, k_scale=torch.from_numpy(ks).to(sdt).cuda(),
+                  v_scale=torch.from_numpy(vs).to(sdt).cuda(), group_size=group)
         okw = dict(fmt=fmt, group=group, k_scale=ks, v_scale=vs)
         kpool, vpool = kc, vc
     else:

@@ -49,7 +49,7 @@ def test_header_compiles_as_c():
 
 
 def test_abi_version():
-    assert qsa.abi_version() == B.ABI_VERSION == 1
+    assert qsa.abi_version() == B.ABI_VERSION == 2
 
 
 def test_plan_and_options():
@@ -135,7 +135,7 @@ def _scales(slots=64, hkv=2, group=256, dtype=B.F32):
     (dict(scales="bf16"), "take no scales"),
     (dict(pool_dtype=B.I8, scales="g48"), "group_size 48 is not supported"),
     (dict(pool_dtype=B.U4X2, scales="g256"), "group_size 256 is not supported"),
-    (dict(pool_dtype=B.I8, scales="f16"), "k_scale must be f32"),
+    (dict(pool_dtype=B.I8, scales="bf16s"), "k_scale must be f32 or f16"),
     (dict(cu_len=3), "cu_seqlens must have bs \\+ 1"),
     (dict(pool_data=FAKE + 8), "16-byte boundaries"),
     (dict(q_strides=(24 * 256, 256, 2)), "contiguous in its last dimension"),
@@ -153,8 +153,8 @@ def test_contract_rejections(kwargs, match):
         kwargs["scales"] = B.QsaKvScales(_t((64, 2, 5), B.F32), _t((64, 2, 5), B.F32), 48)
     elif sc == "g256":
         kwargs["scales"] = _scales(group=256)
-    elif sc == "f16":
-        kwargs["scales"] = _scales(dtype=B.F16)
+    elif sc == "bf16s":
+        kwargs["scales"] = _scales(dtype=B.BF16)
     st, msg = _call(**kwargs)
     assert st == 1, (st, msg)
     assert re.search(match, msg), msg
@@ -165,3 +165,45 @@ def test_null_arguments_are_arg_errors():
     st = lib.qsa_decode(None, None, None, None, None, None, None, None, None)
     assert st == 2
     assert "q is NULL" in lib.qsa_last_error().decode()
+
+
+def _store(n=8, hkv=2, slots=64, pool_dtype=B.BF16, scales=None, new_dtype=B.BF16,
+           new_shape=None, loc_dtype=B.I32, loc_len=None, new_data=FAKE, new_strides=None,
+           v_pool_shape=None):
+    lib = qsa.load_library()
+    row = 256 if pool_dtype != B.U4X2 else 128
+    k_new = _t(new_shape or (n, hkv, 256), new_dtype, new_strides, data=new_data)
+    v_new = _t(new_shape or (n, hkv, 256), new_dtype, new_strides)
+    loc = _t((n if loc_len is None else loc_len,), loc_dtype)
+    kp = _t((slots, hkv, row), pool_dtype)
+    vp = _t(v_pool_shape or (slots, hkv, row), pool_dtype)
+    st = lib.qsa_kv_store(ctypes.byref(k_new), ctypes.byref(v_new), ctypes.byref(loc),
+                          ctypes.byref(kp), ctypes.byref(vp),
+                          ctypes.byref(scales) if scales is not None else None, None)
+    return st, lib.qsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,match", [
+    (dict(new_dtype=B.F32), "k_new must be bf16"),
+    (dict(new_shape=(8, 1, 256)), r"k_new and v_new must be \[n, Hkv, 256\]"),
+    (dict(new_shape=(8, 2, 128)), r"k_new and v_new must be \[n, Hkv, 256\]"),
+    (dict(loc_dtype=B.F32), "loc must be i32 or i64"),
+    (dict(loc_len=7), "loc must have n = 8 entries"),
+    (dict(new_data=FAKE + 8), "rows must start on 16-byte boundaries"),
+    (dict(new_strides=(2 * 260, 260, 1)), "rows must start on 16-byte boundaries"),
+    (dict(pool_dtype=B.I8), "qsa_kv_store: i8 pools need kv_scales"),
+    (dict(scales="g256"), "qsa_kv_store: bf16 pools take no scales"),
+    (dict(pool_dtype=B.U4X2, scales="g256"), "group_size 256 is not supported"),
+    (dict(pool_dtype=B.I8, scales="bf16s"), "k_scale must be f32 or f16"),
+    (dict(v_pool_shape=(32, 2, 256)), "k_pool and v_pool shapes differ"),
+    (dict(hkv=3), "pools must hold 1 or 2 KV heads"),
+])
+def test_store_contract_rejections(kwargs, match):
+    sc = kwargs.pop("scales", None)
+    if sc == "g256":
+        kwargs["scales"] = _scales(group=256)
+    elif sc == "bf16s":
+        kwargs["scales"] = _scales(dtype=B.BF16)
+    st, msg = _store(**kwargs)
+    assert st == 1, (st, msg)
+    assert re.search(match, msg), msg
