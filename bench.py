@@ -10,6 +10,11 @@ re-read the same rows from the caches.
 
 Prints one JSON line.  value = gathered-KV bytes / time (GB/s), where
 gathered-KV bytes = sum_b L_b * Hkv * 2 (K and V) * 512 B.
+
+Other lines (not the default run): ``--kv-format fp8|int8|int4`` decodes
+from quantized pools (written on the device by qsa_kv_store from the same
+bf16 pools; gathered bytes then count codes + scales), and ``--mode store``
+times qsa_kv_store itself.
 """
 from __future__ import annotations
 
@@ -52,6 +57,37 @@ def gathered_bytes(lengths, hkv: int, row_bytes: int = 512) -> int:
     return int(sum(int(x) for x in lengths)) * hkv * 2 * row_bytes
 
 
+FORMATS = {  # kv format -> (pool elements per row, bytes per element, default group, torch dtype)
+    "bf16": (256, 2, 256, "bfloat16"),
+    "fp8": (256, 1, 256, "uint8"),
+    "int8": (256, 1, 64, "int8"),
+    "int4": (128, 1, 32, "uint8"),
+}
+
+
+def row_bytes(fmt: str, group: int, scale_bytes: int) -> int:
+    """Bytes one (slot, KV head) row occupies in the pools: codes + scales."""
+    code = FORMATS[fmt][0] * FORMATS[fmt][1]
+    return code if fmt == "bf16" else code + (256 // group) * scale_bytes
+
+
+def quantized_pools(k, v, fmt, group, scale_dtype):
+    """Device pools of `fmt` written by qsa_kv_store from bf16 device pools
+    (every slot, in slot order)."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    slots, hkv = k.shape[0], k.shape[1]
+    pdt = getattr(torch, FORMATS[fmt][3])
+    kc = torch.empty((slots, hkv, FORMATS[fmt][0]), dtype=pdt, device="cuda")
+    vc = torch.empty_like(kc)
+    ks = torch.empty((slots, hkv, 256 // group), dtype=scale_dtype, device="cuda")
+    vs = torch.empty_like(ks)
+    loc = torch.arange(slots, dtype=torch.int32, device="cuda")
+    qsa.kv_store(k, v, loc, kc, vc, kv_format=fmt, k_scale=ks, v_scale=vs, group_size=group)
+    torch.cuda.synchronize()
+    return kc, vc, ks, vs
+
+
 def cpu_baseline(case, min_seconds: float):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -89,6 +125,65 @@ def copy_mode(args):
                       "ms": dt * 1e3, "GBps_rw": 2 * n * 4 / dt / 1e9}), flush=True)
 
 
+def store_mode(args):
+    """qsa_kv_store throughput: `tokens` new K/V rows per call (TP1 layout,
+    2 KV heads) scattered to distinct random slots of 262144-slot pools.
+    Algorithmic bytes per call = reads of the bf16 rows (2 x 512 B per
+    token and KV head) + slot ids + writes of codes and scales."""
+    import numpy as np
+    import torch
+    import sparse_index_paged_amd as qsa
+    import synth
+    fmt = args.kv_format
+    group = args.group or FORMATS[fmt][2]
+    sdt = torch.float16 if args.scale_dtype == "f16" else torch.float32
+    slots, hkv, n = 262144, args.hkv, args.tokens
+    rng = np.random.default_rng(2024)
+    pdt = getattr(torch, FORMATS[fmt][3])
+    kc = torch.zeros((slots, hkv, FORMATS[fmt][0]), dtype=pdt, device="cuda")
+    vc = torch.zeros_like(kc)
+    scales = {}
+    if fmt != "bf16":
+        scales = dict(kv_format=fmt, group_size=group,
+                      k_scale=torch.zeros((slots, hkv, 256 // group), dtype=sdt, device="cuda"),
+                      v_scale=torch.zeros((slots, hkv, 256 // group), dtype=sdt, device="cuda"))
+    banks = []
+    for i in range(4):
+        xk = synth.normal_bf16(rng, (n, hkv, 256)).cuda()
+        xv = synth.normal_bf16(rng, (n, hkv, 256)).cuda()
+        loc = torch.from_numpy(rng.permutation(slots)[:n].astype(np.int32)).cuda()
+        banks.append((xk, xv, loc))
+    for i in range(args.warmup):
+        xk, xv, loc = banks[i % 4]
+        qsa.kv_store(xk, xv, loc, kc, vc, **scales)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        xk, xv, loc = banks[i % 4]
+        qsa.kv_store(xk, xv, loc, kc, vc, **scales)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    sb = 2 if args.scale_dtype == "f16" else 4
+    b = n * 4 + n * hkv * 2 * (512 + row_bytes(fmt, group, sb))
+    gbs = b / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "qsa_kv_store GB/s (bf16 rows read + codes/scales written)",
+        "value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3),
+        "steps": args.steps, "warmup": args.warmup, "dtype": f"bf16 -> {fmt}",
+        "config": {"workload": f"{n} tokens x {hkv} KV heads into [262144,{hkv},256] {fmt} pools "
+                               f"(group {group}, {args.scale_dtype} scales)",
+                   "tokens": n, "hkv": hkv, "format": fmt, "group": group,
+                   "algorithmic_bytes_per_call": b},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": b, "kernel": f"qsa_store_kernel<{fmt}>"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,7 +194,11 @@ def main():
     ap.add_argument("--hkv", type=int, default=2, choices=[1, 2])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "store"], default="decode")
+    ap.add_argument("--kv-format", choices=list(FORMATS), default="bf16")
+    ap.add_argument("--group", type=int, default=None)
+    ap.add_argument("--scale-dtype", choices=["f32", "f16"], default="f32")
+    ap.add_argument("--tokens", type=int, default=32768, help="tokens per store call")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--split-target", type=int, default=None)
     ap.add_argument("--min-split-keys", type=int, default=None)
@@ -115,6 +214,9 @@ def main():
     import torch
     if args.mode == "copy":
         copy_mode(args)
+        return
+    if args.mode == "store":
+        store_mode(args)
         return
 
     import numpy as np
@@ -143,6 +245,15 @@ def main():
     q = case.q.cuda()
     k = case.k_pool.cuda()
     v = case.v_pool.cuda()
+    fmt = args.kv_format
+    group = args.group or FORMATS[fmt][2]
+    sdt = torch.float16 if args.scale_dtype == "f16" else torch.float32
+    qkw = {}
+    if fmt != "bf16":
+        kc, vc, ks, vs = quantized_pools(k, v, fmt, group, sdt)
+        del k, v
+        k, v = kc, vc
+        qkw = dict(kv_format=fmt, k_scale=ks, v_scale=vs, group_size=group)
     cu = torch.from_numpy(case.cu).cuda()
     sels = [torch.from_numpy(s).cuda() for s in bank_sels]
     out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
@@ -151,24 +262,27 @@ def main():
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse)
+        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse)
+        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     counters_ok = all(c == 0 for c in qsa.debug_counters())
 
-    b_kv = gathered_bytes(case.lengths, case.hkv)
+    rb = row_bytes(fmt, group, 2 if args.scale_dtype == "f16" else 4)
+    b_kv = gathered_bytes(case.lengths, case.hkv, rb)
     gbs = b_kv / (ms_per_step * 1e-3) / 1e9
     splits, wgs = qsa.plan(case.bs, case.hkv)
-    traffic = committed_traffic()
+    traffic = committed_traffic() if fmt == "bf16" else None
+    pool_desc = "bf16 pools" if fmt == "bf16" else (
+        f"{fmt} pools (group {group}, {args.scale_dtype} scales, written by qsa_kv_store)")
 
     line = {
         "metric": METRIC,
@@ -183,11 +297,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if fmt == "bf16" else f"bf16 ({fmt} pools)",
         "data": "synthetic",
         "config": {
             "workload": f"packed QSA decode bs={case.bs} "
-                        f"{'TP1 (24Q/2KV' if case.hkv == 2 else 'TP2 (12Q/1KV'}, D=256) bf16 pools "
+                        f"{'TP1 (24Q/2KV' if case.hkv == 2 else 'TP2 (12Q/1KV'}, D=256) {pool_desc} "
                         f"[262144,{case.hkv},256], 2055 selected slots per row, 5% keys x8",
             "bs": case.bs, "hq": case.hq, "hkv": case.hkv, "head_dim": 256,
             "sel_per_row": int(case.lengths.max()), "pool_slots": int(case.k_pool.shape[0]),
@@ -202,11 +316,11 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": b_kv,
-            "kernel": "qsa_decode_kernel<bf16>",
+            "kernel": f"qsa_decode_kernel<{fmt}>",
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and fmt == "bf16":
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -39,6 +39,8 @@
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
 //     one L2.
+#include <type_traits>
+
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -69,29 +71,20 @@ template <int FMT> struct Geo {
   static constexpr int kParts = 16 / sizeof(typename Fmt<FMT>::Part);  // 8-code parts per lane
 };
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;  // NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even bf16 (one v_cvt_pk_bf16_f32 on
+// gfx950): a in bits 0..15, b in bits 16..31.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// OCP e4m3fn byte -> bf16 bits (exact: every e4m3fn value is a bf16 value).
-__device__ __forceinline__ uint32_t fp8_to_bf16(uint32_t c) {
-  const uint32_t sign = (c & 0x80u) << 8;
-  const uint32_t em = c & 0x7Fu;
-  const uint32_t e = em >> 3, m = em & 7u;
-  uint32_t mag;
-  if (e != 0u)
-    mag = ((e + 120u) << 7) | (m << 4);                       // 2^(e-7) (1 + m/8)
-  else
-    mag = __float_as_uint(static_cast<float>(m) * 0x1p-9f) >> 16;  // m 2^-9
-  if (em == 0x7Fu) mag = 0x7FC0u;                             // S.1111.111 = NaN
-  return sign | mag;
-}
-
-__device__ __forceinline__ uint32_t int_to_bf16(int x) {
-  return __float_as_uint(static_cast<float>(x)) >> 16;  // exact for |x| <= 256
+// Two exact values as a bf16 pair: the high halves of their fp32 bits
+// (lo in bits 0..15, hi in bits 16..31).  Exact because every value
+// converted here (int8 / int4 codes) has at most 8 significant bits.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // 8 codes -> 8 bf16 values packed in a uint4 (element e in half e%2 of word e/2)
@@ -99,15 +92,16 @@ template <int FMT> __device__ __forceinline__ uint4 to_bf16x8(typename Fmt<FMT>:
 
 template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtBF16>(uint4 r) { return r; }
 
+// OCP e4m3fn -> bf16 with the gfx950 conversion (scale 1): exact for every
+// non-NaN code, two codes per instruction.
 template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtFP8>(uint2 r) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t src = (i < 2) ? r.x : r.y;
-    const int sh = (i & 1) * 16;
-    w[i] = fp8_to_bf16((src >> sh) & 0xFFu) | (fp8_to_bf16((src >> (sh + 8)) & 0xFFu) << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  auto lo = [](uint32_t src) {  // codes in bytes 0, 1
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(src), 1.0f, false));
+  };
+  auto hi = [](uint32_t src) {  // codes in bytes 2, 3
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(src), 1.0f, true));
+  };
+  return make_uint4(lo(r.x), hi(r.x), lo(r.y), hi(r.y));
 }
 
 template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT8>(uint2 r) {
@@ -116,22 +110,24 @@ template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT8>(uint2 r) {
   for (int i = 0; i < 4; ++i) {
     const uint32_t src = (i < 2) ? r.x : r.y;
     const int sh = (i & 1) * 16;
-    const int a = static_cast<int8_t>((src >> sh) & 0xFFu);
-    const int b = static_cast<int8_t>((src >> (sh + 8)) & 0xFFu);
-    w[i] = int_to_bf16(a) | (int_to_bf16(b) << 16);
+    const float a = static_cast<float>(static_cast<int8_t>(src >> sh));
+    const float b = static_cast<float>(static_cast<int8_t>(src >> (sh + 8)));
+    w[i] = pack_bf16_exact(a, b);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT4>(uint32_t r) {
-  // byte i holds channel 2i (low nibble) and 2i+1 (high nibble), code = nibble - 8
+  // byte i holds channel 2i (low nibble) and 2i+1 (high nibble), code =
+  // nibble - 8, which is the nibble with its top bit flipped read as a
+  // 4-bit two's-complement number
+  const uint32_t x = r ^ 0x88888888u;
+  auto nib = [&](int k) {  // signed 4-bit field k of x
+    return static_cast<float>(static_cast<int32_t>(x << (28 - 4 * k)) >> 28);
+  };
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lo = static_cast<int>((r >> (8 * i)) & 0xFu) - 8;
-    const int hi = static_cast<int>((r >> (8 * i + 4)) & 0xFu) - 8;
-    w[i] = int_to_bf16(lo) | (int_to_bf16(hi) << 16);
-  }
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16_exact(nib(2 * i), nib(2 * i + 1));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -176,21 +172,26 @@ __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthre
   if (tid < kGqa) p.lse[b * p.l_sb + (g * kGqa + tid) * p.l_sh] = __builtin_nanf("");
 }
 
-template <int FMT, int G, int W>
+template <int FMT, int G, int W, bool SF16>
 __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params p) {
   using Part = typename Fmt<FMT>::Part;
   using GEO = Geo<FMT>;
   using LDS = Lds<W>;
+  using Scale = typename std::conditional<SF16, _Float16, float>::type;
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
+  // tiles in flight: as many as fit the register budget of one bf16 tile
+  // (8 row loads per lane for K and for V), so narrower formats keep as many
+  // bytes in flight per wave as bf16 does
+  constexpr int D = 8 / NI;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave loop bounds scalar
   const int r16 = lane & 15;  // MFMA row / head
   const int qg = lane >> 4;   // lane group 0..3
   const int ldrow = (lane / GEO::kLPR) * NI;  // first tile row this lane loads
@@ -238,9 +239,11 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 
   const uint8_t *kbase = p.k + g * p.k_sh + 16 * lchunk;
   const uint8_t *vbase = p.v + g * p.v_sh + 16 * lchunk;
-  const int sbytes = p.scale_f16 ? 2 : 4;
-  const uint8_t *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + lchunk * sbytes : nullptr;
-  const uint8_t *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + lchunk * sbytes : nullptr;
+  // every lane loads a scale (lanes past the row's NG groups re-read group
+  // 0, so no load is conditional); only lanes lchunk < NG store them
+  const int sgrp = (NG > 0 && lchunk < NG) ? lchunk : 0;
+  const uint8_t *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + sgrp * sizeof(Scale) : nullptr;
+  const uint8_t *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + sgrp * sizeof(Scale) : nullptr;
   const int32_t *selw = p.sel + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
 
@@ -252,58 +255,85 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   for (int mt = 0; mt < 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool bad_slot = false;
 
-  // LDS read offsets of the transposed V operand: entry j = 4*qg + e,
-  // channel 16*mt + r16 at byte j*528 + 2*(16*mt + r16).
-  const unsigned char *vcol = vt + (4 * qg) * kLdsRow + 2 * r16;
+  // LDS row layout of the K and V tiles.  A lane stages P = kParts chunks
+  // of 8 channels (16 B of bf16) per row, chunk c of lane l being channel
+  // chunk m = P*l + c.  Chunk m is stored at byte (m % P) * kPartB +
+  // (m / P) * 16, so the lanes of one 16-byte LDS write are 16 B apart (no
+  // bank conflicts); for bf16 (P = 1) this is the plain row.  With P = 2
+  // the second part starts 16 B past mid-row, so that the column reads of
+  // the V operand (channels c and c + 8 in one instruction) fall into
+  // different banks; the row still fits the 528-byte pitch.
+  constexpr int P = GEO::kParts;
+  constexpr int kPartB = (P == 2) ? 512 / P + 16 : 512 / P;
+  static_assert((P - 1) * kPartB + 512 / P <= kLdsRow, "parts exceed the LDS row pitch");
+  // Transposed V operand: lane (r16, qg) needs V[4*qg + e][16*mt + r16],
+  // e = 0..3.  ds_read_b64_tr_b16 gives lane i of a 16-lane group element
+  // i % 4 of the 8 bytes read by lane 4*e + i / 4 of the group, so lane
+  // r16 of group qg reads channels 16*mt + 4*(r16 & 3) .. + 3 of entry
+  // 4*qg + (r16 >> 2): chunk 2*mt + ((r16 >> 1) & 1), byte 8*(r16 & 1) in
+  // the chunk -- a lane base plus the per-mt constant
+  // (2*mt % P) * kPartB + (2*mt / P) * 16.
+  const int vhalf = (r16 >> 1) & 1;
+  const unsigned char *vtr = vt + (4 * qg + (r16 >> 2)) * kLdsRow + (vhalf % P) * kPartB +
+                             (vhalf / P) * 16 + 8 * (r16 & 1);
 
-  // The K / V rows (and scales) of the next tile are in flight in one
-  // register set that is emptied into the LDS tiles at the start of a step.
-  uint4 kraw[NI], vraw[NI];
-  float ksr[NI], vsr[NI];
+  // The K / V rows (and scales) of the next D tiles are in flight in D
+  // register sets; set u is emptied into the LDS tiles at the start of step
+  // t = u (mod D) and refilled with tile t + D.
+  uint4 kraw[D][NI], vraw[D][NI];
+  Scale ksr[D][NI], vsr[D][NI];  // converted to fp32 when staged
 
+  // Every load of the pipeline is unconditional and its value is used as
+  // loaded, so the compiler's load counting never has to assume a skipped
+  // load (or wait early for a value it post-processes) and wait for every
+  // load in flight: tiles past the end re-read the last entry (cache hits),
+  // and a wave with no entries reads cu[0] as its "slot id" (checked below
+  // without raising the error bit; its rows are never processed).
+  const int32_t *ids = (nkeys > 0) ? selw : p.cu;
+  const int jmax = (nkeys > 0) ? nkeys - 1 : 0;
   auto fetch_slots = [&](int t, int32_t (&sl)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      int j = kTile * t + ldrow + i;
-      j = j < nkeys ? j : nkeys - 1;
-      sl[i] = selw[j];
+      const int j = kTile * t + ldrow + i;
+      sl[i] = ids[j < jmax ? j : jmax];
     }
   };
-  auto load_scale = [&](const uint8_t *ptr) -> float {
-    if (p.scale_f16) return static_cast<float>(*reinterpret_cast<const _Float16 *>(ptr));
-    return *reinterpret_cast<const float *>(ptr);
-  };
   auto checked = [&](int32_t s) -> uint32_t {
-    if (static_cast<uint32_t>(s) >= slots) { bad_slot = true; return 0u; }
-    return static_cast<uint32_t>(s);
+    const bool bad = static_cast<uint32_t>(s) >= slots;
+    bad_slot = bad_slot || (bad && nkeys > 0);
+    return bad ? 0u : static_cast<uint32_t>(s);
   };
-  auto issue = [&](const int32_t (&sl)[NI]) {
+  auto issue = [&](int u, const int32_t (&sl)[NI]) {
     uint32_t slot[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) slot[i] = checked(sl[i]);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kraw[i] = *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(slot[i]) * p.k_ss);
+      kraw[u][i] = *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(slot[i]) * p.k_ss);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      vraw[i] = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(slot[i]) * p.v_ss);
+      vraw[u][i] = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(slot[i]) * p.v_ss);
     if constexpr (NG > 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        ksr[i] = (lchunk < NG) ? load_scale(ksbase + static_cast<int64_t>(slot[i]) * p.ks_ss) : 0.0f;
-        vsr[i] = (lchunk < NG) ? load_scale(vsbase + static_cast<int64_t>(slot[i]) * p.vs_ss) : 0.0f;
+        ksr[u][i] = *reinterpret_cast<const Scale *>(ksbase + static_cast<int64_t>(slot[i]) * p.ks_ss);
+        vsr[u][i] = *reinterpret_cast<const Scale *>(vsbase + static_cast<int64_t>(slot[i]) * p.vs_ss);
       }
     }
   };
 
-  // ---- prologue: the first two tiles' slot ids and Q are in flight
-  // together; Q of the 12 heads of KV head g goes to LDS [16 heads][528 B]
-  // (heads 12..15 zero), where each QK MFMA reads its B operand.
-  int32_t snext[NI];
+  // ---- prologue: the slot ids of tiles 0..2D-1 and Q are in flight
+  // together, then the rows of tiles 0..D-1; Q of the 12 heads of KV head g
+  // goes to LDS [16 heads][528 B] (heads 12..15 zero), where each QK MFMA
+  // reads its B operand.  snext[u] holds the slot ids of the tile that
+  // register set u loads next.
+  int32_t snext[D][NI];
   {
-    int32_t s0[NI];
-    if (ntile > 0) fetch_slots(0, s0);
-    if (ntile > 1) fetch_slots(1, snext);
+    int32_t s0[D][NI];
+#pragma unroll
+    for (int u = 0; u < D; ++u) fetch_slots(u, s0[u]);
+#pragma unroll
+    for (int u = 0; u < D; ++u) fetch_slots(D + u, snext[u]);
     constexpr int CPT = 512 / kThr;  // 16-byte Q chunks per thread
     uint4 qv[CPT];
 #pragma unroll
@@ -315,40 +345,43 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
         qv[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + (g * kGqa + h) * p.q_sh)[c];
     }
 #pragma unroll
+    for (int u = 0; u < D; ++u) issue(u, s0[u]);
+#pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int idx = tid * CPT + i;
       *reinterpret_cast<uint4 *>(qlds + (idx >> 5) * kLdsRow + (idx & 31) * 16) = qv[i];
     }
-    if (ntile > 0) issue(s0);
   }
   __syncthreads();
   auto qfrag = [&](int kk) -> bf16x8 {
     return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
   };
+  // K operand: channel chunk 4*kk + qg of row r16
+  const unsigned char *krow = kt + r16 * kLdsRow + (qg % P) * kPartB + (qg / P) * 16;
   auto kfrag = [&](int kk) -> bf16x8 {
-    return as_bf16x8(*reinterpret_cast<const uint4 *>(kt + r16 * kLdsRow + (4 * kk + qg) * 16));
+    return as_bf16x8(*reinterpret_cast<const uint4 *>(krow + (4 * kk / P) * 16));
   };
 
-  // 1. the current tile's K and V rows, dequantized to bf16, and their
-  // scale rows into the wave's LDS tiles
-  auto stage = [&]() {
+  // 1. register set u (one tile's K and V rows, dequantized to bf16, and
+  // their scale rows) into the wave's LDS tiles
+  auto stage = [&](int u) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int off = (ldrow + i) * kLdsRow + lchunk * 16 * GEO::kParts;
+      const int off = (ldrow + i) * kLdsRow + lchunk * 16;
 #pragma unroll
-      for (int u = 0; u < GEO::kParts; ++u) {
-        const Part kp = reinterpret_cast<const Part *>(&kraw[i])[u];
-        const Part vp = reinterpret_cast<const Part *>(&vraw[i])[u];
-        *reinterpret_cast<uint4 *>(kt + off + 16 * u) = to_bf16x8<FMT>(kp);
-        *reinterpret_cast<uint4 *>(vt + off + 16 * u) = to_bf16x8<FMT>(vp);
+      for (int c = 0; c < P; ++c) {
+        const Part kp = reinterpret_cast<const Part *>(&kraw[u][i])[c];
+        const Part vp = reinterpret_cast<const Part *>(&vraw[u][i])[c];
+        *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = to_bf16x8<FMT>(kp);
+        *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = to_bf16x8<FMT>(vp);
       }
     }
     if constexpr (NG > 0) {
       if (lchunk < NG) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          ksc[(ldrow + i) * NG + lchunk] = ksr[i];
-          vsc[(ldrow + i) * NG + lchunk] = vsr[i];
+          ksc[(ldrow + i) * NG + lchunk] = static_cast<float>(ksr[u][i]);
+          vsc[(ldrow + i) * NG + lchunk] = static_cast<float>(vsr[u][i]);
         }
       }
     }
@@ -398,24 +431,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(s2[e] - m_new);
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
+    // (once the running maxima settle most tiles leave every head's max
+    // unchanged: alpha == 1 exactly and the rescale is skipped)
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
+      for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
+    }
 
     // 4. O^T += V^T . P^T with P as hi + lo bf16
     auto split_p = [&](const float (&pv)[4], i16x4 &hi, i16x4 &lo) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t hb = f32_to_bf16_rne(pv[e]);
-        const float rest = pv[e] - __uint_as_float(hb << 16);
-        hi[e] = static_cast<short>(hb);
-        lo[e] = static_cast<short>(f32_to_bf16_rne(rest));
-      }
+      const uint32_t h01 = bf16x2_rne(pv[0], pv[1]);
+      const uint32_t h23 = bf16x2_rne(pv[2], pv[3]);
+      const uint32_t l01 = bf16x2_rne(pv[0] - __uint_as_float(h01 << 16), pv[1] - __uint_as_float(h01 & 0xFFFF0000u));
+      const uint32_t l23 = bf16x2_rne(pv[2] - __uint_as_float(h23 << 16), pv[3] - __uint_as_float(h23 & 0xFFFF0000u));
+      hi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+      lo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
     };
     auto pv_mfma = [&](int mt, const i16x4 &hi, const i16x4 &lo) {
-      i16x4 a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        a[e] = *reinterpret_cast<const short *>(vcol + e * kLdsRow + 32 * mt);
+      const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4 *)(vtr + (2 * mt % P) * kPartB + (2 * mt / P) * 16));
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[mt], 0, 0, 0);
     };
@@ -449,14 +483,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     wave_lds_fence();  // reads of this tile finish before the next tile's writes
   };
 
-  // ---- software pipeline: the rows of tile t+1 are in flight while tile t
-  // is processed.  Step t: K/V(t) -> LDS, issue K/V(t+1), fetch the slot ids
-  // of t+2, then QK / softmax / PV of tile t.
-  for (int t = 0; t < ntile; ++t) {
-    stage();
-    if (t + 1 < ntile) issue(snext);
-    if (t + 2 < ntile) fetch_slots(t + 2, snext);
-    process(t);
+  // ---- software pipeline: the rows of tiles t+1 .. t+D are in flight
+  // while tile t is processed.  Step t (u = t mod D): K/V(t) -> LDS, issue
+  // K/V(t+D) into the freed register set u, fetch the slot ids of t+2D into
+  // snext[u], then QK / softmax / PV of tile t.  Slot ids are fetched D
+  // steps before their rows are issued, so that waiting for them (loads
+  // complete in issue order) never waits for rows still in flight.
+  // The loop runs whole groups of D steps; a step past the last tile stages
+  // and loads (the clamped rows) but skips the processing, so no load sits
+  // behind a branch and the compiler's load counting never has to assume a
+  // skipped load and wait for every load in flight.
+  for (int t0 = 0; t0 < ntile; t0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int t = t0 + u;
+      stage(u);
+      issue(u, snext[u]);
+      fetch_slots(t + 2 * D, snext[u]);
+      if (t < ntile) process(t);
+    }
   }
 
   // ---- wave result: full sum per head over the 4 lane groups
@@ -537,8 +582,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   auto lse_of = [](float M, float s) { return (s > 0.f || s != s) ? (M + __log2f(s)) * kLn2 : -INFINITY; };
   auto store_out = [&](int h, const f32x4 &o, float inv) {
     uint2 w;
-    w.x = f32_to_bf16_rne(o[0] * inv) | (f32_to_bf16_rne(o[1] * inv) << 16);
-    w.y = f32_to_bf16_rne(o[2] * inv) | (f32_to_bf16_rne(o[3] * inv) << 16);
+    w.x = bf16x2_rne(o[0] * inv, o[1] * inv);
+    w.y = bf16x2_rne(o[2] * inv, o[3] * inv);
     *reinterpret_cast<uint2 *>(p.out + b * p.o_sb + (g * kGqa + h) * p.o_sh + 4 * lane) = w;
   };
   float *lrow = p.lse + b * p.l_sb + (g * kGqa) * p.l_sh;
@@ -706,14 +751,26 @@ __global__ void audit_kernel(const uint32_t *ctr, int n, uint32_t *accum) {
   }
 }
 
+template <int FMT, int G, bool SF16>
+void launch_waves(const Params &p, dim3 grid, hipStream_t stream) {
+  if (p.waves == 8)
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16>), grid, dim3(256), 0, stream, p);
+}
+
 template <int FMT, int G>
 hipError_t launch_one(const Params &p, hipStream_t stream) {
   const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
   const dim3 grid(npairs8 * p.nsplit);
-  if (p.waves == 8)
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4>), grid, dim3(256), 0, stream, p);
+  if constexpr (FMT == kFmtBF16) {
+    launch_waves<FMT, G, false>(p, grid, stream);
+  } else {
+    if (p.scale_f16)
+      launch_waves<FMT, G, true>(p, grid, stream);
+    else
+      launch_waves<FMT, G, false>(p, grid, stream);
+  }
   return hipGetLastError();
 }
 

@@ -15,13 +15,24 @@
 // the same section); codes are computed from the scale as stored.  bf16
 // pools take the rows unchanged.
 //
-// Mapping: one wave per (token, kv head); lanes 0..31 handle the K row and
-// lanes 32..63 the V row, 8 channels (one 16-byte load) per lane, so the
-// absmax of a group of G channels is a butterfly over G/8 lanes.
+// Mapping: a wave handles 4 consecutive (token, kv head) rows; lanes 0..31
+// work on the K rows and lanes 32..63 on the V rows, 8 channels (one
+// 16-byte load) per lane, and all loads of the 4 rows are issued before the
+// first row is processed.  The absmax of a group of G channels is a
+// butterfly over G/8 lanes.
+//
+// x / scale must be the correctly rounded fp32 quotient, because the codes
+// round it once more.  The quotient is first taken as x * rcp(scale)
+// (within 2 ulp of the rounded quotient); only when that value lies within
+// 8 ulp of a rounding boundary of the code (a half-integer for int8 / int4,
+// a midpoint of the e4m3fn grid for fp8) is the full IEEE division done, so
+// the codes equal those of the division everywhere.
 #include "qsa_internal.h"
 
 namespace qsa {
 namespace {
+
+constexpr int kRowsPerWave = 4;
 
 // e4m3fn code of y with |y| <= 448, rounded to nearest even.  Normal codes
 // come from rounding the fp32 significand to 3 bits (a carry moves into the
@@ -39,74 +50,115 @@ __device__ __forceinline__ uint32_t e4m3fn_rne(float y) {
   return sign | code;
 }
 
+// True when rint(v) could change if v moved by up to 8 ulp (or v is not finite).
+__device__ __forceinline__ bool near_half_integer(float v) {
+  const float d = fabsf(v - floorf(v) - 0.5f);
+  return !(d > fmaxf(fabsf(v), 1.0f) * 0x1p-20f);
+}
+
+// Same for the e4m3fn rounding of clamp(v, -448, 448).
+__device__ __forceinline__ bool near_e4m3_boundary(float v) {
+  const float a = fabsf(v);
+  if (!(a <= 448.0f)) return !(a > 448.0f) || a < 456.0f;  // NaN, or just above the clamp
+  if (a < 0x1p-6f) return near_half_integer(a * 512.0f);
+  const int32_t m = static_cast<int32_t>(__float_as_uint(a) & 0xFFFFFu) - 0x80000;
+  return m >= -8 && m <= 8;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t code_of(float y) {
+  if constexpr (FMT == kFmtINT8)
+    return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f))) & 0xFFu;
+  else if constexpr (FMT == kFmtINT4)
+    return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(__builtin_rintf(y), -7.0f), 7.0f)) + 8);
+  else
+    return e4m3fn_rne(fminf(fmaxf(y, -448.0f), 448.0f));
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= p.n * p.hkv) return;
-  const int64_t t = row / p.hkv;
-  const int h = static_cast<int>(row - t * p.hkv);
-  const int64_t slot = p.loc_i64 ? static_cast<const int64_t *>(p.loc)[t]
-                                 : static_cast<int64_t>(static_cast<const int32_t *>(p.loc)[t]);
-  if (slot < 0 || slot >= p.slots) {
-    if (lane == 0) atomicOr(p.err, kErrStoreSlot);
-    return;
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * kRowsPerWave;
+  const int64_t nrows = p.n * p.hkv;
   const bool is_v = lane >= 32;
   const int l = lane & 31;
-  const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
-  const uint4 raw = reinterpret_cast<const uint4 *>(src)[l];
-  uint8_t *dst = is_v ? p.vp + slot * p.vp_ss + h * p.vp_sh : p.kp + slot * p.kp_ss + h * p.kp_sh;
-  if constexpr (FMT == kFmtBF16) {
-    reinterpret_cast<uint4 *>(dst)[l] = raw;
-  } else {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float x[8];
+
+  // ---- all loads of the wave's rows first
+  uint4 raw[kRowsPerWave];
+  int64_t slot[kRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = row0 + i;
+    if (row < nrows) {
+      const int64_t t = (p.hkv == 2) ? (row >> 1) : row;
+      const int h = static_cast<int>(row - t * p.hkv);
+      slot[i] = p.loc_i64 ? static_cast<const int64_t *>(p.loc)[t]
+                          : static_cast<int64_t>(static_cast<const int32_t *>(p.loc)[t]);
+      const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
+      raw[i] = reinterpret_cast<const uint4 *>(src)[l];
     }
-    float am = 0.f;
+  }
+
 #pragma unroll
-    for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
-    const int lpg = p.group >> 3;  // lanes per scale group
-    for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
-    constexpr float kQ = (FMT == kFmtINT8) ? 127.0f : (FMT == kFmtINT4) ? 7.0f : 448.0f;
-    float sc = __fdiv_rn(am, kQ);
-    if (p.scale_f16) sc = static_cast<float>(static_cast<_Float16>(fminf(sc, 65504.0f)));
-    if ((l & (lpg - 1)) == 0) {
-      uint8_t *sd = is_v ? p.vs + slot * p.vs_ss + h * p.vs_sh : p.ks + slot * p.ks_ss + h * p.ks_sh;
-      const int gi = l / lpg;
-      if (p.scale_f16)
-        reinterpret_cast<_Float16 *>(sd)[gi] = static_cast<_Float16>(sc);
-      else
-        reinterpret_cast<float *>(sd)[gi] = sc;
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t row = row0 + i;
+    if (row >= nrows) break;
+    const int64_t t = (p.hkv == 2) ? (row >> 1) : row;
+    const int h = static_cast<int>(row - t * p.hkv);
+    const int64_t s = slot[i];
+    if (s < 0 || s >= p.slots) {
+      if (lane == 0) atomicOr(p.err, kErrStoreSlot);
+      continue;
     }
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (sc > 0.f) ? __fdiv_rn(x[e], sc) : 0.f;
-    if constexpr (FMT == kFmtINT4) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = static_cast<int>(fminf(fmaxf(__builtin_rintf(y[e]), -7.0f), 7.0f));
-        packed |= static_cast<uint32_t>(q + 8) << (4 * e);
-      }
-      reinterpret_cast<uint32_t *>(dst)[l] = packed;
+    uint8_t *dst = is_v ? p.vp + s * p.vp_ss + h * p.vp_sh : p.kp + s * p.kp_ss + h * p.kp_sh;
+    if constexpr (FMT == kFmtBF16) {
+      reinterpret_cast<uint4 *>(dst)[l] = raw[i];
     } else {
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+      float am = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+      const int lpg = p.group >> 3;  // lanes per scale group
+      for (int m = 1; m < lpg; m <<= 1) am = fmaxf(am, __shfl_xor(am, m));
+      constexpr float kQ = (FMT == kFmtINT8) ? 127.0f : (FMT == kFmtINT4) ? 7.0f : 448.0f;
+      float sc = __fdiv_rn(am, kQ);
+      if (p.scale_f16) sc = static_cast<float>(static_cast<_Float16>(fminf(sc, 65504.0f)));
+      if ((l & (lpg - 1)) == 0) {
+        uint8_t *sd = is_v ? p.vs + s * p.vs_ss + h * p.vs_sh : p.ks + s * p.ks_ss + h * p.ks_sh;
+        const int gi = l / lpg;
+        if (p.scale_f16)
+          reinterpret_cast<_Float16 *>(sd)[gi] = static_cast<_Float16>(sc);
+        else
+          reinterpret_cast<float *>(sd)[gi] = sc;
+      }
+      const float rs = __builtin_amdgcn_rcpf(sc);
       uint32_t c[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if constexpr (FMT == kFmtINT8)
-          c[e] = static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(__builtin_rintf(y[e]), -127.0f), 127.0f))) & 0xFFu;
-        else
-          c[e] = e4m3fn_rne(fminf(fmaxf(y[e], -448.0f), 448.0f));
+        float y = x[e] * rs;
+        const bool near = (FMT == kFmtFP8) ? near_e4m3_boundary(y) : near_half_integer(y);
+        if (near) y = __fdiv_rn(x[e], sc);
+        if (!(sc > 0.f)) y = 0.f;
+        c[e] = code_of<FMT>(y);
       }
-      uint2 out;
-      out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-      reinterpret_cast<uint2 *>(dst)[l] = out;
+      if constexpr (FMT == kFmtINT4) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) packed |= c[e] << (4 * e);
+        reinterpret_cast<uint32_t *>(dst)[l] = packed;
+      } else {
+        uint2 out;
+        out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+        out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+        reinterpret_cast<uint2 *>(dst)[l] = out;
+      }
     }
   }
 }
@@ -116,7 +168,8 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream) {
   const int64_t rows = p.n * p.hkv;
   if (rows <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  const int64_t per_block = 4 * kRowsPerWave;
+  const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
   switch (fmt) {
     case kFmtBF16: hipLaunchKernelGGL(qsa_store_kernel<kFmtBF16>, grid, dim3(256), 0, stream, p); break;
     case kFmtFP8: hipLaunchKernelGGL(qsa_store_kernel<kFmtFP8>, grid, dim3(256), 0, stream, p); break;

@@ -231,3 +231,63 @@ def test_pools_written_on_device_feed_the_decode(fmt, group, scale_dtype):
     rows = sorted(np.random.default_rng(1).choice(64, 16, replace=False).tolist())
     run_and_compare(case, f"decode on device-written {fmt} g{group} {scale_dtype}", rows=rows,
                     quant=(fmt, group, kc, ks, vc, vs), scale_dtype=tdt)
+
+
+def _bf16_grid():
+    """Every finite non-negative bf16 value, as float32."""
+    bits = np.arange(0, 0x7F80, dtype=np.uint32) << 16
+    return bits.view(np.float32)
+
+
+def _adversarial_rows(rng, n, hkv, fmt, group, scale_dtype):
+    """bf16 rows whose quotients x / scale sit on or within a few ulp of a
+    rounding boundary of the code (half-integers for int8 / int4, midpoints
+    of the e4m3fn grid for fp8), so that any shortcut in computing the
+    quotient would change codes."""
+    grid = _bf16_grid()
+    qmax = np.float32(QMAX[fmt])
+    x = np.zeros((n, hkv, 256), np.float32)
+    for r in range(n):
+        for h in range(hkv):
+            for g0 in range(0, 256, group):
+                amax = np.float32(grid[rng.integers(0x3F00, 0x4080)])    # [0.5, 4)
+                s = np.float32(amax / qmax)
+                if scale_dtype == "f16":
+                    s = np.float32(np.float16(min(s, np.float32(65504.0))))
+                cand = grid[grid <= amax]
+                y = (cand / s).astype(np.float32)
+                if fmt == "fp8":
+                    yc = np.minimum(y, np.float32(448.0))
+                    bits = yc.view(np.uint32).astype(np.int64)
+                    dist = np.abs((bits & 0xFFFFF) - 0x80000).astype(np.float64)
+                    sub = yc < np.float32(2.0 ** -6)
+                    t = yc[sub] * np.float32(512.0)
+                    dist[sub] = np.abs(t - np.floor(t) - 0.5) / np.maximum(np.spacing(t), 1e-30)
+                else:
+                    dist = np.abs(y - np.floor(y) - 0.5) / np.spacing(np.maximum(y, 1.0))
+                pick = cand[np.argsort(dist, kind="stable")[: 4 * group]]
+                vals = rng.choice(pick, group - 1, replace=False)
+                vals = vals * np.where(rng.random(group - 1) < 0.5, -1, 1)
+                x[r, h, g0] = amax
+                x[r, h, g0 + 1: g0 + group] = vals
+    return synth.to_bf16(x)
+
+
+@pytest.mark.parametrize("fmt,group", [("int8", 32), ("int8", 256), ("int4", 32), ("fp8", 32),
+                                       ("fp8", 256)])
+@pytest.mark.parametrize("scale_dtype", ["f32", "f16"])
+def test_store_quotients_near_rounding_boundaries(fmt, group, scale_dtype):
+    seed = zlib.crc32(f"adv/{fmt}/{group}/{scale_dtype}".encode())
+    rng = np.random.default_rng(seed)
+    slots, n, hkv = 256, 48, 2
+    label = f"near-boundary store {fmt} g{group} {scale_dtype}"
+    say(f"[gpu] {label}")
+    host, dev = _pools(rng, slots, hkv, fmt, group, scale_dtype)
+    xk = _adversarial_rows(rng, n, hkv, fmt, group, scale_dtype)
+    xv = _adversarial_rows(rng, n, hkv, fmt, group, scale_dtype)
+    loc = rng.permutation(slots)[:n].astype(np.int32)
+    qsa.kv_store(xk.cuda(), xv.cuda(), torch.from_numpy(loc).cuda(), dev[0], dev[1], kv_format=fmt,
+                 k_scale=dev[2], v_scale=dev[3], group_size=group)
+    torch.cuda.synchronize()
+    exp = _expected(*host, xk, xv, loc, fmt, group, scale_dtype)
+    _check_pools(dev, exp, label)
