@@ -297,6 +297,23 @@ qsa_status check_pools(const char *fn, const qsa_tensor *k_pool, const qsa_tenso
 }
 
 
+// True when every row and scale the decode can read lies within 4 GiB of
+// its pool's (KV head's) start and the offset is a 24-bit x 24-bit product:
+// slot ids and byte strides below 2^24, (slots - 1) * stride + row bytes
+// below 2^32.  The kernel then forms addresses with 32-bit arithmetic.
+bool addresses_fit_32(const PoolDesc &pd, const qsa_tensor *k_pool, const qsa_tensor *v_pool) {
+  constexpr int64_t k24 = int64_t{1} << 24, k32 = int64_t{1} << 32;
+  if (pd.slots >= k24) return false;
+  auto fits = [&](int64_t ss, int64_t row) { return ss < k24 && (pd.slots - 1) * ss + row < k32; };
+  const int64_t row = (pd.fmt == qsa::kFmtINT4 ? 128 : 256) * pd.eb;
+  if (!fits(k_pool->stride[0] * pd.eb, row) || !fits(v_pool->stride[0] * pd.eb, row)) return false;
+  if (pd.ks != nullptr) {
+    const int64_t srow = (QSA_HEAD_DIM / pd.group) * (pd.scale_f16 ? 2 : 4);
+    if (!fits(pd.ks_ss, srow) || !fits(pd.vs_ss, srow)) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +428,7 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.vs_ss = pd.vs_ss;
   p.vs_sh = pd.vs_sh;
   p.scale_f16 = pd.scale_f16;
+  p.a32 = addresses_fit_32(pd, k_pool, v_pool) ? 1 : 0;
   p.sel = static_cast<const int32_t *>(sel_indices->data);
   p.n_sel = sel_indices->shape[0];
   p.cu = static_cast<const int32_t *>(cu_seqlens->data);

@@ -172,7 +172,7 @@ __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthre
   if (tid < kGqa) p.lse[b * p.l_sb + (g * kGqa + tid) * p.l_sh] = __builtin_nanf("");
 }
 
-template <int FMT, int G, int W, bool SF16>
+template <int FMT, int G, int W, bool SF16, bool A32>
 __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params p) {
   using Part = typename Fmt<FMT>::Part;
   using GEO = Geo<FMT>;
@@ -237,13 +237,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   float *ksc = reinterpret_cast<float *>(wlds + 2 * LDS::kTileB);    // [16][NG]
   float *vsc = ksc + LDS::kScaleFloats;                              // [16][NG]
 
-  const uint8_t *kbase = p.k + g * p.k_sh + 16 * lchunk;
-  const uint8_t *vbase = p.v + g * p.v_sh + 16 * lchunk;
+  // Row addresses.  With A32 (every pool byte within 4 GiB of the pool
+  // start, slot ids and strides below 2^24) a row's address is a
+  // workgroup-uniform base plus one 24-bit multiply-add per lane (a 32-bit
+  // offset the load adds to a scalar base); otherwise 64-bit arithmetic.
+  const uint8_t *kpool = p.k + g * p.k_sh;
+  const uint8_t *vpool = p.v + g * p.v_sh;
+  const uint8_t *kbase = kpool + 16 * lchunk;
+  const uint8_t *vbase = vpool + 16 * lchunk;
+  const uint32_t k_ss32 = static_cast<uint32_t>(p.k_ss), v_ss32 = static_cast<uint32_t>(p.v_ss);
+  const uint32_t lane16 = 16u * static_cast<uint32_t>(lchunk);
   // every lane loads a scale (lanes past the row's NG groups re-read group
   // 0, so no load is conditional); only lanes lchunk < NG store them
   const int sgrp = (NG > 0 && lchunk < NG) ? lchunk : 0;
-  const uint8_t *ksbase = (NG > 0) ? p.ks + g * p.ks_sh + sgrp * sizeof(Scale) : nullptr;
-  const uint8_t *vsbase = (NG > 0) ? p.vs + g * p.vs_sh + sgrp * sizeof(Scale) : nullptr;
+  const uint8_t *kspool = (NG > 0) ? p.ks + g * p.ks_sh : nullptr;
+  const uint8_t *vspool = (NG > 0) ? p.vs + g * p.vs_sh : nullptr;
+  const uint8_t *ksbase = (NG > 0) ? kspool + sgrp * sizeof(Scale) : nullptr;
+  const uint8_t *vsbase = (NG > 0) ? vspool + sgrp * sizeof(Scale) : nullptr;
+  const uint32_t ks_ss32 = static_cast<uint32_t>(p.ks_ss), vs_ss32 = static_cast<uint32_t>(p.vs_ss);
+  const uint32_t sgrpb = static_cast<uint32_t>(sgrp * sizeof(Scale));
   const int32_t *selw = p.sel + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
 
@@ -309,15 +321,19 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     for (int i = 0; i < NI; ++i) slot[i] = checked(sl[i]);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kraw[u][i] = *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(slot[i]) * p.k_ss);
+      kraw[u][i] = A32 ? *reinterpret_cast<const uint4 *>(kpool + static_cast<uint64_t>(__umul24(slot[i], k_ss32) + lane16))
+                       : *reinterpret_cast<const uint4 *>(kbase + static_cast<int64_t>(slot[i]) * p.k_ss);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      vraw[u][i] = *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(slot[i]) * p.v_ss);
+      vraw[u][i] = A32 ? *reinterpret_cast<const uint4 *>(vpool + static_cast<uint64_t>(__umul24(slot[i], v_ss32) + lane16))
+                       : *reinterpret_cast<const uint4 *>(vbase + static_cast<int64_t>(slot[i]) * p.v_ss);
     if constexpr (NG > 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        ksr[u][i] = *reinterpret_cast<const Scale *>(ksbase + static_cast<int64_t>(slot[i]) * p.ks_ss);
-        vsr[u][i] = *reinterpret_cast<const Scale *>(vsbase + static_cast<int64_t>(slot[i]) * p.vs_ss);
+        ksr[u][i] = A32 ? *reinterpret_cast<const Scale *>(kspool + static_cast<uint64_t>(__umul24(slot[i], ks_ss32) + sgrpb))
+                        : *reinterpret_cast<const Scale *>(ksbase + static_cast<int64_t>(slot[i]) * p.ks_ss);
+        vsr[u][i] = A32 ? *reinterpret_cast<const Scale *>(vspool + static_cast<uint64_t>(__umul24(slot[i], vs_ss32) + sgrpb))
+                        : *reinterpret_cast<const Scale *>(vsbase + static_cast<int64_t>(slot[i]) * p.vs_ss);
       }
     }
   };
@@ -751,12 +767,20 @@ __global__ void audit_kernel(const uint32_t *ctr, int n, uint32_t *accum) {
   }
 }
 
-template <int FMT, int G, bool SF16>
+template <int FMT, int G, bool SF16, bool A32>
 void launch_waves(const Params &p, dim3 grid, hipStream_t stream) {
   if (p.waves == 8)
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16, A32>), grid, dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16, A32>), grid, dim3(256), 0, stream, p);
+}
+
+template <int FMT, int G, bool SF16>
+void launch_addr(const Params &p, dim3 grid, hipStream_t stream) {
+  if (p.a32)
+    launch_waves<FMT, G, SF16, true>(p, grid, stream);
+  else
+    launch_waves<FMT, G, SF16, false>(p, grid, stream);
 }
 
 template <int FMT, int G>
@@ -764,12 +788,12 @@ hipError_t launch_one(const Params &p, hipStream_t stream) {
   const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
   const dim3 grid(npairs8 * p.nsplit);
   if constexpr (FMT == kFmtBF16) {
-    launch_waves<FMT, G, false>(p, grid, stream);
+    launch_addr<FMT, G, false>(p, grid, stream);
   } else {
     if (p.scale_f16)
-      launch_waves<FMT, G, true>(p, grid, stream);
+      launch_addr<FMT, G, true>(p, grid, stream);
     else
-      launch_waves<FMT, G, false>(p, grid, stream);
+      launch_addr<FMT, G, false>(p, grid, stream);
   }
   return hipGetLastError();
 }

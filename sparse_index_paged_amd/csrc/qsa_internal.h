@@ -34,6 +34,8 @@ struct Params {
   int64_t ks_ss, ks_sh;     // byte strides
   int64_t vs_ss, vs_sh;
   int scale_f16;            // scales are f16 (else f32)
+  int a32;                  // every row / scale address fits a 24-bit slot x 24-bit stride
+                            // product below 2^32 bytes from its pool's start
   const int32_t *sel;
   int64_t n_sel;
   const int32_t *cu;
