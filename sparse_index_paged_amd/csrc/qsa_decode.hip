@@ -24,15 +24,17 @@
 //     per MFMA), the B operand is Q from a tile shared by the workgroup
 //     (heads 12..15 zero).
 //     The result holds, in lane l, head l % 16 for list entries
-//     4*(l/16) + 0..3 -- exactly the B-operand layout of the PV product, so
-//     P never moves between lanes.
-//   * PV as O^T = V^T . P^T with v_mfma_f32_16x16x16_bf16: V^T needs the
-//     transpose of the gathered rows, which the wave reads column-wise from
-//     its LDS copy of the V tile.  The accumulator O^T keeps head
-//     l % 16 in lane l, the same lane that owns that head's running max and
-//     sum, so the rescale by exp(m_old - m_new) needs no shuffle.
-//   * P enters the PV product as a hi + lo bf16 pair (two MFMAs), so the
-//     product sees P to ~16 bits instead of bf16's 8.  Quantized codes are
+//     4*(l/16) + 0..3 -- the entries whose P values the lane then feeds to
+//     the PV product, so P never moves between lanes.
+//   * PV as O^T = V^T . P^T with v_mfma_f32_16x16x32_bf16: V^T is read
+//     from the wave's LDS copy of the V tile with transposing LDS reads.
+//     The accumulator O^T keeps head l % 16 in lane l, the same lane that
+//     owns that head's running max and sum, so the rescale by
+//     exp(m_old - m_new) needs no shuffle.
+//   * P enters the PV product as a hi + lo bf16 pair, so the product sees P
+//     to ~16 bits instead of bf16's 8: the 32 k-slots of one product hold
+//     the tile's 16 entries twice, with P's hi parts against the first copy
+//     of V and its lo parts against the second.  Quantized codes are
 //     converted exactly to bf16; their fp32 scales are applied outside the
 //     MFMA (K scales on the QK partial of each channel group, V scales folded
 //     into P).
@@ -48,6 +50,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -463,11 +466,17 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       hi = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
       lo = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
     };
+    // One 16x16x32 product per channel block: in lane group qg the eight
+    // k-slots hold entries 4*qg .. 4*qg+3 twice, with the V values
+    // duplicated in A and P's hi parts then lo parts in B, so the product
+    // adds V^T . P_hi + V^T . P_lo.
     auto pv_mfma = [&](int mt, const i16x4 &hi, const i16x4 &lo) {
       const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) i16x4 *)(vtr + (2 * mt % P) * kPartB + (2 * mt / P) * 16));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, hi, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, lo, acc[mt], 0, 0, 0);
+      const i16x8 a2 = __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3);
+      const i16x8 b2 = __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a2),
+                                                        __builtin_bit_cast(bf16x8, b2), acc[mt], 0, 0, 0);
     };
     if constexpr (NG <= 1) {
       float pv[4];

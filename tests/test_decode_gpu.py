@@ -223,3 +223,27 @@ def test_one_launch_per_call_and_counters_at_rest():
     say(f"  decode kernels seen: {len(kernels)}")
     assert len(kernels) == 3
     assert all(v == 0 for v in qsa.debug_counters())
+
+
+def test_pools_beyond_32bit_offsets():
+    """Pools whose slot stride is 2^24 bytes (a strided view into a 4.4 GB
+    buffer per pool), so row offsets do not fit the 32-bit address form and
+    the 64-bit path is used; compared with the oracle on a compact copy."""
+    slots, hkv = 260, 2
+    case = synth.make_case(lengths=[2055, 700, 1, 0, 1500], slots=slots, hkv=hkv, seed=88,
+                           dup_prob=0.05)
+    stride = 1 << 23  # bf16 elements = 2^24 bytes per slot
+    say(f"[gpu] 64-bit addressing: slots={slots} slot stride={2 * stride} B")
+    kb = torch.empty(slots * stride, dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty(slots * stride, dtype=torch.bfloat16, device="cuda")
+    k = kb.as_strided((slots, hkv, 256), (stride, 256, 1))
+    v = vb.as_strided((slots, hkv, 256), (stride, 256, 1))
+    k.copy_(case.k_pool.cuda())
+    v.copy_(case.v_pool.cuda())
+    out, lse = qsa.decode(case.q.cuda(), k, v, torch.from_numpy(case.sel).cuda(),
+                          torch.from_numpy(case.cu).cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_rows(case.q, case.k_pool, case.v_pool, case.sel, case.cu)
+    compare(out, lse, o_ref, l_ref, case.lengths, label="64-bit addressing")
+    del kb, vb
+    torch.cuda.empty_cache()
