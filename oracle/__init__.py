@@ -66,6 +66,11 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
             ctypes.c_int, ctypes.c_int64, P, P, P, P, P, ctypes.c_int64, P,
             ctypes.c_double, P, P, ctypes.c_int]
+        lib.oracle_qsa_decode_tiered.restype = ctypes.c_int
+        lib.oracle_qsa_decode_tiered.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int64, P, P, P, P, P,
+            ctypes.c_int64, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_double, P, P,
+            ctypes.c_int]
         lib.oracle_dequant_row.restype = None
         lib.oracle_dequant_row.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int64,
@@ -144,6 +149,48 @@ def decode(q, k_pool, v_pool, sel, cu, *, fmt: str = "bf16", group: int = 256,
         bs, hq, hkv, _ptr(qb), FMT_BY_NAME[fmt], group, slots, _ptr(kb),
         _ptr(vb), _ptr(ks), _ptr(vs), _ptr(sel_np), sel_np.size, _ptr(cu_np),
         sm_scale, _ptr(out), _ptr(lse), nthreads)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call: {ERRORS.get(rc, rc)}")
+    return out, lse
+
+
+def decode_tiered(q, owner, ring_k, ring_v, ring_k_scale, ring_v_scale, cold_k, cold_v,
+                  cold_k_scale, cold_v_scale, sel, cu, *, sm_scale: float = 1.0 / 16.0,
+                  nthreads: int = 1):
+    """Packed QSA decode over a tiered pool, in float64.
+
+    Follows the page "feat(qsa): quantized KV pools with dequant-on-gather
+    (fp8/int8/int4)", part 4 "Modifications", tiered pool bullet: listed
+    slot s reads ring row r = s & (R - 1) (int8 codes, one scale per 64
+    channels) when owner[r] == s, else its int4 row (one scale per 32
+    channels).
+
+    owner [R] int32 (R a power of two); ring_k / ring_v [R, hkv, 256] int8;
+    ring scales [R, hkv, 4]; cold_k / cold_v [slots, hkv, 128] uint8 (two
+    int4 codes per byte); cold scales [slots, hkv, 8]; scales as float32 or
+    float16 (their values are used).  Returns (out, lse) like decode().
+    """
+    lib = _load()
+    qb = _as_u16(q)
+    bs, hq, d = qb.shape
+    assert d == HEAD_DIM
+    own = np.ascontiguousarray(np.asarray(owner, dtype=np.int32))
+    rk, rv = _as_bytes(ring_k), _as_bytes(ring_v)
+    ck, cv = _as_bytes(cold_k), _as_bytes(cold_v)
+    ring_rows, hkv = rk.shape[0], rk.shape[1]
+    slots = ck.shape[0]
+    rks, rvs = _as_f32(ring_k_scale), _as_f32(ring_v_scale)
+    cks, cvs = _as_f32(cold_k_scale), _as_f32(cold_v_scale)
+    assert own.shape == (ring_rows,) and rks.shape == (ring_rows, hkv, 4)
+    assert ck.shape == (slots, hkv, 128) and cks.shape == (slots, hkv, 8)
+    sel_np = np.ascontiguousarray(np.asarray(sel, dtype=np.int32))
+    cu_np = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    out = np.empty((bs, hq, HEAD_DIM), dtype=np.float64)
+    lse = np.empty((bs, hq), dtype=np.float64)
+    rc = lib.oracle_qsa_decode_tiered(
+        bs, hq, hkv, _ptr(qb), ring_rows, _ptr(own), _ptr(rk), _ptr(rv), _ptr(rks), _ptr(rvs),
+        slots, _ptr(ck), _ptr(cv), _ptr(cks), _ptr(cvs), _ptr(sel_np), sel_np.size,
+        _ptr(cu_np), sm_scale, _ptr(out), _ptr(lse), nthreads)
     if rc != 0:
         raise ValueError(f"oracle rejected the call: {ERRORS.get(rc, rc)}")
     return out, lse

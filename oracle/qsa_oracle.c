@@ -29,6 +29,13 @@
  *   holding the even channel, stored offset-binary (q + 8), times a scale per
  *   32-channel group.  Dequantization is code value times its group scale.
  *
+ *   Same page and section, tiered pool bullet: every token is written to an
+ *   int8 ring of R rows (R a power of two, one fp16 scale per 64 channels)
+ *   and to the full int4 pool (one fp16 scale per 32 channels), and an int32
+ *   owner table records which slot each ring row holds; a reader takes the
+ *   ring row r = slot & (R - 1) when owner[r] == slot and the int4 row
+ *   otherwise.  oracle_qsa_decode_tiered makes that choice per listed entry.
+ *
  * Readings where the pages are silent (each one is listed in the design
  * notes): the softmax scale is 1/sqrt(256) = 1/16; Q head h uses KV head
  * h / 12; lse is the natural log of the sum of exp over the scaled logits;
@@ -150,6 +157,91 @@ static int check_packing(int bs, const int32_t *cu, int64_t n_sel,
   return ORC_OK;
 }
 
+/* Where the K and V rows of a listed slot come from: one pool, or the
+ * tiered pair (int8 ring + int4 pool with an owner table). */
+struct kv_source {
+  int tiered;
+  int hkv;
+  /* single pool (tiered: the int4 pool) */
+  int fmt, group;
+  const void *k_pool, *v_pool;
+  const float *k_scale, *v_scale;
+  /* tiered: ring of R rows */
+  int64_t ring_rows;
+  const int32_t *owner;
+  const void *ring_k, *ring_v;
+  const float *ring_k_scale, *ring_v_scale;
+};
+
+/* The dequantized K (is_v = 0) or V (is_v = 1) row of (slot, kv head g). */
+static void fetch_row(const struct kv_source *src, int is_v, int64_t slot, int g, double *out) {
+  if (src->tiered) {
+    const int64_t r = slot & (src->ring_rows - 1);
+    if (src->owner[r] == slot) {
+      oracle_dequant_row(ORC_INT8, 64, src->hkv, is_v ? src->ring_v : src->ring_k,
+                         is_v ? src->ring_v_scale : src->ring_k_scale, r, g, out);
+      return;
+    }
+    oracle_dequant_row(ORC_INT4, 32, src->hkv, is_v ? src->v_pool : src->k_pool,
+                       is_v ? src->v_scale : src->k_scale, slot, g, out);
+    return;
+  }
+  oracle_dequant_row(src->fmt, src->group, src->hkv, is_v ? src->v_pool : src->k_pool,
+                     is_v ? src->v_scale : src->k_scale, slot, g, out);
+}
+
+/* Two-pass softmax attention of every (row, Q head) over its listed rows. */
+static void attend(int bs, int hq, const uint16_t *q, const struct kv_source *src,
+                   const int32_t *sel, const int32_t *cu, double sm_scale, double *out,
+                   double *lse, int nthreads) {
+  const int npairs = bs * hq;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int pair = 0; pair < npairs; ++pair) {
+    const int b = pair / hq;
+    const int h = pair % hq;
+    const int g = h / ORC_GQA;
+    const int32_t begin = cu[b];
+    const int32_t len = cu[b + 1] - cu[b];
+    double *o = out + ((int64_t)b * hq + h) * ORC_HEAD_DIM;
+
+    double qv[ORC_HEAD_DIM];
+    for (int d = 0; d < ORC_HEAD_DIM; ++d)
+      qv[d] = bf16_to_double(q[((int64_t)b * hq + h) * ORC_HEAD_DIM + d]);
+
+    if (len == 0) { /* empty sum: o = 0, lse = log(0) */
+      for (int d = 0; d < ORC_HEAD_DIM; ++d) o[d] = 0.0;
+      lse[(int64_t)b * hq + h] = -INFINITY;
+      continue;
+    }
+
+    /* pass 1: logits s_j = sm_scale * sum_d q[d] * K_j[d], list order */
+    double *s = (double *)malloc(sizeof(double) * (size_t)len);
+    double row[ORC_HEAD_DIM];
+    double m = -INFINITY;
+    for (int32_t j = 0; j < len; ++j) {
+      fetch_row(src, 0, sel[begin + j], g, row);
+      double dot = 0.0;
+      for (int d = 0; d < ORC_HEAD_DIM; ++d) dot += qv[d] * row[d];
+      s[j] = dot * sm_scale;
+      if (s[j] > m) m = s[j];
+    }
+
+    /* pass 2: p_j = exp(s_j - m), l = sum p_j, o = sum p_j V_j / l */
+    double l = 0.0;
+    double acc[ORC_HEAD_DIM];
+    for (int d = 0; d < ORC_HEAD_DIM; ++d) acc[d] = 0.0;
+    for (int32_t j = 0; j < len; ++j) {
+      double p = exp(s[j] - m);
+      l += p;
+      fetch_row(src, 1, sel[begin + j], g, row);
+      for (int d = 0; d < ORC_HEAD_DIM; ++d) acc[d] += p * row[d];
+    }
+    for (int d = 0; d < ORC_HEAD_DIM; ++d) o[d] = acc[d] / l;
+    lse[(int64_t)b * hq + h] = m + log(l);
+    free(s);
+  }
+}
+
 /*
  * oracle_qsa_decode
  *   q        [bs][hq][256] bf16 bits, contiguous
@@ -177,53 +269,56 @@ int oracle_qsa_decode(int bs, int hq, int hkv, const uint16_t *q, int fmt,
   int rc = check_packing(bs, cu, n_sel, sel, slots);
   if (rc != ORC_OK) return rc;
   if (nthreads < 1) nthreads = 1;
+  struct kv_source src = {0};
+  src.hkv = hkv;
+  src.fmt = fmt;
+  src.group = group;
+  src.k_pool = k_pool;
+  src.v_pool = v_pool;
+  src.k_scale = k_scale;
+  src.v_scale = v_scale;
+  attend(bs, hq, q, &src, sel, cu, sm_scale, out, lse, nthreads);
+  return ORC_OK;
+}
 
-  const int npairs = bs * hq;
-#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
-  for (int pair = 0; pair < npairs; ++pair) {
-    const int b = pair / hq;
-    const int h = pair % hq;
-    const int g = h / ORC_GQA;
-    const int32_t begin = cu[b];
-    const int32_t len = cu[b + 1] - cu[b];
-    double *o = out + ((int64_t)b * hq + h) * ORC_HEAD_DIM;
-
-    double qv[ORC_HEAD_DIM];
-    for (int d = 0; d < ORC_HEAD_DIM; ++d)
-      qv[d] = bf16_to_double(q[((int64_t)b * hq + h) * ORC_HEAD_DIM + d]);
-
-    if (len == 0) { /* empty sum: o = 0, lse = log(0) */
-      for (int d = 0; d < ORC_HEAD_DIM; ++d) o[d] = 0.0;
-      lse[(int64_t)b * hq + h] = -INFINITY;
-      continue;
-    }
-
-    /* pass 1: logits s_j = sm_scale * sum_d q[d] * K_j[d], list order */
-    double *s = (double *)malloc(sizeof(double) * (size_t)len);
-    double row[ORC_HEAD_DIM];
-    double m = -INFINITY;
-    for (int32_t j = 0; j < len; ++j) {
-      oracle_dequant_row(fmt, group, hkv, k_pool, k_scale, sel[begin + j], g, row);
-      double dot = 0.0;
-      for (int d = 0; d < ORC_HEAD_DIM; ++d) dot += qv[d] * row[d];
-      s[j] = dot * sm_scale;
-      if (s[j] > m) m = s[j];
-    }
-
-    /* pass 2: p_j = exp(s_j - m), l = sum p_j, o = sum p_j V_j / l */
-    double l = 0.0;
-    double acc[ORC_HEAD_DIM];
-    for (int d = 0; d < ORC_HEAD_DIM; ++d) acc[d] = 0.0;
-    for (int32_t j = 0; j < len; ++j) {
-      double p = exp(s[j] - m);
-      l += p;
-      oracle_dequant_row(fmt, group, hkv, v_pool, v_scale, sel[begin + j], g, row);
-      for (int d = 0; d < ORC_HEAD_DIM; ++d) acc[d] += p * row[d];
-    }
-    for (int d = 0; d < ORC_HEAD_DIM; ++d) o[d] = acc[d] / l;
-    lse[(int64_t)b * hq + h] = m + log(l);
-    free(s);
-  }
+/*
+ * oracle_qsa_decode_tiered -- same contract, rows from a tiered pool:
+ *   ring_k / ring_v   [ring_rows][hkv][256] int8 codes
+ *   ring_k_scale ...  [ring_rows][hkv][4] fp32 (the fp16 scales' values)
+ *   owner             [ring_rows] int32
+ *   cold_k / cold_v   [slots][hkv][128] int4 pairs
+ *   cold_k_scale ...  [slots][hkv][8] fp32 (the fp16 scales' values)
+ * ring_rows must be a power of two.
+ */
+int oracle_qsa_decode_tiered(int bs, int hq, int hkv, const uint16_t *q, int64_t ring_rows,
+                             const int32_t *owner, const void *ring_k, const void *ring_v,
+                             const float *ring_k_scale, const float *ring_v_scale,
+                             int64_t slots, const void *cold_k, const void *cold_v,
+                             const float *cold_k_scale, const float *cold_v_scale,
+                             const int32_t *sel, int64_t n_sel, const int32_t *cu,
+                             double sm_scale, double *out, double *lse, int nthreads) {
+  if (bs < 1 || hkv < 1 || hq != ORC_GQA * hkv || slots < 1) return ORC_BAD_ARGS;
+  if (ring_rows < 1 || (ring_rows & (ring_rows - 1)) != 0) return ORC_BAD_ARGS;
+  if (!owner || !ring_k || !ring_v || !ring_k_scale || !ring_v_scale || !cold_k || !cold_v ||
+      !cold_k_scale || !cold_v_scale)
+    return ORC_BAD_ARGS;
+  int rc = check_packing(bs, cu, n_sel, sel, slots);
+  if (rc != ORC_OK) return rc;
+  if (nthreads < 1) nthreads = 1;
+  struct kv_source src = {0};
+  src.tiered = 1;
+  src.hkv = hkv;
+  src.k_pool = cold_k;
+  src.v_pool = cold_v;
+  src.k_scale = cold_k_scale;
+  src.v_scale = cold_v_scale;
+  src.ring_rows = ring_rows;
+  src.owner = owner;
+  src.ring_k = ring_k;
+  src.ring_v = ring_v;
+  src.ring_k_scale = ring_k_scale;
+  src.ring_v_scale = ring_v_scale;
+  attend(bs, hq, q, &src, sel, cu, sm_scale, out, lse, nthreads);
   return ORC_OK;
 }
 

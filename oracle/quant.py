@@ -152,3 +152,43 @@ def rel_rms(x, xq) -> float:
     x = np.asarray(x, dtype=np.float64)
     xq = np.asarray(xq, dtype=np.float64)
     return float(np.sqrt(np.mean((x - xq) ** 2) / np.mean(x ** 2)))
+
+
+def store_tiered(k_new, v_new, loc, ring, cold):
+    """Write side of the tiered pool (page "feat(qsa): quantized KV pools
+    with dequant-on-gather (fp8/int8/int4)", part 4 "Modifications", tiered
+    pool bullet): every token is written as int8 with one fp16 scale per 64
+    channels into ring row loc & (R - 1), whose owner entry is stamped with
+    loc, and as int4 with one fp16 scale per 32 channels into its own slot
+    of the full pool.
+
+    Reading where the pages are silent: when several tokens of one call map
+    to the same ring row, the token with the largest index wins (row and
+    owner both come from it).
+
+    ring = dict(k, v, k_scale, v_scale, owner) numpy arrays ([R, hkv, 256]
+    int8, [R, hkv, 4] float32 values of fp16 scales, [R] int32);
+    cold = dict(k, v, k_scale, v_scale) ([slots, hkv, 128] uint8,
+    [slots, hkv, 8]).  Returns updated copies (ring, cold)."""
+    loc = np.asarray(loc, dtype=np.int64)
+    ring = {name: np.array(a, copy=True) for name, a in ring.items()}
+    cold = {name: np.array(a, copy=True) for name, a in cold.items()}
+    r_rows = ring["owner"].shape[0]
+    assert r_rows & (r_rows - 1) == 0
+    k8, ks8 = quantize_int8(k_new, 64, "f16")
+    v8, vs8 = quantize_int8(v_new, 64, "f16")
+    k4, ks4 = quantize_int4(k_new, 32, "f16")
+    v4, vs4 = quantize_int4(v_new, 32, "f16")
+    cold["k"][loc] = k4
+    cold["v"][loc] = v4
+    cold["k_scale"][loc] = ks4
+    cold["v_scale"][loc] = vs4
+    for t in range(loc.shape[0]):          # in token order: a later token overwrites
+        r = int(loc[t]) & (r_rows - 1)
+        ring["k"][r] = k8[t]
+        ring["v"][r] = v8[t]
+        ring["k_scale"][r] = ks8[t]
+        ring["v_scale"][r] = vs8[t]
+        ring["owner"][r] = int(loc[t])
+    return ring, cold
+
