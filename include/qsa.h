@@ -50,7 +50,7 @@ extern "C" {
 /* Same declaration as in the HIP runtime headers. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define QSA_ABI_VERSION 2
+#define QSA_ABI_VERSION 3
 #define QSA_HEAD_DIM 256
 #define QSA_GQA 12
 #define QSA_MAX_SEL 2055
@@ -94,6 +94,34 @@ typedef struct qsa_kv_scales {
   qsa_tensor v_scale;
   int32_t group_size;
 } qsa_kv_scales;
+
+/* A tiered pool (page "feat(qsa): quantized KV pools with dequant-on-gather
+ * (fp8/int8/int4)", part 4 "Modifications", tiered pool bullet): every
+ * token lives as int4 in a full pool and, while it is among the latest
+ * written, also as int8 in a ring of R rows (R a power of two).  Ring row
+ * r holds the token whose slot id is owner[r]; list entry s reads ring row
+ * s & (R-1) when owner[s & (R-1)] == s, otherwise its int4 row.
+ *
+ *   ring_k, ring_v             [R, Hkv, 256] i8, rows on 16-byte boundaries
+ *   ring_k_scale, ring_v_scale [R, Hkv, 4] f16 (one scale per 64 channels)
+ *   owner                      [R] i32, contiguous; a row owned by no slot
+ *                              holds -1 (any value that is not a listed slot
+ *                              id reads the int4 row)
+ *   claim                      [R] i32, contiguous, all zero between calls;
+ *                              scratch of qsa_kv_store_tiered, which leaves
+ *                              it zero (qsa_decode_tiered does not read it)
+ *   cold_k, cold_v             [slots, Hkv, 128] u4x2, rows on 16-byte
+ *                              boundaries
+ *   cold_k_scale, cold_v_scale [slots, Hkv, 8] f16 (one scale per 32 channels)
+ * Hkv is 1 or 2 for both tiers.  All memory is owned by the caller. */
+typedef struct qsa_tiered_pool {
+  qsa_tensor ring_k, ring_v;
+  qsa_tensor ring_k_scale, ring_v_scale;
+  qsa_tensor owner;
+  qsa_tensor claim;
+  qsa_tensor cold_k, cold_v;
+  qsa_tensor cold_k_scale, cold_v_scale;
+} qsa_tiered_pool;
 
 /*
  * qsa_decode -- one packed QSA decode step (one kernel launch).
@@ -157,6 +185,32 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
 qsa_status qsa_kv_store(const qsa_tensor *k_new, const qsa_tensor *v_new,
                         const qsa_tensor *loc, qsa_tensor *k_pool, qsa_tensor *v_pool,
                         const qsa_kv_scales *kv_scales, hipStream_t stream);
+
+/*
+ * qsa_decode_tiered -- qsa_decode over a tiered pool (one kernel launch):
+ * each listed slot is read from the tier the owner table names, dequantized
+ * with that tier's scales.  q, sel_indices, cu_seqlens, out, lse, stream,
+ * the workspace and the device error bits are as for qsa_decode; slot ids
+ * are checked against the int4 pool's slots.
+ */
+qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
+                             const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                             qsa_tensor *out, qsa_tensor *lse, hipStream_t stream);
+
+/*
+ * qsa_kv_store_tiered -- write new K/V rows into a tiered pool (three
+ * kernel launches on `stream`).  k_new, v_new and loc are as for
+ * qsa_kv_store (distinct slot ids).  Every token t is quantized to int4
+ * with 32-channel scales into slot loc[t] of the int4 pool, and to int8
+ * with 64-channel scales into ring row loc[t] & (R-1), whose owner entry
+ * becomes loc[t]; the arithmetic is that of qsa_kv_store.  When several
+ * tokens of one call map to the same ring row, the one with the largest t
+ * is written there.  A slot id outside [0, slots) skips the token and sets
+ * bit 2 of the device error word.  pool->claim must be all zero on entry
+ * and is all zero again when the launches have run.
+ */
+qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
+                               const qsa_tensor *loc, qsa_tiered_pool *pool, hipStream_t stream);
 
 /* Create (or grow) the current device's workspace for calls with up to
  * max_bs rows and the given head layout, and zero its counters.  Call it

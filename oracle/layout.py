@@ -38,3 +38,20 @@ def tiered_bytes_per_token(ring_slots: int, context: int, *, kv_heads: int = 2,
     cold = bytes_per_token("int4", 32, kv_heads=kv_heads, layers=layers)
     hot = bytes_per_token("int8", 64, kv_heads=kv_heads, layers=layers)
     return cold + hot * ring_slots / context
+
+
+def empty_tiered(ring_rows: int, slots: int, hkv: int = 2):
+    """Host arrays of an empty tiered pool: the int8 ring (codes, float32
+    values of the fp16 64-channel scales, owner table with -1 = no slot) and
+    the int4 pool (all codes 0, i.e. nibble 8, and zero 32-channel scales)."""
+    import numpy as np
+    ring = dict(k=np.zeros((ring_rows, hkv, HEAD_DIM), np.int8),
+                v=np.zeros((ring_rows, hkv, HEAD_DIM), np.int8),
+                k_scale=np.zeros((ring_rows, hkv, HEAD_DIM // 64), np.float32),
+                v_scale=np.zeros((ring_rows, hkv, HEAD_DIM // 64), np.float32),
+                owner=np.full(ring_rows, -1, np.int32))
+    cold = dict(k=np.full((slots, hkv, HEAD_DIM // 2), 0x88, np.uint8),
+                v=np.full((slots, hkv, HEAD_DIM // 2), 0x88, np.uint8),
+                k_scale=np.zeros((slots, hkv, HEAD_DIM // 32), np.float32),
+                v_scale=np.zeros((slots, hkv, HEAD_DIM // 32), np.float32))
+    return ring, cold

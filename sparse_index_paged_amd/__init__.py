@@ -17,8 +17,10 @@ from ._binding import (  # noqa: F401
     debug_counters,
     debug_device_error,
     decode,
+    decode_tiered,
     get_option,
     kv_store,
+    kv_store_tiered,
     lib_path,
     load_library,
     plan,
@@ -30,7 +32,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "decode", "kv_store", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
+    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
     "ABI_VERSION",

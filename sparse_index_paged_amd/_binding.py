@@ -7,7 +7,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "libqsa.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # qsa_dtype
 BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2, I64 = 1, 2, 3, 4, 5, 6, 7, 8
@@ -15,7 +15,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORK
           4: "QSA_ERR_HIP"}
 
 EXPORTS = (
-    "qsa_decode", "qsa_kv_store", "qsa_workspace_reserve", "qsa_workspace_reset",
+    "qsa_decode", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_workspace_reserve", "qsa_workspace_reset",
     "qsa_workspace_release", "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
     "qsa_debug_counters", "qsa_debug_read_counters", "qsa_debug_audit_counters",
     "qsa_debug_device_error", "qsa_abi_version",
@@ -36,6 +36,17 @@ class QsaTensor(ctypes.Structure):
 
 class QsaKvScales(ctypes.Structure):
     _fields_ = [("k_scale", QsaTensor), ("v_scale", QsaTensor), ("group_size", ctypes.c_int32)]
+
+
+class QsaTieredPool(ctypes.Structure):
+    _fields_ = [("ring_k", QsaTensor), ("ring_v", QsaTensor), ("ring_k_scale", QsaTensor),
+                ("ring_v_scale", QsaTensor), ("owner", QsaTensor), ("claim", QsaTensor),
+                ("cold_k", QsaTensor), ("cold_v", QsaTensor), ("cold_k_scale", QsaTensor),
+                ("cold_v_scale", QsaTensor)]
+
+
+TIERED_FIELDS = ("ring_k", "ring_v", "ring_k_scale", "ring_v_scale", "owner", "claim",
+                 "cold_k", "cold_v", "cold_k_scale", "cold_v_scale")
 
 
 _lib = None
@@ -60,6 +71,10 @@ def load_library():
     lib.qsa_decode.argtypes = [T, T, T, P(QsaKvScales), T, T, T, T, ctypes.c_void_p]
     lib.qsa_kv_store.restype = ctypes.c_int
     lib.qsa_kv_store.argtypes = [T, T, T, T, T, P(QsaKvScales), ctypes.c_void_p]
+    lib.qsa_decode_tiered.restype = ctypes.c_int
+    lib.qsa_decode_tiered.argtypes = [T, P(QsaTieredPool), T, T, T, T, ctypes.c_void_p]
+    lib.qsa_kv_store_tiered.restype = ctypes.c_int
+    lib.qsa_kv_store_tiered.argtypes = [T, T, T, P(QsaTieredPool), ctypes.c_void_p]
     lib.qsa_workspace_reserve.restype = ctypes.c_int
     lib.qsa_workspace_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.qsa_workspace_reset.restype = ctypes.c_int
@@ -183,6 +198,51 @@ def kv_store(k_new, v_new, loc, k_pool, v_pool, *, kv_format: str = "bf16", k_sc
                           ctypes.byref(vpd), ctypes.byref(scales) if scales is not None else None,
                           _stream_handle(stream))
     _check(st)
+
+
+def tiered_pool(*, ring_k, ring_v, ring_k_scale, ring_v_scale, owner, claim, cold_k, cold_v,
+                cold_k_scale, cold_v_scale) -> QsaTieredPool:
+    """qsa_tiered_pool for torch tensors: ring_k / ring_v int8 [R, Hkv, 256],
+    ring scales float16 [R, Hkv, 4], owner / claim int32 [R], cold_k /
+    cold_v uint8 [slots, Hkv, 128] (two int4 codes per byte), cold scales
+    float16 [slots, Hkv, 8]."""
+    tp = QsaTieredPool()
+    tp.ring_k, tp.ring_v = describe(ring_k), describe(ring_v)
+    tp.ring_k_scale, tp.ring_v_scale = describe(ring_k_scale), describe(ring_v_scale)
+    tp.owner, tp.claim = describe(owner), describe(claim)
+    tp.cold_k, tp.cold_v = describe(cold_k, "int4"), describe(cold_v, "int4")
+    tp.cold_k_scale, tp.cold_v_scale = describe(cold_k_scale), describe(cold_v_scale)
+    return tp
+
+
+def decode_tiered(q, pool: dict, sel, cu_seqlens, *, out=None, lse=None, stream=None):
+    """Packed QSA decode over a tiered pool (dict with the qsa_tiered_pool
+    fields as torch tensors).  One kernel launch; returns (out, lse)."""
+    import torch
+    lib = load_library()
+    bs, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((bs, hq, 256), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((bs, hq), dtype=torch.float32, device=q.device)
+    tp = tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
+    qd, od, ld = describe(q), describe(out), describe(lse)
+    sd, cd = describe(sel), describe(cu_seqlens)
+    _check(lib.qsa_decode_tiered(ctypes.byref(qd), ctypes.byref(tp), ctypes.byref(sd),
+                                 ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
+                                 _stream_handle(stream)))
+    return out, lse
+
+
+def kv_store_tiered(k_new, v_new, loc, pool: dict, *, stream=None):
+    """Write k_new / v_new [n, Hkv, 256] bf16 into a tiered pool: int4 into
+    slot loc[t], int8 into ring row loc[t] & (R-1) with its owner stamp
+    (three kernel launches on `stream`)."""
+    lib = load_library()
+    tp = tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
+    kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
+    _check(lib.qsa_kv_store_tiered(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld),
+                                   ctypes.byref(tp), _stream_handle(stream)))
 
 
 def workspace_reserve(max_bs: int, hq: int, hkv: int, stream=None):

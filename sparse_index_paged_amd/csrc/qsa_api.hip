@@ -314,6 +314,189 @@ bool addresses_fit_32(const PoolDesc &pd, const qsa_tensor *k_pool, const qsa_te
   return true;
 }
 
+// The query's dtype, rank, head dim and batch size (checked before the pools).
+qsa_status check_query(const char *fn, const qsa_tensor *q) {
+  qsa_status st;
+  if ((st = check_tensor(q, "q", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  if (q->shape[2] != QSA_HEAD_DIM)
+    return fail(QSA_ERR_CONTRACT, "%s: head dim must be 256, q.shape[2] = %lld", fn,
+                static_cast<long long>(q->shape[2]));
+  if (q->shape[0] < 1 || q->shape[0] > QSA_MAX_BS)
+    return fail(QSA_ERR_CONTRACT, "%s: bs must be in [1, 128], got %lld", fn,
+                static_cast<long long>(q->shape[0]));
+  return QSA_OK;
+}
+
+// Query, outputs, index lists, workspace and the pool-independent launch
+// parameters of one decode call (the pool fields are left to the caller).
+qsa_status prepare_decode(const char *fn, const qsa_tensor *q, int64_t hkv,
+                          const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                          qsa_tensor *out, qsa_tensor *lse, hipStream_t stream, qsa::Params *pp) {
+  qsa_status st;
+  if ((st = check_query(fn, q)) != QSA_OK) return st;
+  const int64_t bs = q->shape[0], hq = q->shape[1];
+  if (!((hq == 24 && hkv == 2) || (hq == 12 && hkv == 1)))
+    return fail(QSA_ERR_CONTRACT,
+                "%s: (Hq, Hkv) must be (24, 2) or (12, 1) (12:1 GQA), got (%lld, %lld)", fn,
+                static_cast<long long>(hq), static_cast<long long>(hkv));
+  if (!aligned16(q->data) || q->stride[0] % 8 || q->stride[1] % 8)
+    return fail(QSA_ERR_CONTRACT, "%s: q rows must start on 16-byte boundaries", fn);
+
+  if ((st = check_tensor(out, "out", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  if (out->shape[0] != bs || out->shape[1] != hq || out->shape[2] != QSA_HEAD_DIM)
+    return fail(QSA_ERR_CONTRACT, "%s: out must be [bs, Hq, 256] like q", fn);
+  if (!aligned16(out->data) || out->stride[0] % 8 || out->stride[1] % 8)
+    return fail(QSA_ERR_CONTRACT, "%s: out rows must start on 16-byte boundaries", fn);
+  // lse is written one float at a time: any strides
+  if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2, false, fn)) != QSA_OK) return st;
+  if (lse->shape[0] != bs || lse->shape[1] != hq)
+    return fail(QSA_ERR_CONTRACT, "%s: lse must be [bs, Hq]", fn);
+
+  if ((st = check_tensor(sel_indices, "sel_indices", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(cu_seqlens, "cu_seqlens", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if (cu_seqlens->shape[0] != bs + 1)
+    return fail(QSA_ERR_CONTRACT, "%s: cu_seqlens must have bs + 1 = %lld entries, got %lld", fn,
+                static_cast<long long>(bs + 1), static_cast<long long>(cu_seqlens->shape[0]));
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  const int splits = plan_splits(static_cast<int>(bs), static_cast<int>(hkv));
+  const int64_t need = bs * hkv * splits * static_cast<int64_t>(qsa::kPartFloats);
+  Workspace *ws = nullptr;
+  if ((st = ensure_workspace(dev, need, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK) return st;
+
+  qsa::Params &p = *pp;
+  p.q = static_cast<const __bf16 *>(q->data);
+  p.q_sb = q->stride[0];
+  p.q_sh = q->stride[1];
+  p.sel = static_cast<const int32_t *>(sel_indices->data);
+  p.n_sel = sel_indices->shape[0];
+  p.cu = static_cast<const int32_t *>(cu_seqlens->data);
+  p.out = static_cast<__bf16 *>(out->data);
+  p.o_sb = out->stride[0];
+  p.o_sh = out->stride[1];
+  p.lse = static_cast<float *>(lse->data);
+  p.l_sb = lse->stride[0];
+  p.l_sh = lse->stride[1];
+  p.bs = static_cast<int>(bs);
+  p.hkv = static_cast<int>(hkv);
+  p.nsplit = splits;
+  p.waves = static_cast<int>(g_waves.load());
+  p.min_split_keys = static_cast<int>(g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load());
+  p.part = ws->part;
+  p.ctr = ws->words;
+  p.err = ws->words + kCtrWords;
+  return QSA_OK;
+}
+
+// A tiered pool as validated for decode and store: the int8 ring (R rows,
+// 64-channel f16 scales, owner table, and for a store the claim table) and
+// the int4 pool (32-channel f16 scales).
+struct TieredDesc {
+  PoolDesc ring, cold;
+};
+
+qsa_status check_tiered(const char *fn, const qsa_tiered_pool *tp, bool want_claim, TieredDesc *d) {
+  if (tp == nullptr) return fail(QSA_ERR_ARG, "%s: pool is NULL", fn);
+  qsa_status st;
+  if (tp->ring_k.dtype != QSA_DTYPE_I8 || tp->ring_v.dtype != QSA_DTYPE_I8)
+    return fail(QSA_ERR_CONTRACT, "%s: ring_k / ring_v must be i8", fn);
+  if (tp->cold_k.dtype != QSA_DTYPE_U4X2 || tp->cold_v.dtype != QSA_DTYPE_U4X2)
+    return fail(QSA_ERR_CONTRACT, "%s: cold_k / cold_v must be u4x2", fn);
+  for (const qsa_tensor *t : {&tp->ring_k_scale, &tp->ring_v_scale, &tp->cold_k_scale, &tp->cold_v_scale})
+    if (t->dtype != QSA_DTYPE_F16)
+      return fail(QSA_ERR_CONTRACT, "%s: tiered pool scales must be f16, got %s", fn, dtype_name(t->dtype));
+  const qsa_kv_scales rs{tp->ring_k_scale, tp->ring_v_scale, 64};
+  const qsa_kv_scales cs{tp->cold_k_scale, tp->cold_v_scale, 32};
+  if ((st = check_pools(fn, &tp->ring_k, &tp->ring_v, &rs, &d->ring)) != QSA_OK) return st;
+  if ((st = check_pools(fn, &tp->cold_k, &tp->cold_v, &cs, &d->cold)) != QSA_OK) return st;
+  const int64_t r = d->ring.slots;
+  if ((r & (r - 1)) != 0)
+    return fail(QSA_ERR_CONTRACT, "%s: the ring must hold a power of two rows, got %lld", fn,
+                static_cast<long long>(r));
+  if (d->ring.hkv != d->cold.hkv)
+    return fail(QSA_ERR_CONTRACT, "%s: ring and int4 pool hold different KV head counts", fn);
+  if ((st = check_tensor(&tp->owner, "owner", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if (tp->owner.shape[0] != r)
+    return fail(QSA_ERR_CONTRACT, "%s: owner must have one entry per ring row (%lld)", fn,
+                static_cast<long long>(r));
+  if (want_claim) {
+    if ((st = check_tensor(&tp->claim, "claim", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+    if (tp->claim.shape[0] != r)
+      return fail(QSA_ERR_CONTRACT, "%s: claim must have one entry per ring row (%lld)", fn,
+                  static_cast<long long>(r));
+  }
+  return QSA_OK;
+}
+
+// New rows, slot ids and error word of one store call (pool fields are
+// left to set_store_pool).
+qsa_status prepare_store(const char *fn, const qsa_tensor *k_new, const qsa_tensor *v_new,
+                         const qsa_tensor *loc, int64_t hkv, hipStream_t stream,
+                         qsa::StoreParams *pp) {
+  qsa_status st;
+  if ((st = check_tensor(k_new, "k_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(v_new, "v_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  const int64_t n = k_new->shape[0];
+  for (const qsa_tensor *t : {k_new, v_new}) {
+    if (t->shape[0] != n || t->shape[1] != hkv || t->shape[2] != QSA_HEAD_DIM)
+      return fail(QSA_ERR_CONTRACT, "%s: k_new and v_new must be [n, Hkv, 256] = [%lld, %lld, 256]",
+                  fn, static_cast<long long>(n), static_cast<long long>(hkv));
+    if (!aligned16(t->data) || t->stride[0] % 8 || t->stride[1] % 8)
+      return fail(QSA_ERR_CONTRACT, "%s: k_new / v_new rows must start on 16-byte boundaries", fn);
+  }
+  if (loc == nullptr) return fail(QSA_ERR_ARG, "%s: loc is NULL", fn);
+  if (loc->dtype != QSA_DTYPE_I32 && loc->dtype != QSA_DTYPE_I64)
+    return fail(QSA_ERR_CONTRACT, "%s: loc must be i32 or i64, got %s", fn, dtype_name(loc->dtype));
+  if ((st = check_tensor(loc, "loc", loc->dtype, 1, true, fn)) != QSA_OK) return st;
+  if (loc->shape[0] != n)
+    return fail(QSA_ERR_CONTRACT, "%s: loc must have n = %lld entries, got %lld", fn,
+                static_cast<long long>(n), static_cast<long long>(loc->shape[0]));
+  if ((n * hkv + 3) / 4 > 0x7FFFFFFFLL)
+    return fail(QSA_ERR_CONTRACT, "%s: n = %lld rows is too many for one launch", fn,
+                static_cast<long long>(n));
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  Workspace *ws = nullptr;  // only its sticky error word is used
+  if ((st = ensure_workspace(dev, 0, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK) return st;
+
+  qsa::StoreParams &p = *pp;
+  p.k = static_cast<const __bf16 *>(k_new->data);
+  p.v = static_cast<const __bf16 *>(v_new->data);
+  p.k_st = k_new->stride[0];
+  p.k_sh = k_new->stride[1];
+  p.v_st = v_new->stride[0];
+  p.v_sh = v_new->stride[1];
+  p.loc = loc->data;
+  p.loc_i64 = loc->dtype == QSA_DTYPE_I64;
+  p.n = n;
+  p.hkv = static_cast<int>(hkv);
+  p.err = ws->words + kCtrWords;
+  return QSA_OK;
+}
+
+void set_store_pool(qsa::StoreParams *p, const PoolDesc &pd, const qsa_tensor *k_pool,
+                    const qsa_tensor *v_pool) {
+  p->kp = static_cast<uint8_t *>(k_pool->data);
+  p->vp = static_cast<uint8_t *>(v_pool->data);
+  p->kp_ss = k_pool->stride[0] * pd.eb;
+  p->kp_sh = k_pool->stride[1] * pd.eb;
+  p->vp_ss = v_pool->stride[0] * pd.eb;
+  p->vp_sh = v_pool->stride[1] * pd.eb;
+  p->ks = pd.ks;
+  p->vs = pd.vs;
+  p->ks_ss = pd.ks_ss;
+  p->ks_sh = pd.ks_sh;
+  p->vs_ss = pd.vs_ss;
+  p->vs_sh = pd.vs_sh;
+  p->scale_f16 = pd.scale_f16;
+  p->group = pd.group;
+  p->slots = pd.slots;
+}
+
 }  // namespace
 
 extern "C" {
@@ -365,62 +548,20 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
                       const qsa_kv_scales *kv_scales, const qsa_tensor *sel_indices,
                       const qsa_tensor *cu_seqlens, qsa_tensor *out, qsa_tensor *lse,
                       hipStream_t stream) {
+  static const char *fn = "qsa_decode";
   qsa_status st;
-  // -- query / outputs
-  if ((st = check_tensor(q, "q", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
-  const int64_t bs = q->shape[0], hq = q->shape[1];
-  if (q->shape[2] != QSA_HEAD_DIM)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: head dim must be 256, q.shape[2] = %lld",
-                static_cast<long long>(q->shape[2]));
-  if (bs < 1 || bs > QSA_MAX_BS)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: bs must be in [1, 128], got %lld",
-                static_cast<long long>(bs));
+  if ((st = check_query(fn, q)) != QSA_OK) return st;
   PoolDesc pd;
-  if ((st = check_pools("qsa_decode", k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
-  const int64_t slots = pd.slots, hkv = pd.hkv, eb = pd.eb;
-  if (!((hq == 24 && hkv == 2) || (hq == 12 && hkv == 1)))
-    return fail(QSA_ERR_CONTRACT,
-                "qsa_decode: (Hq, Hkv) must be (24, 2) or (12, 1) (12:1 GQA), got (%lld, %lld)",
-                static_cast<long long>(hq), static_cast<long long>(hkv));
-  if (!aligned16(q->data) || q->stride[0] % 8 || q->stride[1] % 8)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: q rows must start on 16-byte boundaries");
-
-  if ((st = check_tensor(out, "out", QSA_DTYPE_BF16, 3)) != QSA_OK) return st;
-  if (out->shape[0] != bs || out->shape[1] != hq || out->shape[2] != QSA_HEAD_DIM)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: out must be [bs, Hq, 256] like q");
-  if (!aligned16(out->data) || out->stride[0] % 8 || out->stride[1] % 8)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: out rows must start on 16-byte boundaries");
-  // lse is written one float at a time: any strides
-  if ((st = check_tensor(lse, "lse", QSA_DTYPE_F32, 2, false)) != QSA_OK) return st;
-  if (lse->shape[0] != bs || lse->shape[1] != hq)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: lse must be [bs, Hq]");
-
-  // -- index lists
-  if ((st = check_tensor(sel_indices, "sel_indices", QSA_DTYPE_I32, 1)) != QSA_OK) return st;
-  if ((st = check_tensor(cu_seqlens, "cu_seqlens", QSA_DTYPE_I32, 1)) != QSA_OK) return st;
-  if (cu_seqlens->shape[0] != bs + 1)
-    return fail(QSA_ERR_CONTRACT, "qsa_decode: cu_seqlens must have bs + 1 = %lld entries, got %lld",
-                static_cast<long long>(bs + 1), static_cast<long long>(cu_seqlens->shape[0]));
-
-  // -- device, workspace, launch
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "qsa_decode: no HIP device");
-  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "qsa_decode: device id out of range");
-  const int splits = plan_splits(static_cast<int>(bs), static_cast<int>(hkv));
-  const int64_t need = bs * hkv * splits * static_cast<int64_t>(qsa::kPartFloats);
-  Workspace *ws = nullptr;
-  if ((st = ensure_workspace(dev, need, stream, !stream_capturing(stream), &ws)) != QSA_OK) return st;
-
+  if ((st = check_pools(fn, k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
   qsa::Params p{};
-  p.q = static_cast<const __bf16 *>(q->data);
-  p.q_sb = q->stride[0];
-  p.q_sh = q->stride[1];
+  if ((st = prepare_decode(fn, q, pd.hkv, sel_indices, cu_seqlens, out, lse, stream, &p)) != QSA_OK)
+    return st;
   p.k = static_cast<const uint8_t *>(k_pool->data);
   p.v = static_cast<const uint8_t *>(v_pool->data);
-  p.k_ss = k_pool->stride[0] * eb;
-  p.k_sh = k_pool->stride[1] * eb;
-  p.v_ss = v_pool->stride[0] * eb;
-  p.v_sh = v_pool->stride[1] * eb;
+  p.k_ss = k_pool->stride[0] * pd.eb;
+  p.k_sh = k_pool->stride[1] * pd.eb;
+  p.v_ss = v_pool->stride[0] * pd.eb;
+  p.v_sh = v_pool->stride[1] * pd.eb;
   p.ks = pd.ks;
   p.vs = pd.vs;
   p.ks_ss = pd.ks_ss;
@@ -429,27 +570,54 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.vs_sh = pd.vs_sh;
   p.scale_f16 = pd.scale_f16;
   p.a32 = addresses_fit_32(pd, k_pool, v_pool) ? 1 : 0;
-  p.sel = static_cast<const int32_t *>(sel_indices->data);
-  p.n_sel = sel_indices->shape[0];
-  p.cu = static_cast<const int32_t *>(cu_seqlens->data);
-  p.out = static_cast<__bf16 *>(out->data);
-  p.o_sb = out->stride[0];
-  p.o_sh = out->stride[1];
-  p.lse = static_cast<float *>(lse->data);
-  p.l_sb = lse->stride[0];
-  p.l_sh = lse->stride[1];
-  p.slots = slots;
-  p.bs = static_cast<int>(bs);
-  p.hkv = static_cast<int>(hkv);
-  p.nsplit = splits;
-  p.waves = static_cast<int>(g_waves.load());
-  p.min_split_keys = static_cast<int>(g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load());
-  p.part = ws->part;
-  p.ctr = ws->words;
-  p.err = ws->words + kCtrWords;
+  p.slots = pd.slots;
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
-  if (e != hipSuccess)
-    return fail(QSA_ERR_HIP, "qsa_decode: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
+                             const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                             qsa_tensor *out, qsa_tensor *lse, hipStream_t stream) {
+  static const char *fn = "qsa_decode_tiered";
+  qsa_status st;
+  if ((st = check_query(fn, q)) != QSA_OK) return st;
+  TieredDesc td;
+  if ((st = check_tiered(fn, pool, false, &td)) != QSA_OK) return st;
+  qsa::Params p{};
+  if ((st = prepare_decode(fn, q, td.cold.hkv, sel_indices, cu_seqlens, out, lse, stream, &p)) != QSA_OK)
+    return st;
+  p.k = static_cast<const uint8_t *>(pool->cold_k.data);
+  p.v = static_cast<const uint8_t *>(pool->cold_v.data);
+  p.k_ss = pool->cold_k.stride[0];
+  p.k_sh = pool->cold_k.stride[1];
+  p.v_ss = pool->cold_v.stride[0];
+  p.v_sh = pool->cold_v.stride[1];
+  p.ks = td.cold.ks;
+  p.vs = td.cold.vs;
+  p.ks_ss = td.cold.ks_ss;
+  p.ks_sh = td.cold.ks_sh;
+  p.vs_ss = td.cold.vs_ss;
+  p.vs_sh = td.cold.vs_sh;
+  p.scale_f16 = 1;
+  p.a32 = 0;
+  p.slots = td.cold.slots;
+  p.ring.k = static_cast<const uint8_t *>(pool->ring_k.data);
+  p.ring.v = static_cast<const uint8_t *>(pool->ring_v.data);
+  p.ring.k_ss = pool->ring_k.stride[0];
+  p.ring.k_sh = pool->ring_k.stride[1];
+  p.ring.v_ss = pool->ring_v.stride[0];
+  p.ring.v_sh = pool->ring_v.stride[1];
+  p.ring.ks = td.ring.ks;
+  p.ring.vs = td.ring.vs;
+  p.ring.ks_ss = td.ring.ks_ss;
+  p.ring.ks_sh = td.ring.ks_sh;
+  p.ring.vs_ss = td.ring.vs_ss;
+  p.ring.vs_sh = td.ring.vs_sh;
+  p.ring.owner = static_cast<const int32_t *>(pool->owner.data);
+  p.ring.mask = static_cast<uint32_t>(td.ring.slots - 1);
+  const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 
@@ -460,61 +628,38 @@ qsa_status qsa_kv_store(const qsa_tensor *k_new, const qsa_tensor *v_new, const 
   qsa_status st;
   PoolDesc pd;
   if ((st = check_pools(fn, k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
-  if ((st = check_tensor(k_new, "k_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
-  if ((st = check_tensor(v_new, "v_new", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
-  const int64_t n = k_new->shape[0];
-  for (const qsa_tensor *t : {k_new, v_new}) {
-    if (t->shape[0] != n || t->shape[1] != pd.hkv || t->shape[2] != QSA_HEAD_DIM)
-      return fail(QSA_ERR_CONTRACT, "%s: k_new and v_new must be [n, Hkv, 256] = [%lld, %lld, 256]",
-                  fn, static_cast<long long>(n), static_cast<long long>(pd.hkv));
-    if (!aligned16(t->data) || t->stride[0] % 8 || t->stride[1] % 8)
-      return fail(QSA_ERR_CONTRACT, "%s: k_new / v_new rows must start on 16-byte boundaries", fn);
-  }
-  if (loc == nullptr) return fail(QSA_ERR_ARG, "%s: loc is NULL", fn);
-  if (loc->dtype != QSA_DTYPE_I32 && loc->dtype != QSA_DTYPE_I64)
-    return fail(QSA_ERR_CONTRACT, "%s: loc must be i32 or i64, got %s", fn, dtype_name(loc->dtype));
-  if ((st = check_tensor(loc, "loc", loc->dtype, 1, true, fn)) != QSA_OK) return st;
-  if (loc->shape[0] != n)
-    return fail(QSA_ERR_CONTRACT, "%s: loc must have n = %lld entries, got %lld", fn,
-                static_cast<long long>(n), static_cast<long long>(loc->shape[0]));
-  if ((n * pd.hkv + 3) / 4 > 0x7FFFFFFFLL)
-    return fail(QSA_ERR_CONTRACT, "%s: n = %lld rows is too many for one launch", fn,
-                static_cast<long long>(n));
-
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
-  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
-  Workspace *ws = nullptr;  // only its sticky error word is used
-  if ((st = ensure_workspace(dev, 0, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK) return st;
-
   qsa::StoreParams p{};
-  p.k = static_cast<const __bf16 *>(k_new->data);
-  p.v = static_cast<const __bf16 *>(v_new->data);
-  p.k_st = k_new->stride[0];
-  p.k_sh = k_new->stride[1];
-  p.v_st = v_new->stride[0];
-  p.v_sh = v_new->stride[1];
-  p.loc = loc->data;
-  p.loc_i64 = loc->dtype == QSA_DTYPE_I64;
-  p.n = n;
-  p.kp = static_cast<uint8_t *>(k_pool->data);
-  p.vp = static_cast<uint8_t *>(v_pool->data);
-  p.kp_ss = k_pool->stride[0] * pd.eb;
-  p.kp_sh = k_pool->stride[1] * pd.eb;
-  p.vp_ss = v_pool->stride[0] * pd.eb;
-  p.vp_sh = v_pool->stride[1] * pd.eb;
-  p.ks = pd.ks;
-  p.vs = pd.vs;
-  p.ks_ss = pd.ks_ss;
-  p.ks_sh = pd.ks_sh;
-  p.vs_ss = pd.vs_ss;
-  p.vs_sh = pd.vs_sh;
-  p.scale_f16 = pd.scale_f16;
-  p.group = pd.group;
-  p.slots = pd.slots;
-  p.hkv = static_cast<int>(pd.hkv);
-  p.err = ws->words + kCtrWords;
+  if ((st = prepare_store(fn, k_new, v_new, loc, pd.hkv, stream, &p)) != QSA_OK) return st;
+  set_store_pool(&p, pd, k_pool, v_pool);
   const hipError_t e = qsa::launch_store(p, pd.fmt, stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
+                               const qsa_tensor *loc, qsa_tiered_pool *pool, hipStream_t stream) {
+  static const char *fn = "qsa_kv_store_tiered";
+  qsa_status st;
+  TieredDesc td;
+  if ((st = check_tiered(fn, pool, true, &td)) != QSA_OK) return st;
+  qsa::StoreParams p{};
+  if ((st = prepare_store(fn, k_new, v_new, loc, td.cold.hkv, stream, &p)) != QSA_OK) return st;
+  if (p.n > 0x7FFFFFFELL)
+    return fail(QSA_ERR_CONTRACT, "%s: n = %lld tokens cannot be ranked in the int32 claim table",
+                fn, static_cast<long long>(p.n));
+  // 1. every token into the int4 pool
+  set_store_pool(&p, td.cold, &pool->cold_k, &pool->cold_v);
+  hipError_t e = qsa::launch_store(p, qsa::kFmtINT4, stream);
+  // 2. the last token of the call per ring row claims it
+  qsa::StoreParams r = p;
+  r.claim = static_cast<int32_t *>(pool->claim.data);
+  r.owner = static_cast<int32_t *>(pool->owner.data);
+  r.ring_mask = static_cast<uint32_t>(td.ring.slots - 1);
+  if (e == hipSuccess) e = qsa::launch_claim(r, stream);
+  // 3. the claimed rows into the ring, with their owner stamps
+  set_store_pool(&r, td.ring, &pool->ring_k, &pool->ring_v);
+  r.slots = td.cold.slots;  // slot ids are checked against the full pool
+  if (e == hipSuccess) e = qsa::launch_store(r, qsa::kFmtINT8, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }

@@ -38,6 +38,14 @@
 //     converted exactly to bf16; their fp32 scales are applied outside the
 //     MFMA (K scales on the QK partial of each channel group, V scales folded
 //     into P).
+//   * Tiered pools (same page, tiered pool bullet): entry j reads ring row
+//     r = sel_j & (R-1) (int8, 64-channel scales) when owner[r] == sel_j,
+//     else its int4 row (32-channel scales).  The owner ids join the
+//     pipeline one stage before the rows: slot ids of tile t+3D, owner ids
+//     of tile t+2D, rows of tile t+D.  Every lane dequantizes 16 channels of
+//     either tier into the same LDS place (an int4 lane loads the aligned
+//     16 bytes holding its 8 bytes), and the scales are staged per 32
+//     channels (a ring scale twice).
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
 //     one L2.
@@ -67,6 +75,9 @@ template <> struct Fmt<kFmtBF16> { using Part = uint4;    static constexpr int k
 template <> struct Fmt<kFmtFP8>  { using Part = uint2;    static constexpr int kRowBytes = 256; };
 template <> struct Fmt<kFmtINT8> { using Part = uint2;    static constexpr int kRowBytes = 256; };
 template <> struct Fmt<kFmtINT4> { using Part = uint32_t; static constexpr int kRowBytes = 128; };
+// tiered: the int8 ring row's geometry; an int4 row's 16 channels of a
+// lane are the half of a 16-byte load selected in stage()
+template <> struct Fmt<kFmtTIERED> { using Part = uint2; static constexpr int kRowBytes = 256; };
 template <int FMT> struct Geo {
   static constexpr int kLPR = Fmt<FMT>::kRowBytes / 16;  // lanes per row
   static constexpr int kRPI = 64 / kLPR;                 // rows per instruction
@@ -181,6 +192,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   using GEO = Geo<FMT>;
   using LDS = Lds<W>;
   using Scale = typename std::conditional<SF16, _Float16, float>::type;
+  constexpr bool TIER = FMT == kFmtTIERED;
+  static_assert(!TIER || (G == 32 && SF16 && !A32), "tiered pools: f16 scales staged per 32 channels");
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
@@ -261,6 +274,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   const uint32_t sgrpb = static_cast<uint32_t>(sgrp * sizeof(Scale));
   const int32_t *selw = p.sel + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
+  // tiered: ring rows of KV head g; a cold lane reads the 16 bytes at
+  // 16 * (lchunk / 2) of the int4 row and a hot lane 16 * lchunk of the ring
+  // row; scale group sgrp of a cold row is group sgrp / 2 of a ring row
+  const uint8_t *rkbase = TIER ? p.ring.k + g * p.ring.k_sh + 16 * lchunk : nullptr;
+  const uint8_t *rvbase = TIER ? p.ring.v + g * p.ring.v_sh + 16 * lchunk : nullptr;
+  const uint8_t *ckbase = TIER ? kpool + 16 * (lchunk >> 1) : nullptr;
+  const uint8_t *cvbase = TIER ? vpool + 16 * (lchunk >> 1) : nullptr;
+  const uint8_t *rksbase = TIER ? p.ring.ks + g * p.ring.ks_sh + (sgrp >> 1) * 2 : nullptr;
+  const uint8_t *rvsbase = TIER ? p.ring.vs + g * p.ring.vs_sh + (sgrp >> 1) * 2 : nullptr;
+  const uint32_t rmask = TIER ? p.ring.mask : 0u;
 
   // per-lane online-softmax state for head r16 (replicated over lane groups)
   float m_run = -INFINITY;
@@ -297,6 +320,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // t = u (mod D) and refilled with tile t + D.
   uint4 kraw[D][NI], vraw[D][NI];
   Scale ksr[D][NI], vsr[D][NI];  // converted to fp32 when staged
+  bool hot[D][NI];               // tiered: the row came from the ring
 
   // Every load of the pipeline is unconditional and its value is used as
   // loaded, so the compiler's load counting never has to assume a skipped
@@ -317,6 +341,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     const bool bad = static_cast<uint32_t>(s) >= slots;
     bad_slot = bad_slot || (bad && nkeys > 0);
     return bad ? 0u : static_cast<uint32_t>(s);
+  };
+  // tiered: owner ids of the ring rows the slot ids map to (always in range)
+  auto fetch_owners = [&](const int32_t (&sl)[NI], int32_t (&ow)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) ow[i] = p.ring.owner[static_cast<uint32_t>(sl[i]) & rmask];
+  };
+  auto issue_tiered = [&](int u, const int32_t (&sl)[NI], const int32_t (&ow)[NI]) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t cs = checked(sl[i]);
+      const uint32_t r = static_cast<uint32_t>(sl[i]) & rmask;
+      const bool h = ow[i] == sl[i];
+      hot[u][i] = h;
+      const int64_t ro = static_cast<int64_t>(r), co = static_cast<int64_t>(cs);
+      kraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rkbase + ro * p.ring.k_ss : ckbase + co * p.k_ss);
+      vraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rvbase + ro * p.ring.v_ss : cvbase + co * p.v_ss);
+      ksr[u][i] = *reinterpret_cast<const Scale *>(h ? rksbase + ro * p.ring.ks_ss : ksbase + co * p.ks_ss);
+      vsr[u][i] = *reinterpret_cast<const Scale *>(h ? rvsbase + ro * p.ring.vs_ss : vsbase + co * p.vs_ss);
+    }
   };
   auto issue = [&](int u, const int32_t (&sl)[NI]) {
     uint32_t slot[NI];
@@ -347,12 +390,21 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // reads its B operand.  snext[u] holds the slot ids of the tile that
   // register set u loads next.
   int32_t snext[D][NI];
+  int32_t onext[D][NI], s2[D][NI];  // tiered: owner ids of snext; slot ids one tile set further
   {
-    int32_t s0[D][NI];
+    int32_t s0[D][NI], o0[D][NI];
 #pragma unroll
     for (int u = 0; u < D; ++u) fetch_slots(u, s0[u]);
 #pragma unroll
     for (int u = 0; u < D; ++u) fetch_slots(D + u, snext[u]);
+    if constexpr (TIER) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) fetch_slots(2 * D + u, s2[u]);
+#pragma unroll
+      for (int u = 0; u < D; ++u) fetch_owners(s0[u], o0[u]);
+#pragma unroll
+      for (int u = 0; u < D; ++u) fetch_owners(snext[u], onext[u]);
+    }
     constexpr int CPT = 512 / kThr;  // 16-byte Q chunks per thread
     uint4 qv[CPT];
 #pragma unroll
@@ -364,7 +416,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
         qv[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + (g * kGqa + h) * p.q_sh)[c];
     }
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(u, s0[u]);
+    for (int u = 0; u < D; ++u) {
+      if constexpr (TIER)
+        issue_tiered(u, s0[u], o0[u]);
+      else
+        issue(u, s0[u]);
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int idx = tid * CPT + i;
@@ -387,12 +444,32 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int off = (ldrow + i) * kLdsRow + lchunk * 16;
+      if constexpr (TIER) {
+        uint4 k0, k1, v0, v1;
+        if (hot[u][i]) {
+          k0 = to_bf16x8<kFmtINT8>(make_uint2(kraw[u][i].x, kraw[u][i].y));
+          k1 = to_bf16x8<kFmtINT8>(make_uint2(kraw[u][i].z, kraw[u][i].w));
+          v0 = to_bf16x8<kFmtINT8>(make_uint2(vraw[u][i].x, vraw[u][i].y));
+          v1 = to_bf16x8<kFmtINT8>(make_uint2(vraw[u][i].z, vraw[u][i].w));
+        } else {
+          const bool odd = lchunk & 1;
+          k0 = to_bf16x8<kFmtINT4>(odd ? kraw[u][i].z : kraw[u][i].x);
+          k1 = to_bf16x8<kFmtINT4>(odd ? kraw[u][i].w : kraw[u][i].y);
+          v0 = to_bf16x8<kFmtINT4>(odd ? vraw[u][i].z : vraw[u][i].x);
+          v1 = to_bf16x8<kFmtINT4>(odd ? vraw[u][i].w : vraw[u][i].y);
+        }
+        *reinterpret_cast<uint4 *>(kt + off) = k0;
+        *reinterpret_cast<uint4 *>(kt + off + kPartB) = k1;
+        *reinterpret_cast<uint4 *>(vt + off) = v0;
+        *reinterpret_cast<uint4 *>(vt + off + kPartB) = v1;
+      } else {
 #pragma unroll
-      for (int c = 0; c < P; ++c) {
-        const Part kp = reinterpret_cast<const Part *>(&kraw[u][i])[c];
-        const Part vp = reinterpret_cast<const Part *>(&vraw[u][i])[c];
-        *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = to_bf16x8<FMT>(kp);
-        *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = to_bf16x8<FMT>(vp);
+        for (int c = 0; c < P; ++c) {
+          const Part kp = reinterpret_cast<const Part *>(&kraw[u][i])[c];
+          const Part vp = reinterpret_cast<const Part *>(&vraw[u][i])[c];
+          *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = to_bf16x8<FMT>(kp);
+          *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = to_bf16x8<FMT>(vp);
+        }
       }
     }
     if constexpr (NG > 0) {
@@ -523,8 +600,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     for (int u = 0; u < D; ++u) {
       const int t = t0 + u;
       stage(u);
-      issue(u, snext[u]);
-      fetch_slots(t + 2 * D, snext[u]);
+      if constexpr (TIER) {
+        issue_tiered(u, snext[u], onext[u]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) snext[u][i] = s2[u][i];
+        fetch_owners(snext[u], onext[u]);
+        fetch_slots(t + 3 * D, s2[u]);
+      } else {
+        issue(u, snext[u]);
+        fetch_slots(t + 2 * D, snext[u]);
+      }
       if (t < ntile) process(t);
     }
   }
@@ -826,6 +911,11 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
       if (group == 64) return launch_one<kFmtINT4, 64>(p, stream);
       if (group == 32) return launch_one<kFmtINT4, 32>(p, stream);
       break;
+    case kFmtTIERED: {
+      const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
+      launch_waves<kFmtTIERED, 32, true, false>(p, dim3(npairs8 * p.nsplit), stream);
+      return hipGetLastError();
+    }
     default: break;
   }
   return hipErrorInvalidValue;

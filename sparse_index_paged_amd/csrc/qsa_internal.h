@@ -17,7 +17,10 @@ constexpr int kTile = 16;         // list entries per wave iteration
 // unnormalised accumulator [12][256].
 constexpr int kPartFloats = 32 + kGqa * kHeadDim;
 
-enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3 };
+// kFmtTIERED: an int8 ring (64-channel f16 scales) of 2^k rows with an
+// owner table over an int4 pool (32-channel f16 scales); the int4 pool sits
+// in the plain pool fields, the ring in Params::ring.
+enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3, kFmtTIERED = 4 };
 
 // Device-side error bits (sticky, OR-ed into Params::err).
 constexpr uint32_t kErrRowRange = 1u;   // cu_seqlens out of range / row > 2055
@@ -44,6 +47,14 @@ struct Params {
   float *lse;
   int64_t l_sb, l_sh;
   int64_t slots;
+  struct Ring {             // tiered pools only
+    const uint8_t *k, *v;   // int8 codes [R, hkv, 256]
+    int64_t k_ss, k_sh, v_ss, v_sh;      // byte strides
+    const uint8_t *ks, *vs; // f16 scales [R, hkv, 4]
+    int64_t ks_ss, ks_sh, vs_ss, vs_sh;  // byte strides
+    const int32_t *owner;   // [R]
+    uint32_t mask;          // R - 1
+  } ring;
   int bs, hkv;
   int nsplit;               // splits per (row, kv head) in the grid
   int waves;                // waves per workgroup: 4 or 8
@@ -72,6 +83,13 @@ struct StoreParams {
   int64_t slots;
   int hkv;
   uint32_t *err;            // sticky error word
+  // ring write of a tiered pool (null otherwise): token t goes to ring row
+  // loc[t] & ring_mask only if claim[row] == t + 1 (the last token of the
+  // call naming that row), which then stamps owner[row] = loc[t] and
+  // clears claim[row]
+  int32_t *claim;
+  int32_t *owner;
+  uint32_t ring_mask;
 };
 
 // Launch the decode kernel for one call (grid = 8 * ceil(npairs/8) * nsplit).
@@ -79,6 +97,10 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
 
 // Launch the quantize + scatter kernel (one wave per (token, kv head)).
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream);
+
+// Ring claims of a tiered write: claim[loc[t] & ring_mask] = max(.., t + 1)
+// for every in-range slot id (p.claim, p.loc, p.n, p.slots).
+hipError_t launch_claim(const StoreParams &p, hipStream_t stream);
 
 // Zero n words at dst with a small kernel (no memset node in captured graphs).
 hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream);

@@ -15,6 +15,13 @@
 // the same section); codes are computed from the scale as stored.  bf16
 // pools take the rows unchanged.
 //
+// Tiered pools (same section, tiered pool bullet) are written by three
+// launches: the int4 store into the full pool, a claim pass that records
+// for every ring row the last token of the call that maps to it, and the
+// int8 store into the ring, where only that token writes the row, stamps
+// the owner table and clears its claim (so the claim table is zero again
+// when the call ends).
+//
 // Mapping: a wave handles 4 consecutive (token, kv head) rows; lanes 0..31
 // work on the K rows and lanes 32..63 on the V rows, 8 channels (one
 // 16-byte load) per lane, and all loads of the 4 rows are issued before the
@@ -84,9 +91,12 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
   const bool is_v = lane >= 32;
   const int l = lane & 31;
 
-  // ---- all loads of the wave's rows first
+  // ---- all loads of the wave's rows first (with a ring, also the claims:
+  // every claim this wave tests is read before it clears any)
   uint4 raw[kRowsPerWave];
   int64_t slot[kRowsPerWave];
+  int32_t claim[kRowsPerWave];
+  const bool ring = p.claim != nullptr;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int64_t row = row0 + i;
@@ -97,6 +107,7 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
                           : static_cast<int64_t>(static_cast<const int32_t *>(p.loc)[t]);
       const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
       raw[i] = reinterpret_cast<const uint4 *>(src)[l];
+      if (ring) claim[i] = p.claim[static_cast<uint32_t>(slot[i]) & p.ring_mask];
     }
   }
 
@@ -106,10 +117,20 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
     if (row >= nrows) break;
     const int64_t t = (p.hkv == 2) ? (row >> 1) : row;
     const int h = static_cast<int>(row - t * p.hkv);
-    const int64_t s = slot[i];
+    int64_t s = slot[i];
     if (s < 0 || s >= p.slots) {
       if (lane == 0) atomicOr(p.err, kErrStoreSlot);
       continue;
+    }
+    if (ring) {
+      // only the last token of the call that maps to this ring row writes it
+      if (claim[i] != static_cast<int32_t>(t + 1)) continue;
+      const int64_t r = static_cast<int64_t>(static_cast<uint32_t>(s) & p.ring_mask);
+      if (h == p.hkv - 1 && lane == 0) {
+        p.owner[r] = static_cast<int32_t>(s);
+        p.claim[r] = 0;
+      }
+      s = r;
     }
     uint8_t *dst = is_v ? p.vp + s * p.vp_ss + h * p.vp_sh : p.kp + s * p.kp_ss + h * p.kp_sh;
     if constexpr (FMT == kFmtBF16) {
@@ -163,7 +184,23 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
   }
 }
 
+__global__ void __launch_bounds__(256) qsa_claim_kernel(const StoreParams p) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= p.n) return;
+  const int64_t s = p.loc_i64 ? static_cast<const int64_t *>(p.loc)[t]
+                              : static_cast<int64_t>(static_cast<const int32_t *>(p.loc)[t]);
+  if (s < 0 || s >= p.slots) return;
+  atomicMax(p.claim + (static_cast<uint32_t>(s) & p.ring_mask), static_cast<int32_t>(t + 1));
+}
+
 }  // namespace
+
+hipError_t launch_claim(const StoreParams &p, hipStream_t stream) {
+  if (p.n <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((p.n + 255) / 256));
+  hipLaunchKernelGGL(qsa_claim_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream) {
   const int64_t rows = p.n * p.hkv;

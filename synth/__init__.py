@@ -198,3 +198,29 @@ def sweep_bank(seed: int, bs: int, kind: str, slots: int, banks: int = 8,
         p[: s.shape[0]] = s
         padded.append((p, c))
     return padded
+
+
+def tiered_lists(rng: np.random.Generator, lengths, slots: int, recent: np.ndarray,
+                 hot_frac: float, dup_prob: float = 0.0) -> tuple[np.ndarray, np.ndarray]:
+    """Packed lists for a tiered pool: each entry is, with probability
+    ``hot_frac``, a uniform draw from ``recent`` (the most recently written
+    slot ids) and otherwise a uniform draw from all slots; duplicate runs as
+    in draw_indices."""
+    lists = []
+    recent = np.asarray(recent, dtype=np.int64)
+    for n in lengths:
+        idx = draw_indices(rng, int(n), slots, dup_prob).astype(np.int64)
+        pick = rng.random(int(n)) < hot_frac
+        idx[pick] = recent[rng.integers(0, len(recent), size=int(pick.sum()))]
+        lists.append(idx.astype(np.int32))
+    return pack(lists)
+
+
+def write_batches(rng: np.random.Generator, order: np.ndarray, batches: int) -> list[np.ndarray]:
+    """Split a write order of slot ids into ``batches`` consecutive calls of
+    random sizes."""
+    n = len(order)
+    if batches <= 1 or n < 2:
+        return [np.asarray(order)]
+    cuts = np.sort(rng.choice(np.arange(1, n), size=min(batches - 1, n - 1), replace=False))
+    return np.split(np.asarray(order), cuts)

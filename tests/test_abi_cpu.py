@@ -49,7 +49,7 @@ def test_header_compiles_as_c():
 
 
 def test_abi_version():
-    assert qsa.abi_version() == B.ABI_VERSION == 2
+    assert qsa.abi_version() == B.ABI_VERSION == 3
 
 
 def test_plan_and_options():
@@ -207,3 +207,82 @@ def test_store_contract_rejections(kwargs, match):
     st, msg = _store(**kwargs)
     assert st == 1, (st, msg)
     assert re.search(match, msg), msg
+
+
+# ---- tiered pool (int8 ring + int4 pool) ----
+
+def _tiered(r=64, slots=256, hkv=2, ring_dtype=B.I8, cold_dtype=B.U4X2, scale_dtype=B.F16,
+            ring_scale_groups=4, cold_scale_groups=8, owner_len=None, claim_len=None,
+            claim_dtype=B.I32, ring_data=FAKE, cold_hkv=None):
+    ch = cold_hkv or hkv
+    return B.QsaTieredPool(
+        _t((r, hkv, 256), ring_dtype, data=ring_data), _t((r, hkv, 256), ring_dtype),
+        _t((r, hkv, ring_scale_groups), scale_dtype), _t((r, hkv, ring_scale_groups), scale_dtype),
+        _t((owner_len or r,), B.I32), _t((claim_len or r,), claim_dtype),
+        _t((slots, ch, 128), cold_dtype), _t((slots, ch, 128), cold_dtype),
+        _t((slots, ch, cold_scale_groups), scale_dtype),
+        _t((slots, ch, cold_scale_groups), scale_dtype))
+
+
+def _decode_tiered(pool, bs=4, hq=24):
+    lib = qsa.load_library()
+    q = _t((bs, hq, 256), B.BF16)
+    sel = _t((100,), B.I32)
+    cu = _t((bs + 1,), B.I32)
+    out = _t((bs, hq, 256), B.BF16)
+    lse = _t((bs, hq), B.F32)
+    st = lib.qsa_decode_tiered(ctypes.byref(q), ctypes.byref(pool), ctypes.byref(sel),
+                               ctypes.byref(cu), ctypes.byref(out), ctypes.byref(lse), None)
+    return st, lib.qsa_last_error().decode()
+
+
+def _store_tiered(pool, n=8, hkv=2):
+    lib = qsa.load_library()
+    k_new = _t((n, hkv, 256), B.BF16)
+    v_new = _t((n, hkv, 256), B.BF16)
+    loc = _t((n,), B.I32)
+    st = lib.qsa_kv_store_tiered(ctypes.byref(k_new), ctypes.byref(v_new), ctypes.byref(loc),
+                                 ctypes.byref(pool), None)
+    return st, lib.qsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,match", [
+    (dict(r=48), "power of two rows"),
+    (dict(ring_dtype=B.FP8_E4M3FN), "ring_k / ring_v must be i8"),
+    (dict(cold_dtype=B.I8), "cold_k / cold_v must be u4x2"),
+    (dict(scale_dtype=B.F32), "tiered pool scales must be f16"),
+    (dict(ring_scale_groups=8), r"scales must be \[slots, Hkv, 256/group\]"),
+    (dict(cold_scale_groups=4), r"scales must be \[slots, Hkv, 256/group\]"),
+    (dict(owner_len=32), "owner must have one entry per ring row"),
+    (dict(ring_data=FAKE + 8), "16-byte boundaries"),
+    (dict(hkv=2, cold_hkv=1), "different KV head counts"),
+])
+def test_tiered_contract_rejections(kwargs, match):
+    st, msg = _decode_tiered(_tiered(**kwargs))
+    assert st == 1, (st, msg)
+    assert re.search(match, msg), msg
+    assert msg.startswith("qsa_decode_tiered")
+
+
+@pytest.mark.parametrize("kwargs,match", [
+    (dict(claim_len=32), "claim must have one entry per ring row"),
+    (dict(claim_dtype=B.I64), "claim must be i32"),
+    (dict(r=12), "power of two rows"),
+])
+def test_tiered_store_contract_rejections(kwargs, match):
+    st, msg = _store_tiered(_tiered(**kwargs))
+    assert st == 1, (st, msg)
+    assert re.search(match, msg), msg
+    assert msg.startswith("qsa_kv_store_tiered")
+
+
+def test_tiered_query_and_store_shape_rejections():
+    st, msg = _decode_tiered(_tiered(hkv=1), hq=24)
+    assert st == 1 and re.search(r"\(Hq, Hkv\)", msg), msg
+    st, msg = _store_tiered(_tiered(hkv=2), hkv=1)
+    assert st == 1 and "k_new and v_new must be [n, Hkv, 256]" in msg, msg
+    lib = qsa.load_library()
+    assert lib.qsa_decode_tiered(None, None, None, None, None, None, None) == 2
+    assert "q is NULL" in lib.qsa_last_error().decode()
+    assert lib.qsa_kv_store_tiered(None, None, None, None, None) == 2
+    assert "pool is NULL" in lib.qsa_last_error().decode()

@@ -20,22 +20,13 @@ import torch
 
 import oracle
 import synth
-from oracle import quant
+from oracle import layout, quant
 
 HKV = 2
 
 
 def empty_tiers(ring_rows: int, slots: int, hkv: int = HKV):
-    ring = dict(k=np.zeros((ring_rows, hkv, 256), np.int8),
-                v=np.zeros((ring_rows, hkv, 256), np.int8),
-                k_scale=np.zeros((ring_rows, hkv, 4), np.float32),
-                v_scale=np.zeros((ring_rows, hkv, 4), np.float32),
-                owner=np.full(ring_rows, -1, np.int32))
-    cold = dict(k=np.full((slots, hkv, 128), 0x88, np.uint8),
-                v=np.full((slots, hkv, 128), 0x88, np.uint8),
-                k_scale=np.zeros((slots, hkv, 8), np.float32),
-                v_scale=np.zeros((slots, hkv, 8), np.float32))
-    return ring, cold
+    return layout.empty_tiered(ring_rows, slots, hkv)
 
 
 def tiered_decode(q, ring, cold, sel, cu, **kw):
