@@ -13,8 +13,12 @@ gathered-KV bytes = sum_b L_b * Hkv * 2 (K and V) * 512 B.
 
 Other lines (not the default run): ``--kv-format fp8|int8|int4`` decodes
 from quantized pools (written on the device by qsa_kv_store from the same
-bf16 pools; gathered bytes then count codes + scales), and ``--mode store``
-times qsa_kv_store itself.
+bf16 pools; gathered bytes then count codes + scales), ``--kv-format
+tiered`` decodes from a tiered pool (int4-g32 pool plus an int8-g64 ring of
+``--ring-rows`` rows, written by qsa_kv_store_tiered in slot order, so the
+ring holds the last ring-rows slots; ``--hot-frac`` draws that fraction of
+the entries from those slots, otherwise the lists are the default uniform
+ones), and ``--mode store`` times qsa_kv_store itself.
 """
 from __future__ import annotations
 
@@ -86,6 +90,44 @@ def quantized_pools(k, v, fmt, group, scale_dtype):
     qsa.kv_store(k, v, loc, kc, vc, kv_format=fmt, k_scale=ks, v_scale=vs, group_size=group)
     torch.cuda.synchronize()
     return kc, vc, ks, vs
+
+
+def tiered_pools(k, v, ring_rows):
+    """Tiered device pool written by qsa_kv_store_tiered from bf16 device
+    pools, every slot in slot order (calls of 32768 tokens)."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    slots, hkv = k.shape[0], k.shape[1]
+    dev = "cuda"
+    pool = dict(
+        ring_k=torch.empty((ring_rows, hkv, 256), dtype=torch.int8, device=dev),
+        ring_v=torch.empty((ring_rows, hkv, 256), dtype=torch.int8, device=dev),
+        ring_k_scale=torch.empty((ring_rows, hkv, 4), dtype=torch.float16, device=dev),
+        ring_v_scale=torch.empty((ring_rows, hkv, 4), dtype=torch.float16, device=dev),
+        owner=torch.full((ring_rows,), -1, dtype=torch.int32, device=dev),
+        claim=torch.zeros((ring_rows,), dtype=torch.int32, device=dev),
+        cold_k=torch.empty((slots, hkv, 128), dtype=torch.uint8, device=dev),
+        cold_v=torch.empty((slots, hkv, 128), dtype=torch.uint8, device=dev),
+        cold_k_scale=torch.empty((slots, hkv, 8), dtype=torch.float16, device=dev),
+        cold_v_scale=torch.empty((slots, hkv, 8), dtype=torch.float16, device=dev))
+    for b0 in range(0, slots, 32768):
+        loc = torch.arange(b0, min(slots, b0 + 32768), dtype=torch.int32, device=dev)
+        qsa.kv_store_tiered(k[b0:b0 + 32768], v[b0:b0 + 32768], loc, pool)
+    torch.cuda.synchronize()
+    return pool
+
+
+def tiered_gathered_bytes(sel, cu, owner, hkv):
+    """Bytes a tiered decode must read: per (entry, KV head) its owner id
+    (4 B) plus K and V of the tier it reads (ring: 256 codes + 4 fp16
+    scales; int4 pool: 128 bytes + 8 fp16 scales)."""
+    import numpy as np
+    s = sel[: int(cu[-1])].astype(np.int64)
+    hot = owner[s & (len(owner) - 1)] == s
+    n_hot = int(hot.sum())
+    n_cold = int(s.size - n_hot)
+    per_head = n_hot * (2 * (256 + 8) + 4) + n_cold * (2 * (128 + 16) + 4)
+    return per_head * hkv, n_hot / max(1, s.size)
 
 
 def cpu_baseline(case, min_seconds: float):
@@ -195,7 +237,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["decode", "copy", "store"], default="decode")
-    ap.add_argument("--kv-format", choices=list(FORMATS), default="bf16")
+    ap.add_argument("--kv-format", choices=list(FORMATS) + ["tiered"], default="bf16")
+    ap.add_argument("--ring-rows", type=int, default=8192, help="tiered: ring rows (power of two)")
+    ap.add_argument("--hot-frac", type=float, default=None,
+                    help="tiered: fraction of entries drawn from the ring's slots")
     ap.add_argument("--group", type=int, default=None)
     ap.add_argument("--scale-dtype", choices=["f32", "f16"], default="f32")
     ap.add_argument("--tokens", type=int, default=32768, help="tokens per store call")
@@ -234,11 +279,16 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     case = synth.case_bs128_tp1_saturated(bs=args.bs, hkv=args.hkv)
+    slots = case.k_pool.shape[0]
     bank_sels = [case.sel]
     for i in range(1, args.banks):
         rng = np.random.default_rng(103_000 + i)
-        lists = [synth.draw_indices(rng, n, case.k_pool.shape[0]) for n in case.lengths]
+        lists = [synth.draw_indices(rng, n, slots) for n in case.lengths]
         bank_sels.append(synth.pack(lists)[0])
+    if args.kv_format == "tiered" and args.hot_frac is not None:
+        recent = np.arange(slots - args.ring_rows, slots)
+        bank_sels = [synth.tiered_lists(np.random.default_rng(104_000 + i), case.lengths, slots,
+                                        recent, args.hot_frac)[0] for i in range(args.banks)]
     print(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
           flush=True)
 
@@ -246,10 +296,15 @@ def main():
     k = case.k_pool.cuda()
     v = case.v_pool.cuda()
     fmt = args.kv_format
-    group = args.group or FORMATS[fmt][2]
+    group = args.group or FORMATS.get(fmt, (0, 0, 32))[2]
     sdt = torch.float16 if args.scale_dtype == "f16" else torch.float32
     qkw = {}
-    if fmt != "bf16":
+    tiered = None
+    if fmt == "tiered":
+        tiered = tiered_pools(k, v, args.ring_rows)
+        del k, v
+        owner_host = tiered["owner"].cpu().numpy()
+    elif fmt != "bf16":
         kc, vc, ks, vs = quantized_pools(k, v, fmt, group, sdt)
         del k, v
         k, v = kc, vc
@@ -261,28 +316,46 @@ def main():
     qsa.workspace_reserve(case.bs, case.hq, case.hkv)
     torch.cuda.synchronize()
 
+    if tiered is not None:
+        def step(i):
+            qsa.decode_tiered(q, tiered, sels[i % len(sels)], cu, out=out, lse=lse)
+    else:
+        def step(i):
+            qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
     for i in range(args.warmup):
-        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
+        step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     counters_ok = all(c == 0 for c in qsa.debug_counters())
 
-    rb = row_bytes(fmt, group, 2 if args.scale_dtype == "f16" else 4)
-    b_kv = gathered_bytes(case.lengths, case.hkv, rb)
+    hot_share = None
+    if tiered is not None:
+        per_bank = [tiered_gathered_bytes(s_, case.cu, owner_host, case.hkv) for s_ in bank_sels]
+        b_kv = int(sum(b for b, _ in per_bank) / len(per_bank))
+        hot_share = round(sum(h for _, h in per_bank) / len(per_bank), 4)
+    else:
+        rb = row_bytes(fmt, group, 2 if args.scale_dtype == "f16" else 4)
+        b_kv = gathered_bytes(case.lengths, case.hkv, rb)
     gbs = b_kv / (ms_per_step * 1e-3) / 1e9
     splits, wgs = qsa.plan(case.bs, case.hkv)
     traffic = committed_traffic() if fmt == "bf16" else None
-    pool_desc = "bf16 pools" if fmt == "bf16" else (
-        f"{fmt} pools (group {group}, {args.scale_dtype} scales, written by qsa_kv_store)")
+    if fmt == "bf16":
+        pool_desc = "bf16 pools"
+    elif tiered is not None:
+        pool_desc = (f"tiered pool (int4-g32 + int8-g64 ring of {args.ring_rows} rows holding the "
+                     f"last written slots, f16 scales, written by qsa_kv_store_tiered; "
+                     f"{hot_share:.1%} of entries read the ring)")
+    else:
+        pool_desc = f"{fmt} pools (group {group}, {args.scale_dtype} scales, written by qsa_kv_store)"
 
     line = {
         "metric": METRIC,
@@ -306,6 +379,7 @@ def main():
             "bs": case.bs, "hq": case.hq, "hkv": case.hkv, "head_dim": 256,
             "sel_per_row": int(case.lengths.max()), "pool_slots": int(case.k_pool.shape[0]),
             "index_banks": len(sels), "splits": splits, "workgroups": wgs,
+            **({"ring_rows": args.ring_rows, "hot_share": hot_share} if tiered is not None else {}),
             "gathered_kv_bytes_per_call": b_kv, "counters_at_rest": counters_ok,
         },
         "roofline": {

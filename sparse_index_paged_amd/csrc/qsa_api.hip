@@ -497,6 +497,44 @@ void set_store_pool(qsa::StoreParams *p, const PoolDesc &pd, const qsa_tensor *k
   p->slots = pd.slots;
 }
 
+// Tiered pools: true when, for each of K, V and their scales, every ring
+// and int4 row lies within 4 GiB above the lower of the two arrays' starts
+// and row offsets are 24-bit x 24-bit products; then sets the common bases
+// and the kernel addresses rows with 32-bit offsets.
+bool tiered_fits_32(const qsa_tiered_pool *tp, const TieredDesc &td, qsa::Params *p) {
+  constexpr int64_t k24 = int64_t{1} << 24, k32 = int64_t{1} << 32;
+  if (td.ring.slots > k24 || td.cold.slots > k24) return false;
+  const int64_t hkv = td.cold.hkv;
+  struct Span {
+    uintptr_t lo, hi;
+  };
+  // byte span of an array of `rows` rows (slot stride ss, head stride sh)
+  auto span = [&](const void *data, int64_t rows, int64_t ss, int64_t sh, int64_t row, bool *ok) {
+    if (ss >= k24) *ok = false;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(data);
+    return Span{lo, lo + static_cast<uintptr_t>((rows - 1) * ss + (hkv - 1) * sh + row)};
+  };
+  const uint8_t *bases[4];
+  const qsa_tensor *rt[4] = {&tp->ring_k, &tp->ring_v, &tp->ring_k_scale, &tp->ring_v_scale};
+  const qsa_tensor *ct[4] = {&tp->cold_k, &tp->cold_v, &tp->cold_k_scale, &tp->cold_v_scale};
+  const int64_t eb[4] = {1, 1, 2, 2};
+  const int64_t rrow[4] = {256, 256, 8, 8}, crow[4] = {128, 128, 16, 16};
+  for (int a = 0; a < 4; ++a) {
+    bool ok = true;
+    const Span r = span(rt[a]->data, td.ring.slots, rt[a]->stride[0] * eb[a], rt[a]->stride[1] * eb[a], rrow[a], &ok);
+    const Span c = span(ct[a]->data, td.cold.slots, ct[a]->stride[0] * eb[a], ct[a]->stride[1] * eb[a], crow[a], &ok);
+    const uintptr_t lo = r.lo < c.lo ? r.lo : c.lo;
+    const uintptr_t hi = r.hi > c.hi ? r.hi : c.hi;
+    if (!ok || hi - lo > static_cast<uintptr_t>(k32)) return false;
+    bases[a] = reinterpret_cast<const uint8_t *>(lo);
+  }
+  p->ring.kb = bases[0];
+  p->ring.vb = bases[1];
+  p->ring.ksb = bases[2];
+  p->ring.vsb = bases[3];
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -600,7 +638,6 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.vs_ss = td.cold.vs_ss;
   p.vs_sh = td.cold.vs_sh;
   p.scale_f16 = 1;
-  p.a32 = 0;
   p.slots = td.cold.slots;
   p.ring.k = static_cast<const uint8_t *>(pool->ring_k.data);
   p.ring.v = static_cast<const uint8_t *>(pool->ring_v.data);
@@ -616,6 +653,7 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.ring.vs_sh = td.ring.vs_sh;
   p.ring.owner = static_cast<const int32_t *>(pool->owner.data);
   p.ring.mask = static_cast<uint32_t>(td.ring.slots - 1);
+  p.a32 = tiered_fits_32(pool, td, &p) ? 1 : 0;
   const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();

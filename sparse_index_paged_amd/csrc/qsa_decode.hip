@@ -193,14 +193,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   using LDS = Lds<W>;
   using Scale = typename std::conditional<SF16, _Float16, float>::type;
   constexpr bool TIER = FMT == kFmtTIERED;
-  static_assert(!TIER || (G == 32 && SF16 && !A32), "tiered pools: f16 scales staged per 32 channels");
+  static_assert(!TIER || (G == 32 && SF16), "tiered pools: f16 scales staged per 32 channels");
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
   // tiles in flight: as many as fit the register budget of one bf16 tile
   // (8 row loads per lane for K and for V), so narrower formats keep as many
-  // bytes in flight per wave as bf16 does
-  constexpr int D = 8 / NI;
+  // bytes in flight per wave as bf16 does; a tiered pool keeps one (its
+  // owner ids and tier selects take the registers of a second)
+  constexpr int D = TIER ? 1 : 8 / NI;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
@@ -284,6 +285,19 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   const uint8_t *rksbase = TIER ? p.ring.ks + g * p.ring.ks_sh + (sgrp >> 1) * 2 : nullptr;
   const uint8_t *rvsbase = TIER ? p.ring.vs + g * p.ring.vs_sh + (sgrp >> 1) * 2 : nullptr;
   const uint32_t rmask = TIER ? p.ring.mask : 0u;
+  // tiered with A32: one uniform base per array; a row's address is that
+  // base plus a 32-bit offset, d*r (ring) or d*c (int4 pool) plus a 24-bit
+  // product, the tier chosen per lane by a select on the offset
+  auto delta = [](const uint8_t *p0, const uint8_t *base) {
+    return static_cast<uint32_t>(static_cast<uint64_t>(p0 - base));
+  };
+  constexpr bool T32 = TIER && A32;
+  const uint32_t dkr = T32 ? delta(rkbase, p.ring.kb) : 0u, dkc = T32 ? delta(ckbase, p.ring.kb) : 0u;
+  const uint32_t dvr = T32 ? delta(rvbase, p.ring.vb) : 0u, dvc = T32 ? delta(cvbase, p.ring.vb) : 0u;
+  const uint32_t dksr = T32 ? delta(rksbase, p.ring.ksb) : 0u, dksc = T32 ? delta(ksbase, p.ring.ksb) : 0u;
+  const uint32_t dvsr = T32 ? delta(rvsbase, p.ring.vsb) : 0u, dvsc = T32 ? delta(vsbase, p.ring.vsb) : 0u;
+  const uint32_t rk_ss32 = static_cast<uint32_t>(p.ring.k_ss), rv_ss32 = static_cast<uint32_t>(p.ring.v_ss);
+  const uint32_t rks_ss32 = static_cast<uint32_t>(p.ring.ks_ss), rvs_ss32 = static_cast<uint32_t>(p.ring.vs_ss);
 
   // per-lane online-softmax state for head r16 (replicated over lane groups)
   float m_run = -INFINITY;
@@ -354,11 +368,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       const uint32_t r = static_cast<uint32_t>(sl[i]) & rmask;
       const bool h = ow[i] == sl[i];
       hot[u][i] = h;
-      const int64_t ro = static_cast<int64_t>(r), co = static_cast<int64_t>(cs);
-      kraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rkbase + ro * p.ring.k_ss : ckbase + co * p.k_ss);
-      vraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rvbase + ro * p.ring.v_ss : cvbase + co * p.v_ss);
-      ksr[u][i] = *reinterpret_cast<const Scale *>(h ? rksbase + ro * p.ring.ks_ss : ksbase + co * p.ks_ss);
-      vsr[u][i] = *reinterpret_cast<const Scale *>(h ? rvsbase + ro * p.ring.vs_ss : vsbase + co * p.vs_ss);
+      if constexpr (A32) {
+        auto at = [&](const uint8_t *base, uint32_t ro, uint32_t co) {
+          return base + static_cast<uint64_t>(h ? ro : co);
+        };
+        kraw[u][i] = *reinterpret_cast<const uint4 *>(
+            at(p.ring.kb, __umul24(r, rk_ss32) + dkr, __umul24(cs, k_ss32) + dkc));
+        vraw[u][i] = *reinterpret_cast<const uint4 *>(
+            at(p.ring.vb, __umul24(r, rv_ss32) + dvr, __umul24(cs, v_ss32) + dvc));
+        ksr[u][i] = *reinterpret_cast<const Scale *>(
+            at(p.ring.ksb, __umul24(r, rks_ss32) + dksr, __umul24(cs, ks_ss32) + dksc));
+        vsr[u][i] = *reinterpret_cast<const Scale *>(
+            at(p.ring.vsb, __umul24(r, rvs_ss32) + dvsr, __umul24(cs, vs_ss32) + dvsc));
+      } else {
+        const int64_t ro = static_cast<int64_t>(r), co = static_cast<int64_t>(cs);
+        kraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rkbase + ro * p.ring.k_ss : ckbase + co * p.k_ss);
+        vraw[u][i] = *reinterpret_cast<const uint4 *>(h ? rvbase + ro * p.ring.v_ss : cvbase + co * p.v_ss);
+        ksr[u][i] = *reinterpret_cast<const Scale *>(h ? rksbase + ro * p.ring.ks_ss : ksbase + co * p.ks_ss);
+        vsr[u][i] = *reinterpret_cast<const Scale *>(h ? rvsbase + ro * p.ring.vs_ss : vsbase + co * p.vs_ss);
+      }
     }
   };
   auto issue = [&](int u, const int32_t (&sl)[NI]) {
@@ -601,10 +629,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       const int t = t0 + u;
       stage(u);
       if constexpr (TIER) {
+        // owner ids of tile t+2D from its slot ids fetched D steps ago; the
+        // same slot ids are fetched again (cache hits) for the row issue D
+        // steps later, so no loaded register is copied
         issue_tiered(u, snext[u], onext[u]);
-#pragma unroll
-        for (int i = 0; i < NI; ++i) snext[u][i] = s2[u][i];
-        fetch_owners(snext[u], onext[u]);
+        fetch_owners(s2[u], onext[u]);
+        fetch_slots(t + 2 * D, snext[u]);
         fetch_slots(t + 3 * D, s2[u]);
       } else {
         issue(u, snext[u]);
@@ -913,7 +943,7 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
       break;
     case kFmtTIERED: {
       const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
-      launch_waves<kFmtTIERED, 32, true, false>(p, dim3(npairs8 * p.nsplit), stream);
+      launch_addr<kFmtTIERED, 32, true>(p, dim3(npairs8 * p.nsplit), stream);
       return hipGetLastError();
     }
     default: break;

@@ -54,6 +54,9 @@ struct Params {
     int64_t ks_ss, ks_sh, vs_ss, vs_sh;  // byte strides
     const int32_t *owner;   // [R]
     uint32_t mask;          // R - 1
+    // with Params::a32: per array a base from which every ring and int4
+    // row (and scale row) lies within 4 GiB, for 32-bit lane offsets
+    const uint8_t *kb, *vb, *ksb, *vsb;
   } ring;
   int bs, hkv;
   int nsplit;               // splits per (row, kv head) in the grid

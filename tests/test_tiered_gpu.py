@@ -235,3 +235,92 @@ def test_tiered_full_size_sampled_rows():
     q = synth.normal_bf16(rng, (bs, 24, 256))
     out, lse = decode_and_compare(q, dev, ring, cold, sel, cu, "bs128 tp1 full size", rows=rows)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_tiered_pools_beyond_32bit_offsets():
+    """int4 pool rows 2^24 bytes apart (strided views into 4.4 GB buffers), so
+    the two tiers cannot share a 32-bit offset range and the 64-bit address
+    path is used; compared with the oracle on compact host copies."""
+    rng = np.random.default_rng(560)
+    slots, hkv, r = 260, 2, 64
+    x = synth.normal_bf16(rng, (slots, hkv, 256))
+    y = synth.normal_bf16(rng, (slots, hkv, 256))
+    ring, cold = write_history(x, y, synth.write_batches(rng, rng.permutation(slots), 4),
+                               *layout.empty_tiered(r, slots, hkv))
+    dev = to_dev(ring, cold)
+    stride = 1 << 24
+    say(f"[gpu] tiered 64-bit addressing: slots={slots} int4 slot stride={stride} B")
+    big = []
+    for name in ("cold_k", "cold_v"):
+        buf = torch.empty(slots * stride, dtype=torch.uint8, device="cuda")
+        view = buf.as_strided((slots, hkv, 128), (stride, 128, 1))
+        view.copy_(dev[name])
+        dev[name] = view
+        big.append(buf)
+    sel, cu = synth.tiered_lists(rng, [2055, 700, 1, 0, 1500], slots, np.arange(slots), 0.3,
+                                 dup_prob=0.05)
+    q = synth.normal_bf16(rng, (5, 24, 256))
+    decode_and_compare(q, dev, ring, cold, sel, cu, "64-bit addressing")
+    del big, dev
+    torch.cuda.empty_cache()
+
+
+def test_tiered_graph_replay_matches_eager():
+    """A captured graph of one tiered write (new tokens into the pool) plus
+    one tiered decode, replayed with new tokens, slot ids, index lists and
+    lengths copied into its buffers between replays; every replay's output
+    and pool state equal those of the same calls made eagerly on a twin
+    pool.  The pages call the tiered read graph-safe (no compactor, no
+    unmapping mid-request)."""
+    rng = np.random.default_rng(570)
+    slots, hkv, r, bs, n_new = 8192, 2, 512, 8, 64
+    x = synth.normal_bf16(rng, (slots, hkv, 256))
+    y = synth.normal_bf16(rng, (slots, hkv, 256))
+    order = rng.permutation(slots)
+    ring, cold = write_history(x, y, synth.write_batches(rng, order[:4096], 4),
+                               *layout.empty_tiered(r, slots, hkv))
+    dev_g, dev_e = to_dev(ring, cold), to_dev(ring, cold)
+    kbuf = torch.empty((n_new, hkv, 256), dtype=torch.bfloat16, device="cuda")
+    vbuf = torch.empty_like(kbuf)
+    locbuf = torch.empty(n_new, dtype=torch.int32, device="cuda")
+    cap = bs * 2055
+    selbuf = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    cubuf = torch.zeros(bs + 1, dtype=torch.int32, device="cuda")
+    qbuf = synth.normal_bf16(rng, (bs, 24, 256)).cuda()
+    out = torch.empty((bs, 24, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((bs, 24), dtype=torch.float32, device="cuda")
+    qsa.workspace_reserve(bs, 24, 2)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qsa.kv_store_tiered(kbuf, vbuf, locbuf, dev_g)
+        qsa.decode_tiered(qbuf, dev_g, selbuf, cubuf, out=out, lse=lse)
+
+    written = 4096
+    for rep in range(6):
+        loc = order[written:written + n_new]
+        written += n_new
+        lens = rng.integers(0, 2056, size=bs)
+        sel, cu = synth.tiered_lists(rng, lens, slots, order[written - r:written], 0.5)
+        kbuf.copy_(x[loc])
+        vbuf.copy_(y[loc])
+        locbuf.copy_(torch.from_numpy(loc.astype(np.int32)))
+        selbuf.zero_()
+        selbuf[:sel.shape[0]].copy_(torch.from_numpy(sel))
+        cubuf.copy_(torch.from_numpy(cu))
+        g.replay()
+        qsa.kv_store_tiered(kbuf, vbuf, locbuf, dev_e)
+        oe, le = qsa.decode_tiered(qbuf, dev_e, selbuf, cubuf)
+        torch.cuda.synchronize()
+        say(f"  replay {rep}: n_sel={sel.shape[0]}")
+        assert torch.equal(out.view(torch.int16), oe.view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(lse.view(torch.int32), le.view(torch.int32)), f"replay {rep}: lse"
+        for name in dev_g:
+            assert torch.equal(dev_g[name].view(torch.uint8), dev_e[name].view(torch.uint8)), \
+                f"replay {rep}: {name}"
+        assert not dev_g["claim"].any().item()
+    # the last replay against the oracle as well
+    ring, cold = write_history(x, y, [order[4096:written]], ring, cold)
+    o_ref, l_ref = oracle_tiered(qbuf.cpu(), ring, cold, sel, cu)
+    compare(out, lse, o_ref, l_ref, np.diff(cu), label="graph replay")
