@@ -152,6 +152,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 // bank groups, and every LDS address stays base + immediate.
 constexpr int kLdsRow = kHeadDim * 2 + 16;
 
+// Rows of the merge's accumulator table are padded from 256 to 260 floats:
+// the 16 lanes of a 16-byte write then cover 16 different 4-bank groups
+// (unpadded, rows 1 KB apart put all 16 into the same banks)
+constexpr int kAccRow = kHeadDim + 4;
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -160,23 +165,20 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // LDS layout for a workgroup of W waves.  During the loop each wave owns a
 // K tile and a V tile [16][528 B] (dequantized to bf16) plus their scale
-// rows, and all waves share Q [16][528 B];
-// afterwards the same bytes are reused to merge the wave states.
+// rows, and all waves share Q [16][528 B]; afterwards each of waves 0..3
+// puts its state (m[16], l[16], acc[12][260]) into its own loop area, and
+// the split merge's per-wave weight tables [4][64][16] reuse the start of
+// the buffer.  A workgroup of 8 waves first folds waves 4..7 into 0..3
+// through [4][16 f32x4][64 lanes].
 template <int W> struct Lds {
   static constexpr int kTileB = kTile * kLdsRow;               // one bf16 tile [16][528 B]
   static constexpr int kScaleFloats = kTile * 8;               // up to 8 groups per row
   static constexpr int kWave = 2 * kTileB + 2 * kScaleFloats * 4;
   static constexpr int kLoop = W * kWave;
   static constexpr int kQ = 16 * kLdsRow;
-  // merge of 4 wave states: m, l [4][16] and acc [4][12][256] (the split
-  // merge's per-wave weight tables [4][64][16] fit in the same bytes); a
-  // workgroup of 8 waves first folds waves 4..7 into 0..3 through
-  // [4][16 f32x4][64 lanes]
-  static constexpr int kMerge4 = (2 * 4 * 16 + 4 * kGqa * kHeadDim) * 4;
-  static_assert(kMerge4 >= 4 * 64 * 16 * 4, "split-merge weight tables exceed the merge area");
+  static_assert(4 * 64 * 16 * 4 <= kLoop, "split-merge weight tables exceed the loop area");
   static constexpr int kFold = (W > 4) ? 4 * (16 * 64 * 16 + 2 * 64 * 4) : 0;
-  static constexpr int kMerge = kMerge4 > kFold ? kMerge4 : kFold;
-  static constexpr int kBytes = (kLoop + kQ) > kMerge ? (kLoop + kQ) : kMerge;
+  static constexpr int kBytes = (kLoop + kQ) > kFold ? (kLoop + kQ) : kFold;
 };
 
 __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthreads) {
@@ -622,8 +624,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // The loop runs whole groups of D steps; a step past the last tile stages
   // and loads (the clamped rows) but skips the processing, so no load sits
   // behind a branch and the compiler's load counting never has to assume a
-  // skipped load and wait for every load in flight.
-  for (int t0 = 0; t0 < ntile; t0 += D) {
+  // skipped load and wait for every load in flight.  The last group is
+  // peeled off the loop and issues no loads.
+  int t0 = 0;
+  for (; t0 + D < ntile; t0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int t = t0 + u;
@@ -643,6 +647,18 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
       if (t < ntile) process(t);
     }
   }
+  // the last group: its rows are in flight already and nothing more is
+  // loaded, so the epilogue never waits for rows that would not be used
+  if (t0 < ntile) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int t = t0 + u;
+      if (t < ntile) {
+        stage(u);
+        process(t);
+      }
+    }
+  }
 
   // ---- wave result: full sum per head over the 4 lane groups
   float l_w = l_run + __shfl_xor(l_run, 16);
@@ -654,8 +670,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 
   // ---- 8-wave workgroups: fold waves 4..7 into waves 0..3 (same lane
   // layout, so the fold is element-wise per lane)
-  __syncthreads();
   if constexpr (W > 4) {
+    __syncthreads();
     f32x4 *fold = reinterpret_cast<f32x4 *>(smem);               // [4][16][64]
     float *fold_ml = reinterpret_cast<float *>(smem + 4 * 16 * 64 * 16);  // [4][2][64]
     if (wave >= 4) {
@@ -680,19 +696,22 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     __syncthreads();
   }
 
-  // ---- merge the (up to) 4 wave states of this workgroup through LDS
-  float *red_m = reinterpret_cast<float *>(smem);   // [4][16]
-  float *red_l = red_m + 4 * 16;                    // [4][16]
-  float *red_acc = red_l + 4 * 16;                  // [4][12][256]
+  // ---- merge the (up to) 4 wave states of this workgroup through LDS.
+  // Wave w's state (m[16], l[16], acc[12][260]) goes into its own loop
+  // area, which no other wave reads, so a wave writes it as soon as its
+  // loop is done and one barrier suffices.
+  auto wstate = [&](int w) { return reinterpret_cast<float *>(smem + w * LDS::kWave); };
+  static_assert((32 + kGqa * kAccRow) * 4 <= LDS::kWave, "a wave state exceeds the wave's loop area");
   if (wave < 4) {
+    float *ws = wstate(wave);
     if (qg == 0) {
-      red_m[wave * 16 + r16] = m_run;
-      red_l[wave * 16 + r16] = l_w;
+      ws[r16] = m_run;
+      ws[16 + r16] = l_w;
     }
     if (r16 < kGqa) {
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt)
-        *reinterpret_cast<f32x4 *>(red_acc + (wave * kGqa + r16) * kHeadDim + 16 * mt + 4 * qg) = acc[mt];
+        *reinterpret_cast<f32x4 *>(ws + 32 + r16 * kAccRow + 16 * mt + 4 * qg) = acc[mt];
     }
   }
   __syncthreads();
@@ -731,7 +750,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   float Mw = 0.f, sw = 0.f;
   f32x4 o[3];
   if (wv < 4) {
-    const float fj = weights4(red_m[lane], red_l[lane], Mw, sw);
+    const float fj = weights4(wstate(sq)[hh], wstate(sq)[16 + hh], Mw, sw);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int h = 4 * k + wv;
@@ -739,7 +758,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
 #pragma unroll
       for (int w = 0; w < 4; ++w)
         o[k] += bcast(fj, 16 * w + h) *
-                *reinterpret_cast<const f32x4 *>(red_acc + (w * kGqa + h) * kHeadDim + 4 * lane);
+                *reinterpret_cast<const f32x4 *>(wstate(w) + 32 + h * kAccRow + 4 * lane);
     }
   }
 
@@ -788,21 +807,31 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   if (!s_last || wv >= 4) return;
 
   // (a) m and l of every split: lane j = 16 s' + h of round r holds split
-  // 4r + s' (at most 64 splits = 16 rounds), issued together with the
-  // accumulators of the first 8 splits
+  // 4r + s' (at most 64 splits = 16 rounds; rounds past the last split
+  // re-read the last split and are masked), then the accumulators of the
+  // first 8 splits.  Round 0 always exists and is straight-line code; the
+  // other rounds sit behind one branch, so the common case of at most 4
+  // splits issues all its loads back to back.
   constexpr int kBatch = 8;
   const int nround = (n_active + 3) >> 2;
-  // (rounds past the last split re-read the last split and are masked)
   float mr[16], lr[16];
+  {
+    const int s = min(sq, n_active - 1);
+    mr[0] = ld(pbase + s * kPartFloats + hh);
+    lr[0] = ld(pbase + s * kPartFloats + 16 + hh);
+  }
+  if (nround > 1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < nround) {
-      const int s = min(4 * r + sq, n_active - 1);
-      mr[r] = ld(pbase + s * kPartFloats + hh);
-      lr[r] = ld(pbase + s * kPartFloats + 16 + hh);
+    for (int r = 1; r < 16; ++r) {
+      if (r < nround) {
+        const int s = min(4 * r + sq, n_active - 1);
+        mr[r] = ld(pbase + s * kPartFloats + hh);
+        lr[r] = ld(pbase + s * kPartFloats + 16 + hh);
+      }
     }
   }
-  auto acc_ld = [&](int s, int k, int i) { return ld(pbase + s * kPartFloats + 32 + ((4 * k + wv) * 4 + i) * 64 + lane); };
+  const float *pacc = pbase + 32 + wv * 4 * 64 + lane;
+  auto acc_ld = [&](int s, int k, int i) { return ld(pacc + s * kPartFloats + (16 * k + i) * 64); };
   // (a split's registers are only written and read when the split exists)
   f32x4 a[kBatch][3];
 #pragma unroll
