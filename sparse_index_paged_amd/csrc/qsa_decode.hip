@@ -844,7 +844,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     }
 
   // (b) per head: merged max, each split's weight (into this wave's LDS
-  // table wf[split][16]), sum and reciprocal
+  // table wf[split][16] beyond 4 splits), sum and reciprocal
   float M = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -855,30 +855,47 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   }
   M = fmaxf(M, __shfl_xor(M, 16));
   M = fmaxf(M, __shfl_xor(M, 32));
+  // (with at most 4 splits the weights stay in registers: lane 16 s + h
+  // holds split s's weight for head h and is read out with readlane)
+  const bool few = n_active <= 4;
   float *wf = reinterpret_cast<float *>(smem) + wv * 64 * 16;
-  float ssum = 0.f;
+  float ssum = 0.f, f0 = 0.f;
+  if (few) {
+    f0 = (mr[0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr[0] - M);
+    ssum = f0 * lr[0];
+  } else {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (r < nround) {
-      const float f = (mr[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr[r] - M);
-      wf[r * 64 + lane] = f;
-      ssum += f * lr[r];
+    for (int r = 0; r < 16; ++r) {
+      if (r < nround) {
+        const float f = (mr[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr[r] - M);
+        wf[r * 64 + lane] = f;
+        ssum += f * lr[r];
+      }
     }
+    wave_lds_fence();
   }
   ssum += __shfl_xor(ssum, 16);
   ssum += __shfl_xor(ssum, 32);
-  wave_lds_fence();
 
   // (c) out = (sum_s w_s acc_s) / l with the splits in index order
   f32x4 acc_o[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) acc_o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (few) {
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u)
-    if (u < n_active) {
+    for (int u = 0; u < 4; ++u)
+      if (u < n_active) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) acc_o[k] += wf[u * 16 + 4 * k + wv] * a[u][k];
-    }
+        for (int k = 0; k < 3; ++k) acc_o[k] += bcast(f0, 16 * u + 4 * k + wv) * a[u][k];
+      }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (u < n_active) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) acc_o[k] += wf[u * 16 + 4 * k + wv] * a[u][k];
+      }
+  }
   for (int s0 = kBatch; s0 < n_active; s0 += kBatch) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
