@@ -30,6 +30,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -130,7 +132,20 @@ def tiered_gathered_bytes(sel, cu, owner, hkv):
     return per_head * hkv, n_hot / max(1, s.size)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, min_seconds: float):
+    """The float64 oracle on the host: the whole workload with the host's
+    threads (at most 16), repeated for about min_seconds, and a bounded
+    sample (8 rows) with one thread."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     used = oracle.threads_used(threads)
@@ -143,10 +158,39 @@ def cpu_baseline(case, min_seconds: float):
             break
     dt = time.perf_counter() - t0
     b = gathered_bytes(case.lengths, case.hkv) * calls
+    rows = min(8, case.bs)
+    cu1 = case.cu[: rows + 1]
+    t1 = time.perf_counter()
+    oracle.decode(case.q[:rows].contiguous(), case.k_pool, case.v_pool, case.sel[: int(cu1[-1])], cu1,
+                  nthreads=1)
+    dt1 = time.perf_counter() - t1
+    b1 = gathered_bytes(np.diff(cu1), case.hkv)
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "sample": f"the full workload (all {case.bs} rows) decoded {calls}x by the float64 "
                       f"oracle with {used} OpenMP threads, {dt:.1f} s wall; "
-                      f"{dt / calls * 1e6:.0f} us per call"}
+                      f"{dt / calls * 1e6:.0f} us per call",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"the first {rows} rows, once, 1 thread, {dt1:.2f} s"}}
+
+
+def copy_rate(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Plain device-to-device copy on the same box (read + write GB/s)."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / reps / 1e3
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / sec / 1e9
 
 
 def copy_mode(args):
@@ -177,6 +221,8 @@ def store_mode(args):
     import sparse_index_paged_amd as qsa
     import synth
     fmt = args.kv_format
+    if fmt == "tiered":
+        return store_tiered_mode(args)
     group = args.group or FORMATS[fmt][2]
     sdt = torch.float16 if args.scale_dtype == "f16" else torch.float32
     slots, hkv, n = 262144, args.hkv, args.tokens
@@ -226,16 +272,64 @@ def store_mode(args):
     }), flush=True)
 
 
+def store_tiered_mode(args):
+    """qsa_kv_store_tiered throughput: `tokens` new rows per call into a
+    tiered pool (int4-g32 pool of 262144 slots, int8-g64 ring of ring-rows
+    rows, f16 scales); slots are consecutive, as handed out in order.
+    Algorithmic bytes per call = bf16 rows read + slot ids + int4 rows and
+    scales written + int8 ring rows, scales and owner ids written for the
+    tokens that keep a ring row."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    import synth
+    slots, hkv, n, r = 262144, args.hkv, args.tokens, args.ring_rows
+    rng = np.random.default_rng(2025)
+    xk = synth.normal_bf16(rng, (slots, hkv, 256)).cuda()
+    xv = synth.normal_bf16(rng, (slots, hkv, 256)).cuda()
+    pool = tiered_pools(xk, xv, r)
+    nb = max(1, slots // n)
+    banks = [(xk[i * n:(i + 1) * n], xv[i * n:(i + 1) * n],
+              torch.arange(i * n, (i + 1) * n, dtype=torch.int32, device="cuda")) for i in range(min(nb, 4))]
+    for i in range(args.warmup):
+        qsa.kv_store_tiered(*banks[i % len(banks)], pool)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        qsa.kv_store_tiered(*banks[i % len(banks)], pool)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kept = min(n, r)
+    b = n * 4 + n * hkv * 2 * (512 + 128 + 16) + kept * (hkv * 2 * (256 + 8) + 4)
+    gbs = b / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "qsa_kv_store_tiered GB/s (bf16 rows read + int4 rows and int8 ring rows written)",
+        "value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3),
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16 -> int4 + int8 ring",
+        "config": {"workload": f"{n} tokens x {hkv} KV heads into a tiered pool: int4-g32 [262144,{hkv},128] "
+                               f"+ int8-g64 ring of {r} rows (f16 scales), consecutive slots",
+                   "tokens": n, "hkv": hkv, "ring_rows": r, "algorithmic_bytes_per_call": b,
+                   "launches_per_call": 3},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": b, "kernel": "qsa_store_kernel<3> + claim + qsa_store_kernel<2>"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats of --steps launches")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--banks", type=int, default=4)
     ap.add_argument("--bs", type=int, default=128)
     ap.add_argument("--hkv", type=int, default=2, choices=[1, 2])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
     ap.add_argument("--mode", choices=["decode", "copy", "store"], default="decode")
     ap.add_argument("--kv-format", choices=list(FORMATS) + ["tiered"], default="bf16")
     ap.add_argument("--ring-rows", type=int, default=8192, help="tiered: ring rows (power of two)")
@@ -325,16 +419,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # timed region: `steps` launches bracketed by HIP events on the stream
+    # the kernels run on, repeated `repeats` times; value = median repeat
     stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / args.steps
+    reps_ms = []
+    for _ in range(args.repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        reps_ms.append(start.elapsed_time(end) / args.steps)
+    ms_per_step = float(np.median(reps_ms))
     counters_ok = all(c == 0 for c in qsa.debug_counters())
 
     hot_share = None
@@ -366,6 +465,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_call": round(ms_per_step * 1e3, 3),
+        "timing": {"repeats": len(reps_ms), "steps_per_repeat": args.steps,
+                   "us_per_call_p10": round(float(np.percentile(reps_ms, 10)) * 1e3, 3),
+                   "us_per_call_median": round(ms_per_step * 1e3, 3),
+                   "us_per_call_p90": round(float(np.percentile(reps_ms, 90)) * 1e3, 3)},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -394,6 +497,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_copy:
+        cr = copy_rate()
+        line["roofline"]["copy_GBps"] = round(cr, 1)
+        line["roofline"]["frac_of_copy"] = round(gbs / cr, 4)
     if not args.no_cpu_baseline and fmt == "bf16":
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
