@@ -6,7 +6,9 @@ x8, every row at 2055 selected entries drawn uniformly with replacement.
 Inputs are resident in HBM before timing starts.  One step = one
 qsa_decode call (one kernel launch).  Several index banks (same recipe,
 different seeds) rotate between steps so that consecutive steps do not
-re-read the same rows from the caches.
+re-read the same rows from the caches.  K timed eager launches, 5 repeats,
+median (``--timing graph`` times the K steps captured once into a HIP graph
+and replayed instead; on this stack that is slightly slower, not faster).
 
 Prints one JSON line.  value = gathered-KV bytes / time (GB/s), where
 gathered-KV bytes = sum_b L_b * Hkv * 2 (K and V) * 512 B.
@@ -323,6 +325,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--repeats", type=int, default=5, help="timed repeats of --steps launches")
+    ap.add_argument("--timing", choices=["eager", "graph"], default="eager",
+                    help="time the steps as eager launches (default) or as a replayed HIP graph")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--banks", type=int, default=4)
     ap.add_argument("--bs", type=int, default=128)
@@ -419,20 +423,42 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: `steps` launches bracketed by HIP events on the stream
-    # the kernels run on, repeated `repeats` times; value = median repeat
-    stream = torch.cuda.current_stream()
-    reps_ms = []
-    for _ in range(args.repeats):
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        start.record(stream)
+
+    def timed(run_steps):
+        """`repeats` timed runs of `steps` calls, each bracketed by HIP
+        events on the stream the kernels run on; ms per call of each."""
+        stream = torch.cuda.current_stream()
+        out_ms = []
+        for _ in range(args.repeats):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            run_steps()
+            end.record(stream)
+            torch.cuda.synchronize()
+            out_ms.append(start.elapsed_time(end) / args.steps)
+        return out_ms
+
+    def eager_steps():
         for i in range(args.steps):
             step(i)
-        end.record(stream)
+
+    # eager timing (reported); with --timing graph the `steps` calls (index
+    # banks rotating as in the eager loop) are also captured once into a HIP
+    # graph and replayed, and that timing is reported instead
+    eager_ms = timed(eager_steps)
+    reps_ms = eager_ms
+    timing_mode = "eager"
+    if args.timing == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_steps()
+        graph.replay()
         torch.cuda.synchronize()
-        reps_ms.append(start.elapsed_time(end) / args.steps)
+        reps_ms = timed(graph.replay)
+        timing_mode = "graph"
+        del graph
     ms_per_step = float(np.median(reps_ms))
     counters_ok = all(c == 0 for c in qsa.debug_counters())
 
@@ -465,7 +491,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_call": round(ms_per_step * 1e3, 3),
-        "timing": {"repeats": len(reps_ms), "steps_per_repeat": args.steps,
+        "timing": {"mode": timing_mode, "repeats": len(reps_ms), "steps_per_repeat": args.steps,
+                   "us_per_call_eager_median": round(float(np.median(eager_ms)) * 1e3, 3),
                    "us_per_call_p10": round(float(np.percentile(reps_ms, 10)) * 1e3, 3),
                    "us_per_call_median": round(ms_per_step * 1e3, 3),
                    "us_per_call_p90": round(float(np.percentile(reps_ms, 90)) * 1e3, 3)},

@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "libqsa.so")
@@ -111,32 +112,43 @@ def _check(status: int):
         raise QsaError(status, msg)
 
 
+_FORMAT_CODES = {"bf16": BF16, "fp8": FP8_E4M3FN, "int8": I8, "int4": U4X2}
+_DTYPE_CODES = None
+_TENSOR_LAYOUT = struct.Struct("<Qii4q4q")  # qsa_tensor: data, dtype, ndim, shape[4], stride[4]
+_PAD = (0, 0, 0, 0)
+assert _TENSOR_LAYOUT.size == ctypes.sizeof(QsaTensor)
+
+
 def _torch_dtype_code(t, kv_format: str | None = None) -> int:
-    import torch
+    global _DTYPE_CODES
     if kv_format is not None:
-        return {"bf16": BF16, "fp8": FP8_E4M3FN, "int8": I8, "int4": U4X2}[kv_format]
-    m = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32,
-         torch.int8: I8, torch.int64: I64}
-    fp8 = getattr(torch, "float8_e4m3fn", None)
-    if fp8 is not None:
-        m[fp8] = FP8_E4M3FN
-    if t.dtype not in m:
+        return _FORMAT_CODES[kv_format]
+    if _DTYPE_CODES is None:
+        import torch
+        m = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32,
+             torch.int8: I8, torch.int64: I64}
+        fp8 = getattr(torch, "float8_e4m3fn", None)
+        if fp8 is not None:
+            m[fp8] = FP8_E4M3FN
+        _DTYPE_CODES = m
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
         raise TypeError(f"no qsa dtype for {t.dtype}")
-    return m[t.dtype]
+    return code
 
 
 def describe(t, kv_format: str | None = None, dtype_code: int | None = None) -> QsaTensor:
     """qsa_tensor for a torch tensor (strides in elements)."""
-    if t.dim() > 4:
+    nd = t.dim()
+    if nd > 4:
         raise ValueError("at most 4 dimensions")
-    d = QsaTensor()
-    d.data = t.data_ptr() if t.numel() > 0 else (t.data_ptr() or 16)
-    d.dtype = dtype_code if dtype_code is not None else _torch_dtype_code(t, kv_format)
-    d.ndim = t.dim()
-    for i in range(t.dim()):
-        d.shape[i] = t.shape[i]
-        d.stride[i] = t.stride(i)
-    return d
+    ptr = t.data_ptr()
+    if not ptr or t.numel() == 0:
+        ptr = ptr or 16
+    code = dtype_code if dtype_code is not None else _torch_dtype_code(t, kv_format)
+    pad = _PAD[nd:]
+    return QsaTensor.from_buffer_copy(
+        _TENSOR_LAYOUT.pack(ptr, code, nd, *t.shape, *pad, *t.stride(), *pad))
 
 
 def _stream_handle(stream):
