@@ -242,7 +242,9 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
  *   "max_splits"     upper bound on splits per (row, KV head) (default 16)
  *   "min_split_keys" fewest list entries a split is given before another
  *                    split is used (default 256)
- *   "waves_per_workgroup" 4 or 8 (default 4)
+ *   "waves_per_workgroup" 4 or 8, or 0 (default): 8 for int4 pools without
+ *                    splits and for tiered pools when the grid has at most
+ *                    one workgroup per CU (256), else 4
  * Changing them affects later launches and later reservations. */
 qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);

@@ -24,7 +24,7 @@ def _default_options():
     qsa.set_option("split_target", 0)
     qsa.set_option("max_splits", 16)
     qsa.set_option("min_split_keys", 256)
-    qsa.set_option("waves_per_workgroup", 4)
+    qsa.set_option("waves_per_workgroup", 0)
 
 
 def test_bs1_tp1_l128():
@@ -59,10 +59,26 @@ def test_bs64_tp1_quantized_full_size(fmt, group, seed):
     run_and_compare(case, f"bs64 tp1 {fmt} g{group}", quant=(fmt, group, kc, ks, vc, vs))
 
 
+@pytest.mark.parametrize("scale_dtype", [torch.float32, torch.float16])
+def test_bs128_tp1_int4_unsplit_eight_waves(scale_dtype):
+    """bs=128 TP1 runs unsplit, where int4 pools take 8-wave workgroups by
+    default; 12 sampled rows against the oracle."""
+    case = synth.case_bs64_tp1_quantsrc(1044, bs=128)
+    assert qsa.plan(128, 2)[0] == 1
+    sd = "f16" if scale_dtype == torch.float16 else "f32"
+    kc, ks = quant.quantize(case.k_pool, "int4", 32, sd)
+    vc, vs = quant.quantize(case.v_pool, "int4", 32, sd)
+    rows = sorted(np.random.default_rng(9).choice(128, size=12, replace=False).tolist())
+    run_and_compare(case, f"bs128 tp1 int4 {sd}", rows=rows, quant=("int4", 32, kc, ks, vc, vs),
+                    scale_dtype=scale_dtype)
+
+
 @pytest.mark.parametrize("fmt,group", [("fp8", 64), ("fp8", 32), ("int8", 64), ("int8", 32),
                                        ("int4", 64)])
 @pytest.mark.parametrize("hkv", [1, 2])
-def test_quantized_group_sizes(fmt, group, hkv):
+@pytest.mark.parametrize("waves", [0, 8])
+def test_quantized_group_sizes(fmt, group, hkv, waves):
+    qsa.set_option("waves_per_workgroup", waves)
     lens = [1, 17, 300, 2055, 64, 0, 1000]
     case = synth.make_case(lengths=lens, slots=4096, hkv=hkv, seed=2000 + group + hkv,
                            dup_prob=0.05)
