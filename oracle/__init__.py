@@ -31,6 +31,7 @@ from . import layout, quant  # noqa: F401  (re-exported)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qsa_oracle.c")
+_SRC_INDEX = os.path.join(_HERE, "qsa_index_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_BF16, FMT_FP8, FMT_INT8, FMT_INT4 = 0, 1, 2, 3
@@ -39,13 +40,15 @@ CAPACITY = 2055
 HEAD_DIM = 256
 GQA = 12
 ERRORS = {1: "bad arguments", 2: "bad cu_seqlens", 3: "row longer than 2055",
-          4: "slot index out of range"}
+          4: "slot index out of range", 5: "context length out of range",
+          6: "block table entry out of range"}
 
 
 def build() -> str:
-    """Compile qsa_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
-    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
-           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    """Compile qsa_oracle.c and qsa_index_oracle.c with gcc (-O2, no
+    fast-math, no floating-point contraction, OpenMP)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off",
+           "-o", _LIB + ".tmp", _SRC, _SRC_INDEX, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -77,6 +80,10 @@ def _load():
             ctypes.c_int, P]
         lib.oracle_fp8_e4m3fn_to_double.restype = ctypes.c_double
         lib.oracle_fp8_e4m3fn_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_qsa_index.restype = ctypes.c_int
+        lib.oracle_qsa_index.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int64, P, ctypes.c_int,
+            P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, P, P]
         lib.oracle_threads_used.restype = ctypes.c_int
         lib.oracle_threads_used.argtypes = [ctypes.c_int]
         _lib = lib
@@ -194,6 +201,42 @@ def decode_tiered(q, owner, ring_k, ring_v, ring_k_scale, ring_v_scale, cold_k, 
     if rc != 0:
         raise ValueError(f"oracle rejected the call: {ERRORS.get(rc, rc)}")
     return out, lse
+
+
+def index(q, k_pool, block_table, req_to_token, ctx_len, *, budget: int, compress_ratio: int,
+          weights=None, return_scores: bool = False):
+    """The QSA indexer step (MQA block scores, exact top-k, expansion to
+    KV slots) as read in qsa_index_oracle.c.
+
+    q [bs, hi, di] bf16 (index query heads); k_pool [n, di] bf16 (one
+    compressed index key per block row); block_table [bs, max_blocks] int32;
+    req_to_token [bs, max_tokens] int32; ctx_len [bs] int32; weights
+    [bs, hi] float32 or None (all 1).  Returns (sel int32 packed, cu
+    [bs + 1] int32) and, with return_scores, the [bs, max_blocks] float32
+    block scores (NaN past each row's blocks)."""
+    lib = _load()
+    qb = _as_u16(q)
+    bs, hi, di = qb.shape
+    kb = _as_u16(k_pool)
+    assert kb.ndim == 2 and kb.shape[1] == di
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    r2t = np.ascontiguousarray(np.asarray(req_to_token, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(ctx_len, dtype=np.int32))
+    assert bt.shape[0] == bs and r2t.shape[0] == bs and cl.shape == (bs,)
+    w = None if weights is None else _as_f32(weights)
+    if w is not None:
+        assert w.shape == (bs, hi)
+    c = int(compress_ratio)
+    sel = np.empty(bs * (budget + c - 1) + 1, dtype=np.int32)
+    cu = np.empty(bs + 1, dtype=np.int32)
+    scores = np.full((bs, bt.shape[1]), np.nan, dtype=np.float32)
+    rc = lib.oracle_qsa_index(bs, hi, di, _ptr(qb), _ptr(w), _ptr(kb), kb.shape[0], _ptr(bt),
+                              bt.shape[1], _ptr(r2t), r2t.shape[1], _ptr(cl), int(budget), c,
+                              _ptr(sel), _ptr(cu), _ptr(scores))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call: {ERRORS.get(rc, rc)}")
+    out = (sel[: cu[-1]].copy(), cu)
+    return out + (scores,) if return_scores else out
 
 
 def dequant_row(pool, scale, slot: int, g: int, *, fmt: str, group: int = 256):

@@ -224,3 +224,25 @@ def write_batches(rng: np.random.Generator, order: np.ndarray, batches: int) -> 
         return [np.asarray(order)]
     cuts = np.sort(rng.choice(np.arange(1, n), size=min(batches - 1, n - 1), replace=False))
     return np.split(np.asarray(order), cuts)
+
+
+def index_inputs(rng: np.random.Generator, ctx, *, hi: int = 4, di: int = 64, c: int = 4,
+                 max_tokens: int | None = None, weights: bool = True, slots: int = 1 << 20):
+    """Inputs of the indexer step for rows of context lengths ``ctx``: index
+    query heads q [bs, hi, di] and one compressed key per block row of a
+    key pool [bs * max_blocks, di] (bf16 N(0, 1)); a block table that
+    scatters each row's blocks over the pool (a random permutation); a
+    token -> KV slot table per row (distinct slots drawn from [0, slots));
+    head weights U[0.5, 1.5) or None."""
+    bs = len(ctx)
+    max_tokens = max_tokens or max(max(int(t) for t in ctx), 1)
+    max_blocks = max_tokens // c + 1
+    n_kpool = bs * max_blocks
+    q = normal_bf16(rng, (bs, hi, di))
+    k = normal_bf16(rng, (n_kpool, di))
+    bt = rng.permutation(n_kpool).reshape(bs, max_blocks).astype(np.int32)
+    r2t = np.stack([rng.choice(slots, size=max_tokens, replace=False) for _ in range(bs)])
+    w = (rng.random((bs, hi), dtype=np.float32) + np.float32(0.5)) if weights else None
+    return dict(q=q, k_pool=k, block_table=bt, req_to_token=r2t.astype(np.int32),
+                ctx_len=np.asarray(ctx, np.int32), weights=w)
+
