@@ -50,11 +50,12 @@ extern "C" {
 /* Same declaration as in the HIP runtime headers. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define QSA_ABI_VERSION 3
+#define QSA_ABI_VERSION 4
 #define QSA_HEAD_DIM 256
 #define QSA_GQA 12
 #define QSA_MAX_SEL 2055
 #define QSA_MAX_BS 128
+#define QSA_INDEX_MAX_TOKENS 262144 /* the indexer's context capacity per row */
 
 typedef enum qsa_status {
   QSA_OK = 0,
@@ -212,6 +213,61 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
 qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
                                const qsa_tensor *loc, qsa_tiered_pool *pool, hipStream_t stream);
 
+/*
+ * qsa_index -- the indexer step that produces the decode's lists (two
+ * kernel launches on `stream`).  The pages name its parts -- MQA scoring,
+ * an exact top-k and an index expansion with a fixed 256K-token capacity
+ * (page "[Kernel][WIP] Integrate native FlashInfer SM70 batch GDN and QSA
+ * probes", follow-up "device-planned MQA and QSA quality attribution") --
+ * and its row width token_topk + compress_ratio - 1 (page "feat(qsa):
+ * quantized KV pools with dequant-on-gather (fp8/int8/int4)", part 4,
+ * decode routing paragraph); the rest is this library's reading:
+ *
+ *   Row b has T_b = context_lens[b] tokens.  Logical block j < n_b =
+ *   T_b / c (c = compress_ratio) covers tokens j*c .. j*c + c - 1 and has
+ *   one compressed index key, row block_table[b][j] of k_index_pool.  Its
+ *   score is s_j = sum_h w_h (q_h . k_j) over the row's index heads (w_h =
+ *   head_weights[b][h], or 1 without weights), in fp32 in this order: per
+ *   head, a = 0 then a = fma(q_h[d], k_j[d], a) for d = 0, 1, ...; then
+ *   s = 0 and s = fma(w_h, a_h, s) for h = 0, 1, ...; -0 reads as +0.
+ *   The row keeps the K = budget / c blocks with the largest scores (a tie
+ *   goes to the lower block index; every block when n_b <= K), and lists,
+ *   in ascending block order, each kept block's c tokens, then the
+ *   T_b mod c tokens past the last complete block: min(n_b, K)*c +
+ *   T_b mod c entries (at most budget + c - 1), token t written as the KV
+ *   slot req_to_token[b][t].  Rows are packed in order into sel_out, and
+ *   cu_out receives the offsets (the cu_seqlens of qsa_decode).
+ *
+ *   q_index       [bs, hi, di] bf16, 1 <= bs <= 128, 1 <= hi <= 64,
+ *                 di = 64 or 128, rows on 16-byte boundaries
+ *   head_weights  [bs, hi] f32, or NULL
+ *   k_index_pool  [n, di] bf16, rows on 16-byte boundaries
+ *   block_table   [bs, max_blocks] i32 (max_blocks <= 262144)
+ *   req_to_token  [bs, max_tokens] i32 (max_tokens <= 262144)
+ *   context_lens  [bs] i32, read on the device only
+ *   budget, compress_ratio  1 <= c <= 64, budget a multiple of c,
+ *                 budget + c - 1 <= 2055
+ *   sel_out       [>= bs * (budget + c - 1)] i32, written
+ *   cu_out        [bs + 1] i32, written
+ *
+ * Uses the device workspace's score scratch (bs * max_blocks floats),
+ * created on first use outside stream capture; under capture it must have
+ * been reserved with qsa_index_reserve.  A row whose T_b is negative, above
+ * max_tokens or has more blocks than max_blocks lists nothing, and a block
+ * table entry outside [0, n) scores -inf; both set bit 3 of the device
+ * error word.
+ */
+qsa_status qsa_index(const qsa_tensor *q_index, const qsa_tensor *head_weights,
+                     const qsa_tensor *k_index_pool, const qsa_tensor *block_table,
+                     const qsa_tensor *req_to_token, const qsa_tensor *context_lens, int budget,
+                     int compress_ratio, qsa_tensor *sel_out, qsa_tensor *cu_out,
+                     hipStream_t stream);
+
+/* Create (or grow) the current device's indexer score scratch for calls
+ * with up to max_bs rows and max_blocks blocks per row.  Call it before
+ * capturing a graph that contains qsa_index. */
+qsa_status qsa_index_reserve(int max_bs, int max_blocks, hipStream_t stream);
+
 /* Create (or grow) the current device's workspace for calls with up to
  * max_bs rows and the given head layout, and zero its counters.  Call it
  * before capturing a graph that contains qsa_decode.  Synchronises the
@@ -266,7 +322,9 @@ qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream);
 /* Copy the sticky device error word to *host_word (synchronises `stream`).
  * Bit 0: a row's cu_seqlens were out of range or longer than 2055.
  * Bit 1: a slot id was outside [0, slots).
- * Bit 2: a qsa_kv_store slot id was outside [0, slots). */
+ * Bit 2: a qsa_kv_store slot id was outside [0, slots).
+ * Bit 3: a qsa_index row's context length or block table entry was out of
+ *        range. */
 qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream);
 
 int qsa_abi_version(void);

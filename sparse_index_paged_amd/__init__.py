@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     decode,
     decode_tiered,
     get_option,
+    index,
+    index_reserve,
     kv_store,
     kv_store_tiered,
     lib_path,
@@ -32,7 +34,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
+    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
     "ABI_VERSION",

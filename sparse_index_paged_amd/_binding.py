@@ -8,7 +8,7 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "libqsa.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # qsa_dtype
 BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2, I64 = 1, 2, 3, 4, 5, 6, 7, 8
@@ -16,7 +16,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORK
           4: "QSA_ERR_HIP"}
 
 EXPORTS = (
-    "qsa_decode", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_workspace_reserve", "qsa_workspace_reset",
+    "qsa_decode", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_index",
+    "qsa_index_reserve", "qsa_workspace_reserve", "qsa_workspace_reset",
     "qsa_workspace_release", "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
     "qsa_debug_counters", "qsa_debug_read_counters", "qsa_debug_audit_counters",
     "qsa_debug_device_error", "qsa_abi_version",
@@ -76,6 +77,10 @@ def load_library():
     lib.qsa_decode_tiered.argtypes = [T, P(QsaTieredPool), T, T, T, T, ctypes.c_void_p]
     lib.qsa_kv_store_tiered.restype = ctypes.c_int
     lib.qsa_kv_store_tiered.argtypes = [T, T, T, P(QsaTieredPool), ctypes.c_void_p]
+    lib.qsa_index.restype = ctypes.c_int
+    lib.qsa_index.argtypes = [T, T, T, T, T, T, ctypes.c_int, ctypes.c_int, T, T, ctypes.c_void_p]
+    lib.qsa_index_reserve.restype = ctypes.c_int
+    lib.qsa_index_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.qsa_workspace_reserve.restype = ctypes.c_int
     lib.qsa_workspace_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.qsa_workspace_reset.restype = ctypes.c_int
@@ -255,6 +260,35 @@ def kv_store_tiered(k_new, v_new, loc, pool: dict, *, stream=None):
     kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
     _check(lib.qsa_kv_store_tiered(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld),
                                    ctypes.byref(tp), _stream_handle(stream)))
+
+
+def index(q_index, k_index_pool, block_table, req_to_token, context_lens, *, budget: int,
+          compress_ratio: int, head_weights=None, sel_out=None, cu_out=None, stream=None):
+    """The indexer step (two kernel launches on `stream`): per row, the
+    top budget / compress_ratio blocks by MQA score, expanded to KV slots.
+    Returns (sel [bs * (budget + compress_ratio - 1)] int32, whose first
+    cu[-1] entries are the packed lists, cu [bs + 1] int32)."""
+    import torch
+    lib = load_library()
+    bs = q_index.shape[0]
+    dev = q_index.device
+    if sel_out is None:
+        sel_out = torch.empty(bs * (budget + compress_ratio - 1), dtype=torch.int32, device=dev)
+    if cu_out is None:
+        cu_out = torch.empty(bs + 1, dtype=torch.int32, device=dev)
+    qd, kd = describe(q_index), describe(k_index_pool)
+    wd = describe(head_weights) if head_weights is not None else None
+    bd, rd, cd = describe(block_table), describe(req_to_token), describe(context_lens)
+    sd, ud = describe(sel_out), describe(cu_out)
+    _check(lib.qsa_index(ctypes.byref(qd), ctypes.byref(wd) if wd is not None else None,
+                         ctypes.byref(kd), ctypes.byref(bd), ctypes.byref(rd), ctypes.byref(cd),
+                         int(budget), int(compress_ratio), ctypes.byref(sd), ctypes.byref(ud),
+                         _stream_handle(stream)))
+    return sel_out, cu_out
+
+
+def index_reserve(max_bs: int, max_blocks: int, stream=None):
+    _check(load_library().qsa_index_reserve(max_bs, max_blocks, _stream_handle(stream)))
 
 
 def workspace_reserve(max_bs: int, hq: int, hkv: int, stream=None):

@@ -8,7 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("qsa_decode.hip", "qsa_store.hip", "qsa_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("qsa_decode.hip", "qsa_store.hip", "qsa_index.hip", "qsa_api.hip")]
 LIB = os.path.join(PKG, "libqsa.so")
 
 HIPCC_FLAGS = [

@@ -111,6 +111,8 @@ struct Workspace {
   int64_t part_floats = 0;
   uint32_t *words = nullptr;  // [kMaxBs * 2 counters][1 error word]
   int64_t n_ctr = 0;
+  float *iscores = nullptr;   // indexer block scores
+  int64_t iscore_floats = 0;
 };
 
 std::mutex g_ws_mutex;
@@ -152,7 +154,11 @@ qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool al
       return fail(QSA_ERR_HIP, "workspace: hipDeviceSynchronize failed");
     (void)hipFree(ws.part);
     (void)hipFree(ws.words);
+    float *keep = ws.iscores;
+    const int64_t keep_n = ws.iscore_floats;
     ws = Workspace{};
+    ws.iscores = keep;
+    ws.iscore_floats = keep_n;
   }
   void *part = nullptr, *words = nullptr;
   if (hipMalloc(&part, static_cast<size_t>(floats) * sizeof(float)) != hipSuccess)
@@ -169,6 +175,34 @@ qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool al
   if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
     return fail(QSA_ERR_HIP, "workspace: zeroing the counters failed");
   *out = &ws;
+  return QSA_OK;
+}
+
+// The current device's indexer score scratch, holding at least `floats`
+// (the counters and error word are created with it when missing).
+qsa_status ensure_index_scores(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
+                               Workspace **out, const char *fn) {
+  qsa_status st = ensure_workspace(dev, 0, stream, allow_alloc, out, fn);
+  if (st != QSA_OK) return st;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace &ws = g_ws[dev];
+  if (ws.iscore_floats >= floats && (floats == 0 || ws.iscores != nullptr)) return QSA_OK;
+  if (!allow_alloc)
+    return fail(QSA_ERR_WORKSPACE,
+                "%s: the stream is capturing and the device %d index scratch holds %lld floats, "
+                "%lld needed; call qsa_index_reserve before capture", fn, dev,
+                static_cast<long long>(ws.iscore_floats), static_cast<long long>(floats));
+  if (ws.iscores != nullptr) {
+    if (hipDeviceSynchronize() != hipSuccess) return fail(QSA_ERR_HIP, "%s: hipDeviceSynchronize failed", fn);
+    (void)hipFree(ws.iscores);
+    ws.iscores = nullptr;
+    ws.iscore_floats = 0;
+  }
+  void *ptr = nullptr;
+  if (hipMalloc(&ptr, static_cast<size_t>(floats) * sizeof(float)) != hipSuccess)
+    return fail(QSA_ERR_HIP, "%s: hipMalloc of %lld bytes failed", fn, static_cast<long long>(floats * 4));
+  ws.iscores = static_cast<float *>(ptr);
+  ws.iscore_floats = floats;
   return QSA_OK;
 }
 
@@ -721,6 +755,108 @@ qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
   return ok();
 }
 
+qsa_status qsa_index(const qsa_tensor *q_index, const qsa_tensor *head_weights,
+                     const qsa_tensor *k_index_pool, const qsa_tensor *block_table,
+                     const qsa_tensor *req_to_token, const qsa_tensor *context_lens, int budget,
+                     int compress_ratio, qsa_tensor *sel_out, qsa_tensor *cu_out,
+                     hipStream_t stream) {
+  static const char *fn = "qsa_index";
+  qsa_status st;
+  if ((st = check_tensor(q_index, "q_index", QSA_DTYPE_BF16, 3, true, fn)) != QSA_OK) return st;
+  const int64_t bs = q_index->shape[0], hi = q_index->shape[1], di = q_index->shape[2];
+  if (bs < 1 || bs > QSA_MAX_BS)
+    return fail(QSA_ERR_CONTRACT, "%s: bs must be in [1, 128], got %lld", fn, static_cast<long long>(bs));
+  if (hi < 1 || hi > 64)
+    return fail(QSA_ERR_CONTRACT, "%s: index heads must be in [1, 64], got %lld", fn, static_cast<long long>(hi));
+  if (di != 64 && di != 128)
+    return fail(QSA_ERR_CONTRACT, "%s: index head dim must be 64 or 128, got %lld", fn, static_cast<long long>(di));
+  if (!aligned16(q_index->data) || q_index->stride[0] % 8 || q_index->stride[1] % 8)
+    return fail(QSA_ERR_CONTRACT, "%s: q_index rows must start on 16-byte boundaries", fn);
+  if (head_weights != nullptr) {
+    if ((st = check_tensor(head_weights, "head_weights", QSA_DTYPE_F32, 2, true, fn)) != QSA_OK) return st;
+    if (head_weights->shape[0] != bs || head_weights->shape[1] != hi)
+      return fail(QSA_ERR_CONTRACT, "%s: head_weights must be [bs, index heads]", fn);
+  }
+  if ((st = check_tensor(k_index_pool, "k_index_pool", QSA_DTYPE_BF16, 2, true, fn)) != QSA_OK) return st;
+  if (k_index_pool->shape[1] != di)
+    return fail(QSA_ERR_CONTRACT, "%s: k_index_pool rows must hold %lld elements like q_index", fn,
+                static_cast<long long>(di));
+  if (!aligned16(k_index_pool->data) || k_index_pool->stride[0] % 8)
+    return fail(QSA_ERR_CONTRACT, "%s: k_index_pool rows must start on 16-byte boundaries", fn);
+  if ((st = check_tensor(block_table, "block_table", QSA_DTYPE_I32, 2, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(req_to_token, "req_to_token", QSA_DTYPE_I32, 2, true, fn)) != QSA_OK) return st;
+  if ((st = check_tensor(context_lens, "context_lens", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if (block_table->shape[0] != bs || req_to_token->shape[0] != bs || context_lens->shape[0] != bs)
+    return fail(QSA_ERR_CONTRACT, "%s: block_table, req_to_token and context_lens need one row per q_index row", fn);
+  if (req_to_token->shape[1] > QSA_INDEX_MAX_TOKENS)
+    return fail(QSA_ERR_CONTRACT, "%s: req_to_token holds more than %d tokens per row", fn, QSA_INDEX_MAX_TOKENS);
+  const int c = compress_ratio;
+  if (c < 1 || c > 64)
+    return fail(QSA_ERR_CONTRACT, "%s: compress_ratio must be in [1, 64], got %d", fn, c);
+  if (budget < c || budget % c != 0 || budget + c - 1 > QSA_MAX_SEL)
+    return fail(QSA_ERR_CONTRACT, "%s: budget must be a positive multiple of compress_ratio with "
+                "budget + compress_ratio - 1 <= 2055, got budget %d, ratio %d", fn, budget, c);
+  if (block_table->shape[1] > QSA_INDEX_MAX_TOKENS)
+    return fail(QSA_ERR_CONTRACT, "%s: block_table holds more than %d blocks per row", fn, QSA_INDEX_MAX_TOKENS);
+  if ((st = check_tensor(sel_out, "sel_out", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if (sel_out->shape[0] < bs * (budget + c - 1))
+    return fail(QSA_ERR_CONTRACT, "%s: sel_out must hold bs * (budget + compress_ratio - 1) = %lld entries", fn,
+                static_cast<long long>(bs * (budget + c - 1)));
+  if ((st = check_tensor(cu_out, "cu_out", QSA_DTYPE_I32, 1, true, fn)) != QSA_OK) return st;
+  if (cu_out->shape[0] != bs + 1)
+    return fail(QSA_ERR_CONTRACT, "%s: cu_out must have bs + 1 entries", fn);
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  const int64_t max_blocks = block_table->shape[1];
+  Workspace *ws = nullptr;
+  if ((st = ensure_index_scores(dev, bs * max_blocks, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK)
+    return st;
+
+  qsa::IndexParams p{};
+  p.q = static_cast<const __bf16 *>(q_index->data);
+  p.q_sb = q_index->stride[0];
+  p.q_sh = q_index->stride[1];
+  p.w = head_weights ? static_cast<const float *>(head_weights->data) : nullptr;
+  p.w_sb = head_weights ? head_weights->stride[0] : 0;
+  p.k = static_cast<const __bf16 *>(k_index_pool->data);
+  p.k_ss = k_index_pool->stride[0];
+  p.n_k = k_index_pool->shape[0];
+  p.bt = static_cast<const int32_t *>(block_table->data);
+  p.bt_sb = block_table->stride[0];
+  p.max_blocks = static_cast<int>(max_blocks);
+  p.r2t = static_cast<const int32_t *>(req_to_token->data);
+  p.r2t_sb = req_to_token->stride[0];
+  p.max_tokens = static_cast<int>(req_to_token->shape[1]);
+  p.ctx = static_cast<const int32_t *>(context_lens->data);
+  p.bs = static_cast<int>(bs);
+  p.hi = static_cast<int>(hi);
+  p.di = static_cast<int>(di);
+  p.budget = budget;
+  p.c = c;
+  p.scores = ws->iscores;
+  p.sel = static_cast<int32_t *>(sel_out->data);
+  p.cu = static_cast<int32_t *>(cu_out->data);
+  p.err = ws->words + kCtrWords;
+  const hipError_t e = qsa::launch_index(p, stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_index_reserve(int max_bs, int max_blocks, hipStream_t stream) {
+  static const char *fn = "qsa_index_reserve";
+  if (max_bs < 1 || max_bs > QSA_MAX_BS) return fail(QSA_ERR_CONTRACT, "%s: max_bs must be in [1, 128]", fn);
+  if (max_blocks < 0 || max_blocks > QSA_INDEX_MAX_TOKENS)
+    return fail(QSA_ERR_CONTRACT, "%s: max_blocks must be in [0, %d]", fn, QSA_INDEX_MAX_TOKENS);
+  if (stream_capturing(stream)) return fail(QSA_ERR_WORKSPACE, "%s: called while the stream is capturing", fn);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  Workspace *ws = nullptr;
+  qsa_status st = ensure_index_scores(dev, static_cast<int64_t>(max_bs) * max_blocks, stream, true, &ws, fn);
+  return st == QSA_OK ? ok() : st;
+}
+
 qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream) {
   if (max_bs < 1 || max_bs > QSA_MAX_BS)
     return fail(QSA_ERR_CONTRACT, "qsa_workspace_reserve: max_bs must be in [1, 128]");
@@ -761,6 +897,7 @@ qsa_status qsa_workspace_release(void) {
     if (hipSetDevice(dev) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
       (void)hipFree(ws.part);
       (void)hipFree(ws.words);
+      if (ws.iscores) (void)hipFree(ws.iscores);
     }
     ws = Workspace{};
   }
@@ -774,7 +911,7 @@ int64_t qsa_workspace_bytes(void) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   const Workspace &ws = g_ws[dev];
   if (ws.words == nullptr) return 0;
-  return ws.part_floats * 4 + (kCtrWords + 1) * 4;
+  return ws.part_floats * 4 + (kCtrWords + 1) * 4 + ws.iscore_floats * 4;
 }
 
 qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n) {

@@ -1,0 +1,253 @@
+// qsa_index.hip -- the QSA indexer step on gfx950: block scores, exact
+// top-k, expansion of the chosen blocks to KV slots.
+//
+// What it computes is stated in include/qsa.h (qsa_index).  The pages name
+// the step's parts -- MQA scoring, an exact top-k and an index expansion,
+// with a fixed 256K-token capacity (page "[Kernel][WIP] Integrate native
+// FlashInfer SM70 batch GDN and QSA probes", follow-up "device-planned MQA
+// and QSA quality attribution") -- and the row width token_topk +
+// compress_ratio - 1 (page "feat(qsa): quantized KV pools with
+// dequant-on-gather (fp8/int8/int4)", part 4, decode routing paragraph).
+//
+// Two launches:
+//   * scores: one lane per (row, block).  The block's key row is held in
+//     registers and every index head's query comes from LDS (a broadcast
+//     read), so each key byte is read once for all heads.  The score is
+//     evaluated in the order the contract fixes -- per head one fused
+//     multiply-add per element in element order, then the weighted heads in
+//     head order -- so that the top-k decisions are reproducible exactly.
+//   * select: one 1024-thread workgroup per row.  Its offset in the packed
+//     output depends only on the context lengths, so every workgroup
+//     computes its own; an exact radix select (4 passes of 8 bits over
+//     order-preserving 32-bit keys, histograms in LDS) finds the K-th
+//     largest key, and one pass in ascending block order keeps the blocks
+//     above it plus the lowest-indexed blocks equal to it (wave ballots
+//     give each thread its rank), expanding each kept block to its c KV
+//     slots.  The tokens past the last complete block follow.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
+constexpr int kMaxIndexHeads = 64;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Tokens a row lists, from its context length alone (0 for a length
+// outside the contract).
+__device__ __forceinline__ int row_length(const IndexParams &p, int32_t t) {
+  if (t < 0 || t > p.max_tokens || t / p.c > p.max_blocks) return 0;
+  const int n = t / p.c, k = p.budget / p.c;
+  return (n < k ? n : k) * p.c + t % p.c;
+}
+
+template <int DI>
+__global__ void __launch_bounds__(kScoreThreads) qsa_index_score_kernel(const IndexParams p) {
+  constexpr int NC = DI / 8;  // 16-byte chunks per row
+  const int b = blockIdx.y;
+  const int32_t t = p.ctx[b];
+  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
+  const int n = row_ok ? t / p.c : 0;
+  if (static_cast<int>(blockIdx.x) * kScoreThreads >= n) return;  // uniform
+
+  __shared__ uint4 qs[kMaxIndexHeads * NC];
+  __shared__ float ws[kMaxIndexHeads];
+  for (int i = threadIdx.x; i < p.hi * NC; i += kScoreThreads) {
+    const int h = i / NC, c8 = i - h * NC;
+    qs[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[c8];
+  }
+  if (static_cast<int>(threadIdx.x) < p.hi) ws[threadIdx.x] = p.w ? p.w[b * p.w_sb + threadIdx.x] : 1.0f;
+  __syncthreads();
+
+  const int j = blockIdx.x * kScoreThreads + threadIdx.x;
+  if (j >= n) return;
+  const int32_t row = p.bt[b * p.bt_sb + j];
+  float s;
+  if (row < 0 || row >= p.n_k) {
+    s = -INFINITY;
+    atomicOr(p.err, kErrIndexRow);
+  } else {
+    uint4 kr[NC];
+    const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + static_cast<int64_t>(row) * p.k_ss);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) kr[i] = kp[i];
+    s = 0.0f;
+    for (int h = 0; h < p.hi; ++h) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const uint4 qv = qs[h * NC + i];
+        a = __builtin_fmaf(bf_lo(qv.x), bf_lo(kr[i].x), a);
+        a = __builtin_fmaf(bf_hi(qv.x), bf_hi(kr[i].x), a);
+        a = __builtin_fmaf(bf_lo(qv.y), bf_lo(kr[i].y), a);
+        a = __builtin_fmaf(bf_hi(qv.y), bf_hi(kr[i].y), a);
+        a = __builtin_fmaf(bf_lo(qv.z), bf_lo(kr[i].z), a);
+        a = __builtin_fmaf(bf_hi(qv.z), bf_hi(kr[i].z), a);
+        a = __builtin_fmaf(bf_lo(qv.w), bf_lo(kr[i].w), a);
+        a = __builtin_fmaf(bf_hi(qv.w), bf_hi(kr[i].w), a);
+      }
+      s = __builtin_fmaf(ws[h], a, s);
+    }
+    s = s + 0.0f;  // -0 -> +0
+  }
+  p.scores[static_cast<int64_t>(b) * p.max_blocks + j] = s;
+}
+
+// Order-preserving 32-bit key of a float (larger float, larger key).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of set bits of m below this lane.
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+__global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const IndexParams p) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ uint32_t hist[256];
+  __shared__ int32_t wsum[2][kSelectWaves];
+  __shared__ uint32_t s_prefix;
+  __shared__ int32_t s_krem;
+
+  // ---- this row's offset in the packed output
+  int part = 0;
+  for (int i = tid; i < b; i += kSelectThreads) part += row_length(p, p.ctx[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) wsum[0][wave] = part;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < kSelectWaves; ++w) off += wsum[0][w];
+  const int32_t t = p.ctx[b];
+  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
+  const int len = row_length(p, t);
+  if (tid == 0) {
+    p.cu[b + 1] = off + len;
+    if (b == 0) p.cu[0] = 0;
+    if (!row_ok) atomicOr(p.err, kErrIndexRow);
+  }
+  if (!row_ok) return;  // uniform; the row lists nothing
+  const int n = t / p.c, k = p.budget / p.c, c = p.c;
+  int32_t *out = p.sel + off;
+  const int32_t *r2t = p.r2t + b * p.r2t_sb;
+  if (n <= k) {  // every block is taken: the row is every token in order
+    for (int i = tid; i < t; i += kSelectThreads) out[i] = r2t[i];
+    return;
+  }
+  const float *sc = p.scores + static_cast<int64_t>(b) * p.max_blocks;
+
+  // ---- radix select of the k-th largest key
+  uint32_t prefix = 0, mask = 0;
+  int krem = k;  // keys still to take among those matching `prefix` under `mask`
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += kSelectThreads) {
+      const uint32_t key = order_key(sc[j]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 255 - 4l .. 252 - 4l (from the top down)
+      uint32_t h4[4];
+      int c4 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h4[i] = hist[255 - 4 * lane - i];
+        c4 += static_cast<int>(h4[i]);
+      }
+      int incl = c4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      const int excl = incl - c4;
+      if (excl < krem && krem <= incl) {
+        int run = excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (run + static_cast<int>(h4[i]) >= krem) {
+            s_prefix = prefix | (static_cast<uint32_t>(255 - 4 * lane - i) << shift);
+            s_krem = krem - run;
+            break;
+          }
+          run += static_cast<int>(h4[i]);
+        }
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    krem = s_krem;
+    mask |= 0xFFu << shift;
+  }
+  const uint32_t thr = prefix;  // the k-th largest key
+  const int need_eq = krem;     // keys equal to thr that are taken (the lowest-indexed ones)
+
+  // ---- keep, in ascending block order, the blocks above thr and the
+  // first need_eq blocks equal to it; block of rank r fills out[r*c ..]
+  int gt_run = 0, eq_run = 0;
+  for (int j0 = 0; j0 < n; j0 += kSelectThreads) {
+    const int j = j0 + tid;
+    const uint32_t key = j < n ? order_key(sc[j]) : 0u;
+    const bool gt = j < n && key > thr;
+    const bool eq = j < n && key == thr;
+    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+    if (lane == 0) {
+      wsum[0][wave] = __popcll(bgt);
+      wsum[1][wave] = __popcll(beq);
+    }
+    __syncthreads();
+    int gt_before = gt_run + bits_below(bgt), eq_before = eq_run + bits_below(beq);
+    int gt_all = 0, eq_all = 0;
+#pragma unroll
+    for (int w = 0; w < kSelectWaves; ++w) {
+      if (w < wave) {
+        gt_before += wsum[0][w];
+        eq_before += wsum[1][w];
+      }
+      gt_all += wsum[0][w];
+      eq_all += wsum[1][w];
+    }
+    if (gt || (eq && eq_before < need_eq)) {
+      const int rank = gt_before + (eq_before < need_eq ? eq_before : need_eq);
+      if (rank < k)  // always true (k keys are kept); keeps every write inside the row
+        for (int e = 0; e < c; ++e) out[rank * c + e] = r2t[j * c + e];
+    }
+    gt_run += gt_all;
+    eq_run += eq_all;
+    __syncthreads();
+  }
+  // ---- the tokens past the last complete block
+  for (int i = tid; i < t - n * c; i += kSelectThreads) out[k * c + i] = r2t[n * c + i];
+}
+
+}  // namespace
+
+hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
+  const dim3 sgrid(static_cast<unsigned>((p.max_blocks + kScoreThreads - 1) / kScoreThreads),
+                   static_cast<unsigned>(p.bs));
+  if (p.max_blocks > 0) {
+    switch (p.di) {
+      case 64: hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(kScoreThreads), 0, stream, p); break;
+      case 128: hipLaunchKernelGGL(qsa_index_score_kernel<128>, sgrid, dim3(kScoreThreads), 0, stream, p); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  hipLaunchKernelGGL(qsa_index_select_kernel, dim3(static_cast<unsigned>(p.bs)), dim3(kSelectThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -95,6 +95,36 @@ struct StoreParams {
   uint32_t ring_mask;
 };
 
+constexpr uint32_t kErrIndexRow = 8u;  // an indexer row's context length / block table entry out of range
+
+// One indexer call: block scores of every row, then per row the top
+// budget / c blocks, expanded to KV slots and packed.
+struct IndexParams {
+  const __bf16 *q;          // [bs, hi, di]
+  int64_t q_sb, q_sh;       // element strides
+  const float *w;           // [bs, hi] or null (all 1)
+  int64_t w_sb;
+  const __bf16 *k;          // key pool [n_k, di]
+  int64_t k_ss;             // element stride between key rows
+  int64_t n_k;
+  const int32_t *bt;        // block table [bs, max_blocks]
+  int64_t bt_sb;
+  int max_blocks;
+  const int32_t *r2t;       // token -> KV slot [bs, max_tokens]
+  int64_t r2t_sb;
+  int max_tokens;
+  const int32_t *ctx;       // [bs] context lengths
+  int bs, hi, di;
+  int budget, c;
+  float *scores;            // scratch [bs, max_blocks]
+  int32_t *sel;             // packed output
+  int32_t *cu;              // [bs + 1]
+  uint32_t *err;
+};
+
+// Score kernel then select/expand kernel on `stream`.
+hipError_t launch_index(const IndexParams &p, hipStream_t stream);
+
 // Launch the decode kernel for one call (grid = 8 * ceil(npairs/8) * nsplit).
 hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream);
 

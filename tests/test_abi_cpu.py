@@ -49,7 +49,7 @@ def test_header_compiles_as_c():
 
 
 def test_abi_version():
-    assert qsa.abi_version() == B.ABI_VERSION == 3
+    assert qsa.abi_version() == B.ABI_VERSION == 4
 
 
 def test_plan_and_options():
@@ -286,3 +286,47 @@ def test_tiered_query_and_store_shape_rejections():
     assert "q is NULL" in lib.qsa_last_error().decode()
     assert lib.qsa_kv_store_tiered(None, None, None, None, None) == 2
     assert "pool is NULL" in lib.qsa_last_error().decode()
+
+
+# ---- indexer ----
+
+def _index(bs=2, hi=4, di=64, n_k=100, max_blocks=32, max_tokens=128, budget=64, c=4,
+           q_dtype=B.BF16, weights="f32", sel_len=None, cu_len=None, k_di=None, bt_rows=None,
+           q_data=FAKE):
+    lib = qsa.load_library()
+    q = _t((bs, hi, di), q_dtype, data=q_data)
+    w = _t((bs, hi), B.F32 if weights == "f32" else B.BF16) if weights else None
+    k = _t((n_k, k_di or di), B.BF16)
+    bt = _t((bt_rows or bs, max_blocks), B.I32)
+    r2t = _t((bs, max_tokens), B.I32)
+    cl = _t((bs,), B.I32)
+    sel = _t((sel_len if sel_len is not None else bs * (budget + c - 1),), B.I32)
+    cu = _t((cu_len or bs + 1,), B.I32)
+    st = lib.qsa_index(ctypes.byref(q), ctypes.byref(w) if w is not None else None, ctypes.byref(k),
+                       ctypes.byref(bt), ctypes.byref(r2t), ctypes.byref(cl), budget, c,
+                       ctypes.byref(sel), ctypes.byref(cu), None)
+    return st, lib.qsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,match", [
+    (dict(bs=129), r"bs must be in \[1, 128\]"),
+    (dict(hi=65), r"index heads must be in \[1, 64\]"),
+    (dict(di=96), "index head dim must be 64 or 128"),
+    (dict(q_dtype=B.F16), "q_index must be bf16"),
+    (dict(weights="bf16"), "head_weights must be f32"),
+    (dict(k_di=128), "k_index_pool rows must hold 64 elements"),
+    (dict(bt_rows=3), "one row per q_index row"),
+    (dict(max_tokens=262145), "more than 262144 tokens"),
+    (dict(c=0), r"compress_ratio must be in \[1, 64\]"),
+    (dict(budget=66, c=4), "budget must be a positive multiple"),
+    (dict(budget=2048, c=16), r"budget \+ compress_ratio - 1 <= 2055"),
+    (dict(sel_len=10), "sel_out must hold"),
+    (dict(cu_len=5), "cu_out must have bs \\+ 1"),
+    (dict(q_data=FAKE + 8), "16-byte boundaries"),
+])
+def test_index_contract_rejections(kwargs, match):
+    st, msg = _index(**kwargs)
+    assert st == 1, (st, msg)
+    assert re.search(match, msg), msg
+    assert msg.startswith("qsa_index")
+
