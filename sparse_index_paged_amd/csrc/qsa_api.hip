@@ -778,6 +778,8 @@ qsa_status qsa_index(const qsa_tensor *q_index, const qsa_tensor *head_weights,
       return fail(QSA_ERR_CONTRACT, "%s: head_weights must be [bs, index heads]", fn);
   }
   if ((st = check_tensor(k_index_pool, "k_index_pool", QSA_DTYPE_BF16, 2, true, fn)) != QSA_OK) return st;
+  if (k_index_pool->shape[0] < 1)
+    return fail(QSA_ERR_CONTRACT, "%s: k_index_pool holds no rows", fn);
   if (k_index_pool->shape[1] != di)
     return fail(QSA_ERR_CONTRACT, "%s: k_index_pool rows must hold %lld elements like q_index", fn,
                 static_cast<long long>(di));

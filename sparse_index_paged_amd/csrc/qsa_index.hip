@@ -10,12 +10,13 @@
 // dequant-on-gather (fp8/int8/int4)", part 4, decode routing paragraph).
 //
 // Two launches:
-//   * scores: one lane per (row, block).  The block's key row is held in
-//     registers and every index head's query comes from LDS (a broadcast
-//     read), so each key byte is read once for all heads.  The score is
-//     evaluated in the order the contract fixes -- per head one fused
-//     multiply-add per element in element order, then the weighted heads in
-//     head order -- so that the top-k decisions are reproducible exactly.
+//   * scores: a workgroup per 64 blocks of a row.  A lane holds its block's
+//     key row in registers; the heads are spread over the 4 waves, 8
+//     independent dot products per lane at a time, with the queries read
+//     from LDS (broadcast).  The score is evaluated in the order the
+//     contract fixes -- per head one fused multiply-add per element in
+//     element order, then the weighted heads in head order -- so that the
+//     top-k decisions are reproducible exactly.
 //   * select: one 1024-thread workgroup per row.  Its offset in the packed
 //     output depends only on the context lengths, so every workgroup
 //     computes its own; an exact radix select (4 passes of 8 bits over
@@ -33,6 +34,7 @@ constexpr int kScoreThreads = 256;
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kMaxIndexHeads = 64;
+constexpr int kMaxRegKeys = 16;  // keys per thread held in registers by the select kernel
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -45,56 +47,85 @@ __device__ __forceinline__ int row_length(const IndexParams &p, int32_t t) {
   return (n < k ? n : k) * p.c + t % p.c;
 }
 
+// A workgroup scores 64 consecutive blocks of one row: lane l of every wave
+// takes block 64*blockIdx.x + l, and wave w the heads w, w + 4, ..., in
+// groups of 8 independent dot products (each one a fused multiply-add chain
+// in element order).  The row's queries are converted to fp32 once into
+// LDS (read back as broadcasts, 4 elements per read), and each key element
+// is converted once for 8 heads.  The per-head results meet in LDS, where
+// the first wave adds them up in head order.
 template <int DI>
 __global__ void __launch_bounds__(kScoreThreads) qsa_index_score_kernel(const IndexParams p) {
-  constexpr int NC = DI / 8;  // 16-byte chunks per row
+  constexpr int NC = DI / 8;  // 16-byte chunks of a bf16 row
+  constexpr int kWaves = kScoreThreads / 64;
+  constexpr int kGroup = 8;   // dot products in flight per lane
   const int b = blockIdx.y;
   const int32_t t = p.ctx[b];
   const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
   const int n = row_ok ? t / p.c : 0;
-  if (static_cast<int>(blockIdx.x) * kScoreThreads >= n) return;  // uniform
+  if (static_cast<int>(blockIdx.x) * 64 >= n) return;  // uniform
 
-  __shared__ uint4 qs[kMaxIndexHeads * NC];
-  __shared__ float ws[kMaxIndexHeads];
+  __shared__ float4 qf[kMaxIndexHeads * DI / 4];   // [hi][DI] fp32
+  __shared__ float dots[kMaxIndexHeads][64];
   for (int i = threadIdx.x; i < p.hi * NC; i += kScoreThreads) {
     const int h = i / NC, c8 = i - h * NC;
-    qs[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[c8];
+    const uint4 v = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[c8];
+    qf[2 * i] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+    qf[2 * i + 1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
   }
-  if (static_cast<int>(threadIdx.x) < p.hi) ws[threadIdx.x] = p.w ? p.w[b * p.w_sb + threadIdx.x] : 1.0f;
   __syncthreads();
 
-  const int j = blockIdx.x * kScoreThreads + threadIdx.x;
-  if (j >= n) return;
-  const int32_t row = p.bt[b * p.bt_sb + j];
-  float s;
-  if (row < 0 || row >= p.n_k) {
-    s = -INFINITY;
-    atomicOr(p.err, kErrIndexRow);
-  } else {
-    uint4 kr[NC];
-    const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + static_cast<int64_t>(row) * p.k_ss);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int j = blockIdx.x * 64 + lane;
+  const bool live = j < n;
+  const int32_t row = live ? p.bt[b * p.bt_sb + j] : 0;
+  const bool row_in = row >= 0 && row < p.n_k;
+  if (live && !row_in && wave == 0) atomicOr(p.err, kErrIndexRow);
+  uint4 kr[NC];
+  const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + static_cast<int64_t>(row_in ? row : 0) * p.k_ss);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) kr[i] = kp[i];
-    s = 0.0f;
-    for (int h = 0; h < p.hi; ++h) {
-      float a = 0.0f;
+  for (int i = 0; i < NC; ++i) kr[i] = kp[i];
+
+  for (int h0 = wave; h0 < p.hi; h0 += kWaves * kGroup) {
+    float a[kGroup];
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const uint4 qv = qs[h * NC + i];
-        a = __builtin_fmaf(bf_lo(qv.x), bf_lo(kr[i].x), a);
-        a = __builtin_fmaf(bf_hi(qv.x), bf_hi(kr[i].x), a);
-        a = __builtin_fmaf(bf_lo(qv.y), bf_lo(kr[i].y), a);
-        a = __builtin_fmaf(bf_hi(qv.y), bf_hi(kr[i].y), a);
-        a = __builtin_fmaf(bf_lo(qv.z), bf_lo(kr[i].z), a);
-        a = __builtin_fmaf(bf_hi(qv.z), bf_hi(kr[i].z), a);
-        a = __builtin_fmaf(bf_lo(qv.w), bf_lo(kr[i].w), a);
-        a = __builtin_fmaf(bf_hi(qv.w), bf_hi(kr[i].w), a);
+    for (int u = 0; u < kGroup; ++u) a[u] = 0.0f;
+    // heads h0, h0 + 4, ..., (those < hi)
+    const int nh = min(kGroup, (p.hi - h0 + kWaves - 1) / kWaves);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float kf[8] = {bf_lo(kr[i].x), bf_hi(kr[i].x), bf_lo(kr[i].y), bf_hi(kr[i].y),
+                           bf_lo(kr[i].z), bf_hi(kr[i].z), bf_lo(kr[i].w), bf_hi(kr[i].w)};
+#pragma unroll
+      for (int u = 0; u < kGroup; ++u) {
+        if (u < nh) {
+          const float4 q0 = qf[((h0 + kWaves * u) * DI) / 4 + 2 * i];
+          const float4 q1 = qf[((h0 + kWaves * u) * DI) / 4 + 2 * i + 1];
+          a[u] = __builtin_fmaf(q0.x, kf[0], a[u]);
+          a[u] = __builtin_fmaf(q0.y, kf[1], a[u]);
+          a[u] = __builtin_fmaf(q0.z, kf[2], a[u]);
+          a[u] = __builtin_fmaf(q0.w, kf[3], a[u]);
+          a[u] = __builtin_fmaf(q1.x, kf[4], a[u]);
+          a[u] = __builtin_fmaf(q1.y, kf[5], a[u]);
+          a[u] = __builtin_fmaf(q1.z, kf[6], a[u]);
+          a[u] = __builtin_fmaf(q1.w, kf[7], a[u]);
+        }
       }
-      s = __builtin_fmaf(ws[h], a, s);
     }
-    s = s + 0.0f;  // -0 -> +0
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      if (u < nh) dots[h0 + kWaves * u][lane] = a[u];
   }
-  p.scores[static_cast<int64_t>(b) * p.max_blocks + j] = s;
+  __syncthreads();
+  if (wave == 0 && live) {
+    float s = 0.0f;
+    for (int h = 0; h < p.hi; ++h) {
+      const float wh = p.w ? p.w[b * p.w_sb + h] : 1.0f;
+      s = __builtin_fmaf(wh, dots[h][lane], s);
+    }
+    p.scores[static_cast<int64_t>(b) * p.max_blocks + j] = row_in ? s + 0.0f : -INFINITY;  // -0 -> +0
+  }
 }
 
 // Order-preserving 32-bit key of a float (larger float, larger key).
@@ -109,6 +140,10 @@ __device__ __forceinline__ int bits_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
+// KEYS_IN_REGS: the row's keys (at most 16 per thread, 16,384 blocks) are
+// loaded once into registers for all passes; otherwise every pass reads the
+// scores again.
+template <bool KEYS_IN_REGS>
 __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const IndexParams p) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -146,6 +181,32 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
     return;
   }
   const float *sc = p.scores + static_cast<int64_t>(b) * p.max_blocks;
+  constexpr int kRegKeys = KEYS_IN_REGS ? kMaxRegKeys : 1;
+  uint32_t keys[kRegKeys];
+  if constexpr (KEYS_IN_REGS) {
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const int j = i * kSelectThreads + tid;
+      keys[i] = (j < n) ? order_key(sc[j]) : 0u;
+    }
+  }
+  const int nchunk = (n + kSelectThreads - 1) / kSelectThreads;
+  // body(j, key) for this thread's block j = i * kSelectThreads + tid of
+  // every chunk i < nchunk in order (key 0 when j >= n)
+  auto each_chunk = [&](auto &&body) {
+    if constexpr (KEYS_IN_REGS) {
+#pragma unroll
+      for (int i = 0; i < kRegKeys; ++i) {
+        if (i >= nchunk) break;  // uniform
+        body(i * kSelectThreads + tid, keys[i]);
+      }
+    } else {
+      for (int i = 0; i < nchunk; ++i) {
+        const int j = i * kSelectThreads + tid;
+        body(j, j < n ? order_key(sc[j]) : 0u);
+      }
+    }
+  };
 
   // ---- radix select of the k-th largest key
   uint32_t prefix = 0, mask = 0;
@@ -153,10 +214,9 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
   for (int shift = 24; shift >= 0; shift -= 8) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kSelectThreads) {
-      const uint32_t key = order_key(sc[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
+    each_chunk([&](int j, uint32_t key) {
+      if (j < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    });
     __syncthreads();
     if (wave == 0) {
       // lane l holds bins 255 - 4l .. 252 - 4l (from the top down)
@@ -198,9 +258,7 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
   // ---- keep, in ascending block order, the blocks above thr and the
   // first need_eq blocks equal to it; block of rank r fills out[r*c ..]
   int gt_run = 0, eq_run = 0;
-  for (int j0 = 0; j0 < n; j0 += kSelectThreads) {
-    const int j = j0 + tid;
-    const uint32_t key = j < n ? order_key(sc[j]) : 0u;
+  each_chunk([&](int j, uint32_t key) {
     const bool gt = j < n && key > thr;
     const bool eq = j < n && key == thr;
     const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
@@ -228,7 +286,7 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
     gt_run += gt_all;
     eq_run += eq_all;
     __syncthreads();
-  }
+  });
   // ---- the tokens past the last complete block
   for (int i = tid; i < t - n * c; i += kSelectThreads) out[k * c + i] = r2t[n * c + i];
 }
@@ -236,8 +294,7 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
 }  // namespace
 
 hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
-  const dim3 sgrid(static_cast<unsigned>((p.max_blocks + kScoreThreads - 1) / kScoreThreads),
-                   static_cast<unsigned>(p.bs));
+  const dim3 sgrid(static_cast<unsigned>((p.max_blocks + 63) / 64), static_cast<unsigned>(p.bs));
   if (p.max_blocks > 0) {
     switch (p.di) {
       case 64: hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(kScoreThreads), 0, stream, p); break;
@@ -245,8 +302,12 @@ hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
       default: return hipErrorInvalidValue;
     }
   }
-  hipLaunchKernelGGL(qsa_index_select_kernel, dim3(static_cast<unsigned>(p.bs)), dim3(kSelectThreads), 0,
-                     stream, p);
+  if (p.max_blocks <= kMaxRegKeys * kSelectThreads)
+    hipLaunchKernelGGL(qsa_index_select_kernel<true>, dim3(static_cast<unsigned>(p.bs)), dim3(kSelectThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(qsa_index_select_kernel<false>, dim3(static_cast<unsigned>(p.bs)), dim3(kSelectThreads), 0,
+                       stream, p);
   return hipGetLastError();
 }
 
