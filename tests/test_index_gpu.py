@@ -180,3 +180,49 @@ def test_graph_replay_with_changing_lengths():
         assert torch.equal(out.view(torch.int16), oe.view(torch.int16)), f"replay {rep}"
         assert torch.equal(lse.view(torch.int32), le.view(torch.int32)), f"replay {rep}"
         say(f"  replay {rep}: lists {int(ref_cu[-1])} entries")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_outputs_are_bitwise_invariant_under_kv_relocation(fmt):
+    """Moving every token's K/V to other physical slots (a relocation, with
+    req_to_token rewritten to match) leaves indexer + decode outputs bitwise
+    unchanged: the lists come out in logical order and the decode's
+    arithmetic depends only on list order and the K/V values -- the
+    property the pages' canonical-order planner restores for their path
+    (page "[Kernel][WIP] Integrate native FlashInfer SM70 batch GDN and QSA
+    probes", follow-up "stable planning": twelve physical relocations
+    bitwise identical)."""
+    rng = np.random.default_rng(770)
+    bs, slots = 16, 65536
+    ctx = rng.integers(2000, 12000, size=bs)
+    inp = synth.index_inputs(rng, ctx, hi=8, di=128, c=4, slots=slots)
+    k_log = synth.normal_bf16(rng, (slots, 2, 256))       # K/V by the slot ids of req_to_token
+    v_log = synth.normal_bf16(rng, (slots, 2, 256))
+    q = synth.normal_bf16(rng, (bs, 24, 256)).cuda()
+    outs = []
+    for reloc in range(3):
+        perm = np.arange(slots) if reloc == 0 else rng.permutation(slots)   # old slot -> new slot
+        kp = torch.empty_like(k_log)
+        vp = torch.empty_like(v_log)
+        kp[torch.from_numpy(perm)] = k_log
+        vp[torch.from_numpy(perm)] = v_log
+        d = to_dev(dict(inp, req_to_token=perm[inp["req_to_token"]].astype(np.int32)))
+        sel, cu = gpu_index(d, 2048, 4)
+        kw = {}
+        kd, vd = kp.cuda(), vp.cuda()
+        if fmt == "fp8":
+            kc = torch.empty((slots, 2, 256), dtype=torch.uint8, device="cuda")
+            vc = torch.empty_like(kc)
+            ks = torch.empty((slots, 2, 1), dtype=torch.float32, device="cuda")
+            vs = torch.empty_like(ks)
+            qsa.kv_store(kd, vd, torch.arange(slots, dtype=torch.int32, device="cuda"), kc, vc,
+                         kv_format="fp8", k_scale=ks, v_scale=vs)
+            kd, vd = kc, vc
+            kw = dict(kv_format="fp8", k_scale=ks, v_scale=vs)
+        out, lse = qsa.decode(q, kd, vd, sel, cu, **kw)
+        torch.cuda.synchronize()
+        say(f"  {fmt} relocation {reloc}: {int(cu[-1])} entries")
+        outs.append((out.clone(), lse.clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l.view(torch.int32), outs[0][1].view(torch.int32))
