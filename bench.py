@@ -61,6 +61,22 @@ def committed_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "qsa_decode_bs128_tp1_bf16_counters.md")
+
+
+def committed_mfma_busy():
+    """MFMA busy share (%) from the committed shader-counter summary of the
+    current kernel source, or None if absent / taken on another version."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    sha = re.search(r"Kernel source sha256\[:16\] = `([0-9a-f]+)`", text)
+    busy = re.search(r"MFMA busy share = .*?= ([0-9.]+) %", text, re.S)
+    if not sha or not busy or sha.group(1) != kernel_sha():
+        return None
+    return float(busy.group(1))
+
+
 def gathered_bytes(lengths, hkv: int, row_bytes: int = 512) -> int:
     return int(sum(int(x) for x in lengths)) * hkv * 2 * row_bytes
 
@@ -594,6 +610,7 @@ def main():
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "mfma_busy_pct": committed_mfma_busy() if fmt == "bf16" else None,
             "algorithmic_bytes_per_launch": b_kv,
             "kernel": f"qsa_decode_kernel<{fmt}>",
         },
