@@ -37,6 +37,20 @@
  *     cu_seqlens entry outside [0, n_sel], a slot id outside [0, slots))
  *     never fault: the offending row's out/lse are written as NaN and a bit
  *     is set in a sticky device error word (qsa_debug_device_error).
+ *   - Workspaces: the library owns the device memory the kernels use beyond
+ *     their arguments (split partials, split counters that are zero between
+ *     calls, the error word, the indexer's block scores).  Each device has
+ *     one shared workspace; qsa_workspace_attach gives a stream a private
+ *     one.  A call uses the workspace of its stream: the private one if the
+ *     stream has one, else the shared one.  Calls that use the same
+ *     workspace must not run concurrently, so concurrent streams each need
+ *     a private workspace.  Outside stream capture a workspace is created
+ *     or grown on first use; under capture it must already be large enough
+ *     (qsa_workspace_reserve / qsa_index_reserve on the capturing stream,
+ *     QSA_ERR_WORKSPACE otherwise).  The error word is per workspace.
+ *     (Page "[Kernel][WIP] Integrate native FlashInfer SM70 batch GDN and
+ *     QSA probes", change summary: scratch stays local to the call rather
+ *     than shared between callers; here a stream's own workspace is that.)
  */
 #ifndef QSA_H_
 #define QSA_H_
@@ -50,7 +64,7 @@ extern "C" {
 /* Same declaration as in the HIP runtime headers. */
 typedef struct ihipStream_t *hipStream_t;
 
-#define QSA_ABI_VERSION 4
+#define QSA_ABI_VERSION 5
 #define QSA_HEAD_DIM 256
 #define QSA_GQA 12
 #define QSA_MAX_SEL 2055
@@ -143,11 +157,8 @@ typedef struct qsa_tiered_pool {
  *   lse         [bs, Hq] fp32, fully overwritten.
  *   stream      HIP stream the kernel is enqueued on (NULL = default).
  *
- * Uses the calling device's workspace (split partials + counters); it is
- * created on first use outside stream capture.  Under capture a workspace
- * reserved beforehand is required (QSA_ERR_WORKSPACE otherwise).  Calls
- * that share a device's workspace must not run concurrently on different
- * streams.
+ * Uses the split partials, counters and error word of the workspace of
+ * `stream` (see the conventions above).
  */
 qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
                       const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
@@ -179,9 +190,9 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
  * Non-finite inputs are outside the contract.
  *
  * A slot id outside [0, slots) skips that token (nothing is written for it)
- * and sets bit 2 of the device error word.  Uses the device workspace's
- * error word only: outside capture it is created on first use; under
- * capture it must exist already (QSA_ERR_WORKSPACE otherwise).
+ * and sets bit 2 of the device error word.  Uses only the error word of
+ * the workspace of `stream`: outside capture it is created on first use;
+ * under capture it must exist already (QSA_ERR_WORKSPACE otherwise).
  */
 qsa_status qsa_kv_store(const qsa_tensor *k_new, const qsa_tensor *v_new,
                         const qsa_tensor *loc, qsa_tensor *k_pool, qsa_tensor *v_pool,
@@ -250,9 +261,9 @@ qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
  *   sel_out       [>= bs * (budget + c - 1)] i32, written
  *   cu_out        [bs + 1] i32, written
  *
- * Uses the device workspace's score scratch (bs * max_blocks floats),
- * created on first use outside stream capture; under capture it must have
- * been reserved with qsa_index_reserve.  A row whose T_b is negative, above
+ * Uses the score scratch (bs * max_blocks floats) of the workspace of
+ * `stream`, created on first use outside stream capture; under capture it
+ * must have been reserved with qsa_index_reserve on that stream.  A row whose T_b is negative, above
  * max_tokens or has more blocks than max_blocks lists nothing, and a block
  * table entry outside [0, n) scores -inf; both set bit 3 of the device
  * error word.
@@ -263,25 +274,40 @@ qsa_status qsa_index(const qsa_tensor *q_index, const qsa_tensor *head_weights,
                      int compress_ratio, qsa_tensor *sel_out, qsa_tensor *cu_out,
                      hipStream_t stream);
 
-/* Create (or grow) the current device's indexer score scratch for calls
- * with up to max_bs rows and max_blocks blocks per row.  Call it before
- * capturing a graph that contains qsa_index. */
+/* Create (or grow) the indexer score scratch of the workspace `stream`
+ * uses, for calls with up to max_bs rows and max_blocks blocks per row.
+ * Call it on the capturing stream before capturing a graph that contains
+ * qsa_index. */
 qsa_status qsa_index_reserve(int max_bs, int max_blocks, hipStream_t stream);
 
-/* Create (or grow) the current device's workspace for calls with up to
- * max_bs rows and the given head layout, and zero its counters.  Call it
- * before capturing a graph that contains qsa_decode.  Synchronises the
- * device when it has to replace an existing workspace. */
+/* Create (or grow) the workspace `stream` uses for calls with up to max_bs
+ * rows and the given head layout, and zero its counters and error word.
+ * Call it on the capturing stream before capturing a graph that contains
+ * qsa_decode.  Replacing an existing workspace synchronises `stream` (a
+ * private workspace) or the device (the shared one). */
 qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream);
 
-/* Re-zero the split counters and the device error word of the current
- * device's workspace (one small kernel on `stream`). */
+/* Give `stream` a private workspace on the current device, so that its
+ * calls can run concurrently with calls on other streams.  It starts empty
+ * and is created or grown like the shared one (reserve it before capture).
+ * Attaching an attached stream does nothing; at most 64 streams per device
+ * (QSA_ERR_WORKSPACE beyond).  Not allowed while `stream` is capturing. */
+qsa_status qsa_workspace_attach(hipStream_t stream);
+
+/* Free the private workspace of `stream` (synchronises `stream`, which must
+ * still exist); later calls on it use the shared workspace.  A stream
+ * without one is left as it is.  Not allowed while `stream` is capturing. */
+qsa_status qsa_workspace_detach(hipStream_t stream);
+
+/* Re-zero the split counters and the error word of the workspace `stream`
+ * uses (one small kernel on `stream`). */
 qsa_status qsa_workspace_reset(hipStream_t stream);
 
-/* Free the workspaces of all devices (synchronises each device). */
+/* Free every workspace, shared and private, of every device and detach all
+ * streams (synchronises each device). */
 qsa_status qsa_workspace_release(void);
 
-/* Bytes of split scratch + counters the current device's workspace holds. */
+/* Bytes held by the current device's workspaces, shared and private. */
 int64_t qsa_workspace_bytes(void);
 
 /* Thread-local message describing the last failed call ("" if none). */
@@ -305,21 +331,23 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
 qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);
 
-/* Device pointer and count of the current device's split counters (uint32,
- * zero between calls), for audits after a launch. */
-qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n);
+/* Device pointer and count of the split counters (uint32, zero between
+ * calls) of the workspace `stream` uses, for audits after a launch. */
+qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n, hipStream_t stream);
 
-/* Copy the first n split counters of the current device to host memory
- * (synchronises `stream`). */
+/* Copy the first n split counters of the workspace `stream` uses to host
+ * memory (synchronises `stream`). */
 qsa_status qsa_debug_read_counters(uint32_t *host, int n, hipStream_t stream);
 
 /* Enqueue one small kernel on `stream` that adds the sum of all split
- * counters of the current device to *dev_accum (a device uint32).  Safe to
- * use between graph replays; *dev_accum stays 0 while every launch leaves
- * its counters at rest. */
+ * counters of the workspace `stream` uses to *dev_accum (a device uint32).
+ * Safe to use between graph replays; *dev_accum stays 0 while every launch
+ * leaves its counters at rest. */
 qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream);
 
-/* Copy the sticky device error word to *host_word (synchronises `stream`).
+/* Copy the sticky device error word of the workspace `stream` uses to
+ * *host_word (synchronises `stream`; 0 when that workspace does not exist
+ * yet).
  * Bit 0: a row's cu_seqlens were out of range or longer than 2055.
  * Bit 1: a slot id was outside [0, slots).
  * Bit 2: a qsa_kv_store slot id was outside [0, slots).

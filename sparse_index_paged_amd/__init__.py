@@ -27,14 +27,17 @@ from ._binding import (  # noqa: F401
     load_library,
     plan,
     set_option,
+    workspace_attach,
     workspace_bytes,
+    workspace_detach,
     workspace_release,
     workspace_reserve,
     workspace_reset,
 )
 
 __all__ = [
-    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_reset", "workspace_release",
+    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_attach",
+    "workspace_detach", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
     "ABI_VERSION",

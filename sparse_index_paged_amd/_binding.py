@@ -8,7 +8,7 @@ import struct
 PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(PKG, "libqsa.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # qsa_dtype
 BF16, F16, F32, I32, FP8_E4M3FN, I8, U4X2, I64 = 1, 2, 3, 4, 5, 6, 7, 8
@@ -17,7 +17,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORK
 
 EXPORTS = (
     "qsa_decode", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_index",
-    "qsa_index_reserve", "qsa_workspace_reserve", "qsa_workspace_reset",
+    "qsa_index_reserve", "qsa_workspace_reserve", "qsa_workspace_attach", "qsa_workspace_detach",
+    "qsa_workspace_reset",
     "qsa_workspace_release", "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
     "qsa_debug_counters", "qsa_debug_read_counters", "qsa_debug_audit_counters",
     "qsa_debug_device_error", "qsa_abi_version",
@@ -83,6 +84,10 @@ def load_library():
     lib.qsa_index_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.qsa_workspace_reserve.restype = ctypes.c_int
     lib.qsa_workspace_reserve.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.qsa_workspace_attach.restype = ctypes.c_int
+    lib.qsa_workspace_attach.argtypes = [ctypes.c_void_p]
+    lib.qsa_workspace_detach.restype = ctypes.c_int
+    lib.qsa_workspace_detach.argtypes = [ctypes.c_void_p]
     lib.qsa_workspace_reset.restype = ctypes.c_int
     lib.qsa_workspace_reset.argtypes = [ctypes.c_void_p]
     lib.qsa_workspace_release.restype = ctypes.c_int
@@ -98,7 +103,7 @@ def load_library():
     lib.qsa_get_option.restype = ctypes.c_int
     lib.qsa_get_option.argtypes = [ctypes.c_char_p, P(ctypes.c_int64)]
     lib.qsa_debug_counters.restype = ctypes.c_int
-    lib.qsa_debug_counters.argtypes = [P(ctypes.c_void_p), P(ctypes.c_int)]
+    lib.qsa_debug_counters.argtypes = [P(ctypes.c_void_p), P(ctypes.c_int), ctypes.c_void_p]
     lib.qsa_debug_read_counters.restype = ctypes.c_int
     lib.qsa_debug_read_counters.argtypes = [P(ctypes.c_uint32), ctypes.c_int, ctypes.c_void_p]
     lib.qsa_debug_audit_counters.restype = ctypes.c_int
@@ -295,6 +300,18 @@ def workspace_reserve(max_bs: int, hq: int, hkv: int, stream=None):
     _check(load_library().qsa_workspace_reserve(max_bs, hq, hkv, _stream_handle(stream)))
 
 
+def workspace_attach(stream=None):
+    """Give `stream` (default: torch's current stream) a private workspace,
+    so that its calls may run concurrently with calls on other streams."""
+    _check(load_library().qsa_workspace_attach(_stream_handle(stream)))
+
+
+def workspace_detach(stream=None):
+    """Free the private workspace of `stream` (synchronises it); its later
+    calls use the device's shared workspace."""
+    _check(load_library().qsa_workspace_detach(_stream_handle(stream)))
+
+
 def workspace_reset(stream=None):
     _check(load_library().qsa_workspace_reset(_stream_handle(stream)))
 
@@ -324,13 +341,14 @@ def get_option(name: str) -> int:
 
 
 def debug_counters(stream=None) -> list[int]:
-    """Current values of the device's split counters (synchronises); they
-    read zero between calls."""
+    """Current values of the split counters of the workspace `stream` uses
+    (synchronises `stream`); they read zero between calls."""
     ptr, n = ctypes.c_void_p(), ctypes.c_int()
     lib = load_library()
-    _check(lib.qsa_debug_counters(ctypes.byref(ptr), ctypes.byref(n)))
+    h = _stream_handle(stream)
+    _check(lib.qsa_debug_counters(ctypes.byref(ptr), ctypes.byref(n), h))
     buf = (ctypes.c_uint32 * n.value)()
-    _check(lib.qsa_debug_read_counters(buf, n.value, _stream_handle(stream)))
+    _check(lib.qsa_debug_read_counters(buf, n.value, h))
     return list(buf)
 
 

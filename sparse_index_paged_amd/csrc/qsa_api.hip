@@ -103,8 +103,15 @@ int waves_for(int fmt, int64_t workgroups, int splits) {
   return 4;
 }
 
-// ---- workspace -------------------------------------------------------------
+// ---- workspaces ------------------------------------------------------------
+// A workspace holds the split partials, the split counters followed by the
+// sticky error word, and the indexer's block scores.  Each device has one
+// shared workspace, used by every stream without one of its own, and up to
+// kMaxAttached private workspaces, each bound to one stream by
+// qsa_workspace_attach.  Calls on different streams run concurrently only
+// when their workspaces differ.
 constexpr int kMaxDevices = 64;
+constexpr int kMaxAttached = 64;
 
 struct Workspace {
   float *part = nullptr;
@@ -115,8 +122,15 @@ struct Workspace {
   int64_t iscore_floats = 0;
 };
 
+struct DeviceWorkspaces {
+  Workspace shared;
+  bool used[kMaxAttached] = {};
+  hipStream_t stream[kMaxAttached] = {};
+  Workspace own[kMaxAttached];
+};
+
 std::mutex g_ws_mutex;
-Workspace g_ws[kMaxDevices];
+DeviceWorkspaces g_ws[kMaxDevices];
 
 constexpr int64_t kCtrWords = static_cast<int64_t>(qsa::kMaxBs) * 2;
 
@@ -135,23 +149,54 @@ bool stream_capturing(hipStream_t stream) {
   return st != hipStreamCaptureStatusNone;
 }
 
-// Ensure the current device's workspace holds `floats` partial floats.
+// Index of the private workspace bound to `stream` on `dev`, or -1 (the
+// caller holds g_ws_mutex).
+int attached_slot(int dev, hipStream_t stream) {
+  const DeviceWorkspaces &d = g_ws[dev];
+  for (int i = 0; i < kMaxAttached; ++i)
+    if (d.used[i] && d.stream[i] == stream) return i;
+  return -1;
+}
+
+// The workspace that calls on `stream` use (the caller holds g_ws_mutex).
+// Slots never move, so the reference stays valid until a detach or release.
+Workspace &workspace_of(int dev, hipStream_t stream, bool *own = nullptr) {
+  const int i = attached_slot(dev, stream);
+  if (own) *own = i >= 0;
+  return i >= 0 ? g_ws[dev].own[i] : g_ws[dev].shared;
+}
+
+void free_workspace(Workspace &ws) {
+  if (ws.part) (void)hipFree(ws.part);
+  if (ws.words) (void)hipFree(ws.words);
+  if (ws.iscores) (void)hipFree(ws.iscores);
+  ws = Workspace{};
+}
+
+// Wait until nothing can still use a workspace that is about to be replaced:
+// its own stream for a private one, the whole device for the shared one.
+hipError_t quiesce(bool own, hipStream_t stream) {
+  return own ? hipStreamSynchronize(stream) : hipDeviceSynchronize();
+}
+
+// Ensure the workspace `stream` uses on `dev` holds `floats` partial floats.
 qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
                             Workspace **out, const char *fn = "qsa_decode") {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace &ws = g_ws[dev];
+  bool own = false;
+  Workspace &ws = workspace_of(dev, stream, &own);
   if (ws.words != nullptr && ws.part_floats >= floats) {
     *out = &ws;
     return QSA_OK;
   }
   if (!allow_alloc)
     return fail(QSA_ERR_WORKSPACE,
-                "%s: the stream is capturing and the device %d workspace holds %lld "
+                "%s: the stream is capturing and the %s workspace of device %d holds %lld "
                 "partial floats, %lld needed; call qsa_workspace_reserve before capture",
-                fn, dev, static_cast<long long>(ws.part_floats), static_cast<long long>(floats));
+                fn, own ? "stream's own" : "shared", dev, static_cast<long long>(ws.part_floats),
+                static_cast<long long>(floats));
   if (ws.words != nullptr) {
-    if (hipDeviceSynchronize() != hipSuccess)
-      return fail(QSA_ERR_HIP, "workspace: hipDeviceSynchronize failed");
+    if (quiesce(own, stream) != hipSuccess) return fail(QSA_ERR_HIP, "workspace: synchronisation failed");
     (void)hipFree(ws.part);
     (void)hipFree(ws.words);
     float *keep = ws.iscores;
@@ -178,22 +223,24 @@ qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool al
   return QSA_OK;
 }
 
-// The current device's indexer score scratch, holding at least `floats`
-// (the counters and error word are created with it when missing).
+// The indexer score scratch of the workspace `stream` uses, holding at least
+// `floats` (the counters and error word are created with it when missing).
 qsa_status ensure_index_scores(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
                                Workspace **out, const char *fn) {
   qsa_status st = ensure_workspace(dev, 0, stream, allow_alloc, out, fn);
   if (st != QSA_OK) return st;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace &ws = g_ws[dev];
+  bool own = false;
+  Workspace &ws = workspace_of(dev, stream, &own);
   if (ws.iscore_floats >= floats && (floats == 0 || ws.iscores != nullptr)) return QSA_OK;
   if (!allow_alloc)
     return fail(QSA_ERR_WORKSPACE,
-                "%s: the stream is capturing and the device %d index scratch holds %lld floats, "
-                "%lld needed; call qsa_index_reserve before capture", fn, dev,
-                static_cast<long long>(ws.iscore_floats), static_cast<long long>(floats));
+                "%s: the stream is capturing and the %s workspace of device %d holds %lld index "
+                "score floats, %lld needed; call qsa_index_reserve before capture", fn,
+                own ? "stream's own" : "shared", dev, static_cast<long long>(ws.iscore_floats),
+                static_cast<long long>(floats));
   if (ws.iscores != nullptr) {
-    if (hipDeviceSynchronize() != hipSuccess) return fail(QSA_ERR_HIP, "%s: hipDeviceSynchronize failed", fn);
+    if (quiesce(own, stream) != hipSuccess) return fail(QSA_ERR_HIP, "%s: synchronisation failed", fn);
     (void)hipFree(ws.iscores);
     ws.iscores = nullptr;
     ws.iscore_floats = 0;
@@ -203,6 +250,7 @@ qsa_status ensure_index_scores(int dev, int64_t floats, hipStream_t stream, bool
     return fail(QSA_ERR_HIP, "%s: hipMalloc of %lld bytes failed", fn, static_cast<long long>(floats * 4));
   ws.iscores = static_cast<float *>(ptr);
   ws.iscore_floats = floats;
+  *out = &ws;
   return QSA_OK;
 }
 
@@ -877,12 +925,51 @@ qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream
   return ok();
 }
 
+qsa_status qsa_workspace_attach(hipStream_t stream) {
+  static const char *fn = "qsa_workspace_attach";
+  if (stream_capturing(stream)) return fail(QSA_ERR_WORKSPACE, "%s: called while the stream is capturing", fn);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (attached_slot(dev, stream) >= 0) return ok();
+  DeviceWorkspaces &d = g_ws[dev];
+  for (int i = 0; i < kMaxAttached; ++i) {
+    if (d.used[i]) continue;
+    d.own[i] = Workspace{};
+    d.stream[i] = stream;
+    d.used[i] = true;
+    return ok();
+  }
+  return fail(QSA_ERR_WORKSPACE, "%s: device %d already has %d streams with their own workspace", fn,
+              dev, kMaxAttached);
+}
+
+qsa_status qsa_workspace_detach(hipStream_t stream) {
+  static const char *fn = "qsa_workspace_detach";
+  if (stream_capturing(stream)) return fail(QSA_ERR_WORKSPACE, "%s: called while the stream is capturing", fn);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  const int i = attached_slot(dev, stream);
+  if (i < 0) return ok();
+  DeviceWorkspaces &d = g_ws[dev];
+  if (d.own[i].words != nullptr || d.own[i].iscores != nullptr) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return fail(QSA_ERR_HIP, "%s: hipStreamSynchronize failed", fn);
+    free_workspace(d.own[i]);
+  }
+  d.used[i] = false;
+  d.stream[i] = nullptr;
+  return ok();
+}
+
 qsa_status qsa_workspace_reset(hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return fail(QSA_ERR_HIP, "qsa_workspace_reset: no HIP device");
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  Workspace &ws = g_ws[dev];
+  Workspace &ws = workspace_of(dev, stream);
   if (ws.words == nullptr) return ok();
   if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
     return fail(QSA_ERR_HIP, "qsa_workspace_reset: zeroing the counters failed");
@@ -894,14 +981,15 @@ qsa_status qsa_workspace_release(void) {
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) cur = -1;
   for (int dev = 0; dev < kMaxDevices; ++dev) {
-    Workspace &ws = g_ws[dev];
-    if (ws.words == nullptr) continue;
+    DeviceWorkspaces &d = g_ws[dev];
+    bool any = d.shared.words != nullptr || d.shared.iscores != nullptr;
+    for (int i = 0; i < kMaxAttached; ++i) any = any || d.used[i];
+    if (!any) continue;
     if (hipSetDevice(dev) == hipSuccess && hipDeviceSynchronize() == hipSuccess) {
-      (void)hipFree(ws.part);
-      (void)hipFree(ws.words);
-      if (ws.iscores) (void)hipFree(ws.iscores);
+      free_workspace(d.shared);
+      for (int i = 0; i < kMaxAttached; ++i) free_workspace(d.own[i]);
     }
-    ws = Workspace{};
+    d = DeviceWorkspaces{};
   }
   if (cur >= 0) (void)hipSetDevice(cur);
   return ok();
@@ -911,18 +999,23 @@ int64_t qsa_workspace_bytes(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  const Workspace &ws = g_ws[dev];
-  if (ws.words == nullptr) return 0;
-  return ws.part_floats * 4 + (kCtrWords + 1) * 4 + ws.iscore_floats * 4;
+  auto bytes = [](const Workspace &ws) {
+    return ws.part_floats * 4 + (ws.words ? (kCtrWords + 1) * 4 : 0) + ws.iscore_floats * 4;
+  };
+  const DeviceWorkspaces &d = g_ws[dev];
+  int64_t total = bytes(d.shared);
+  for (int i = 0; i < kMaxAttached; ++i)
+    if (d.used[i]) total += bytes(d.own[i]);
+  return total;
 }
 
-qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n) {
+qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n, hipStream_t stream) {
   if (dev_ptr == nullptr || n == nullptr) return fail(QSA_ERR_ARG, "qsa_debug_counters: NULL argument");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return fail(QSA_ERR_HIP, "qsa_debug_counters: no HIP device");
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  const Workspace &ws = g_ws[dev];
+  const Workspace &ws = workspace_of(dev, stream);
   if (ws.words == nullptr) return fail(QSA_ERR_WORKSPACE, "qsa_debug_counters: no workspace yet");
   *dev_ptr = ws.words;
   *n = static_cast<int>(ws.n_ctr);
@@ -932,7 +1025,7 @@ qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n) {
 qsa_status qsa_debug_read_counters(uint32_t *host, int n, hipStream_t stream) {
   const uint32_t *ctr = nullptr;
   int total = 0;
-  qsa_status st = qsa_debug_counters(&ctr, &total);
+  qsa_status st = qsa_debug_counters(&ctr, &total, stream);
   if (st != QSA_OK) return st;
   if (host == nullptr || n < 0 || n > total)
     return fail(QSA_ERR_ARG, "qsa_debug_read_counters: n must be in [0, %d]", total);
@@ -945,7 +1038,7 @@ qsa_status qsa_debug_read_counters(uint32_t *host, int n, hipStream_t stream) {
 qsa_status qsa_debug_audit_counters(uint32_t *dev_accum, hipStream_t stream) {
   const uint32_t *ctr = nullptr;
   int total = 0;
-  qsa_status st = qsa_debug_counters(&ctr, &total);
+  qsa_status st = qsa_debug_counters(&ctr, &total, stream);
   if (st != QSA_OK) return st;
   if (dev_accum == nullptr) return fail(QSA_ERR_ARG, "qsa_debug_audit_counters: NULL accumulator");
   if (qsa::launch_audit(ctr, total, dev_accum, stream) != hipSuccess)
@@ -961,11 +1054,12 @@ qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream) {
   uint32_t *word = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (g_ws[dev].words == nullptr) {
+    const Workspace &ws = workspace_of(dev, stream);
+    if (ws.words == nullptr) {
       *host_word = 0;
       return ok();
     }
-    word = g_ws[dev].words + kCtrWords;
+    word = ws.words + kCtrWords;
   }
   if (hipMemcpyAsync(host_word, word, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)

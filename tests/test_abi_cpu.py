@@ -49,7 +49,7 @@ def test_header_compiles_as_c():
 
 
 def test_abi_version():
-    assert qsa.abi_version() == B.ABI_VERSION == 4
+    assert qsa.abi_version() == B.ABI_VERSION == 5
 
 
 def test_plan_and_options():
@@ -165,6 +165,22 @@ def test_null_arguments_are_arg_errors():
     st = lib.qsa_decode(None, None, None, None, None, None, None, None, None)
     assert st == 2
     assert "q is NULL" in lib.qsa_last_error().decode()
+
+
+def test_workspace_calls_without_a_device():
+    """Without a HIP device the workspace calls fail cleanly (nothing is
+    launched); with none attached there is nothing to free or count."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a HIP device is present")
+    lib = qsa.load_library()
+    for name in ("qsa_workspace_attach", "qsa_workspace_detach"):
+        assert getattr(lib, name)(None) == 4
+        assert "no HIP device" in lib.qsa_last_error().decode()
+    assert lib.qsa_workspace_bytes() == 0
+    assert lib.qsa_workspace_release() == 0
+    ptr, n = ctypes.c_void_p(), ctypes.c_int()
+    assert lib.qsa_debug_counters(ctypes.byref(ptr), ctypes.byref(n), None) == 4
 
 
 def _store(n=8, hkv=2, slots=64, pool_dtype=B.BF16, scales=None, new_dtype=B.BF16,
