@@ -20,7 +20,8 @@ tiered`` decodes from a tiered pool (int4-g32 pool plus an int8-g64 ring of
 ``--ring-rows`` rows, written by qsa_kv_store_tiered in slot order, so the
 ring holds the last ring-rows slots; ``--hot-frac`` draws that fraction of
 the entries from those slots, otherwise the lists are the default uniform
-ones), and ``--mode store`` times qsa_kv_store itself.
+ones), ``--mode store`` times qsa_kv_store itself, and ``--mode configs`` prints
+one line per measured workload configuration (see configs_mode).
 """
 from __future__ import annotations
 
@@ -403,6 +404,199 @@ def index_mode(args):
     }), flush=True)
 
 
+def time_calls(run_steps, calls: int, repeats: int):
+    """`repeats` runs of run_steps() (which issues `calls` decode calls on
+    torch's current stream), each bracketed by HIP events on that stream;
+    returns (median, p10, p90) in microseconds per call."""
+    import torch
+    stream = torch.cuda.current_stream()
+    per_call = []
+    for _ in range(repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        run_steps()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return (float(np.median(per_call)), float(np.percentile(per_call, 10)),
+            float(np.percentile(per_call, 90)))
+
+
+def configs_mode(args):
+    """One JSON line per workload of the five measured configurations:
+    bs=1 TP1 L=128 over a 4096-slot pool; bs=16 TP2 with mixed lengths over
+    65536 slots; bs=128 TP1 saturated (the default line's workload); bs=64
+    TP1 quantized pools (fp8 + f32 row scale, int8 + f32 row scale, int4 +
+    f32 scale per 32 channels) over 131072 slots with L~U[256,2055], warm
+    (one pool) and cold (4 pool copies rotating, 4 x the Infinity Cache's
+    256 MB is not reached by one copy); and the graph-replay sweep (TP1 and
+    TP2, every bs 1..16 plus 17/24/32/48/64/96/128, short / medium /
+    saturated lists with duplicate runs), timed as (a) a captured graph of 8
+    calls over 8 resident index banks and (b) per replay of one captured
+    call with its cu_seqlens and indices rewritten on the device before it."""
+    import torch
+
+    import sparse_index_paged_amd as qsa
+    import synth
+
+    torch.cuda.set_device(0)
+    qsa.workspace_reserve(128, 24, 2)
+    steps, reps = args.steps, args.repeats
+
+    def log(msg):
+        print(f"[configs] {msg}", file=sys.stderr, flush=True)
+
+    def emit(name, workload, b_kv, us, extra=None):
+        med, p10, p90 = us
+        gbs = b_kv / (med * 1e-6) / 1e9
+        rec = {"mode": "configs", "config": name, "workload": workload,
+               "us_per_call": round(med, 3), "us_p10": round(p10, 3), "us_p90": round(p90, 3),
+               "gathered_kv_bytes_per_call": int(b_kv), "GBps": round(gbs, 1),
+               "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if extra:
+            rec.update(extra)
+        print(json.dumps(rec), flush=True)
+
+    def bank_sel(seed, lengths, slots):
+        """Another packed index list for the same lengths: one generator
+        per bank, every row its own draws."""
+        rng = np.random.default_rng(seed)
+        return synth.pack([synth.draw_indices(rng, n, slots) for n in lengths])[0]
+
+    def bf16_case(case, bank_seed, name, workload):
+        slots = case.k_pool.shape[0]
+        sels = [case.sel] + [bank_sel(bank_seed + i, case.lengths, slots) for i in range(1, 4)]
+        q, k, v = case.q.cuda(), case.k_pool.cuda(), case.v_pool.cuda()
+        cu = torch.from_numpy(case.cu).cuda()
+        sd = [torch.from_numpy(s).cuda() for s in sels]
+        out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            qsa.decode(q, k, v, sd[i % 4], cu, out=out, lse=lse)
+        b_kv = gathered_bytes(case.lengths, case.hkv)
+        us, us_graph = eager_and_graph(call)
+        emit(name, workload, b_kv, us, {"splits": qsa.plan(case.bs, case.hkv)[0], **us_graph})
+        return k, v
+
+    def eager_and_graph(call):
+        """Eager launches (which at small sizes measure the host's submission
+        rate) and a captured graph of 8 calls replayed (device time)."""
+        def run():
+            for i in range(steps):
+                call(i)
+        run()
+        us = time_calls(run, steps, reps)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(8):
+                call(i)
+        g.replay()
+        n8 = max(1, steps // 8)
+
+        def run8():
+            for _ in range(n8):
+                g.replay()
+        med, p10, p90 = time_calls(run8, 8 * n8, reps)
+        del g
+        return us, {"graph_us_per_call": round(med, 3), "graph_us_p10": round(p10, 3),
+                    "graph_us_p90": round(p90, 3)}
+
+    log("bs=1 TP1")
+    bf16_case(synth.case_bs1_tp1(), 101_000, "bs1_tp1_L128",
+              "bs=1 TP1 (24Q/2KV) bf16 pools [4096,2,256], 128 uniform indices")
+    log("bs=16 TP2 mixed")
+    bf16_case(synth.case_bs16_tp2_mixed(), 102_000, "bs16_tp2_mixed",
+              "bs=16 TP2 (12Q/1KV) bf16 pools [65536,1,256], 8 rows L~U[1,64], 4 rows 2055, "
+              "4 rows L~U[65,2054]")
+    log("bs=128 TP1 saturated")
+    k_big, v_big = bf16_case(synth.case_bs128_tp1_saturated(), 103_000, "bs128_tp1_saturated",
+                             "bs=128 TP1 (24Q/2KV) bf16 pools [262144,2,256], 2055 entries per "
+                             "row, 5% keys x8")
+
+    # ---- quantized pools, warm and cold
+    for fmt, group, seed in (("fp8", 256, 1041), ("int8", 256, 1042), ("int4", 32, 1043)):
+        log(f"bs=64 TP1 {fmt}")
+        case = synth.case_bs64_tp1_quantsrc(seed)
+        kc, vc, ks, vs = quantized_pools(case.k_pool.cuda(), case.v_pool.cuda(), fmt, group,
+                                         torch.float32)
+        copies = [(kc, vc, ks, vs)] + [tuple(t.clone() for t in (kc, vc, ks, vs)) for _ in range(3)]
+        slots = case.k_pool.shape[0]
+        sels = [case.sel] + [bank_sel(seed * 1000 + i, case.lengths, slots) for i in range(1, 4)]
+        q = case.q.cuda()
+        cu = torch.from_numpy(case.cu).cuda()
+        sd = [torch.from_numpy(s).cuda() for s in sels]
+        out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
+        b_kv = gathered_bytes(case.lengths, case.hkv, row_bytes(fmt, group, 4))
+        for variant, ncopy in (("warm", 1), ("cold", 4)):
+            def call(i):
+                k_, v_, ks_, vs_ = copies[i % ncopy]
+                qsa.decode(q, k_, v_, sd[i % 4], cu, out=out, lse=lse, kv_format=fmt,
+                           k_scale=ks_, v_scale=vs_, group_size=group)
+            us, us_graph = eager_and_graph(call)
+            emit(f"bs64_tp1_{fmt}_{variant}",
+                 f"bs=64 TP1 (24Q/2KV) {fmt} pools [131072,2,{FORMATS[fmt][0]}] + f32 scales per "
+                 f"{group} channels (written by qsa_kv_store), L~U[256,2055], "
+                 f"{ncopy} pool cop{'y' if ncopy == 1 else 'ies'} rotating", b_kv, us,
+                 {"kv_format": fmt, "group": group, "pool_copies": ncopy, **us_graph})
+        del copies, kc, vc, ks, vs
+        torch.cuda.empty_cache()
+
+    # ---- graph-replay sweep over the bench's bf16 pools (TP2 uses KV head 0)
+    slots = k_big.shape[0]
+    for hkv in (2, 1):
+        kd, vd = (k_big, v_big) if hkv == 2 else (k_big[:, :1], v_big[:, :1])
+        hq = 12 * hkv
+        for kind in ("short", "medium", "saturated"):
+            log(f"graph sweep hkv={hkv} {kind}")
+            table = {}
+            for bs in synth.SWEEP_BS:
+                banks = synth.sweep_bank(1050 + bs, bs, kind, slots, banks=8)
+                sel_banks = [torch.from_numpy(s).cuda() for s, _ in banks]
+                cu_banks = [torch.from_numpy(c).cuda() for _, c in banks]
+                q = synth.normal_bf16(np.random.default_rng(bs * 7 + hkv), (bs, hq, 256)).cuda()
+                out = torch.empty(bs, hq, 256, dtype=torch.bfloat16, device="cuda")
+                lse = torch.empty(bs, hq, dtype=torch.float32, device="cuda")
+                qsa.decode(q, kd, vd, sel_banks[0], cu_banks[0], out=out, lse=lse)
+                torch.cuda.synchronize()
+                g8 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g8):
+                    for b in range(8):
+                        qsa.decode(q, kd, vd, sel_banks[b], cu_banks[b], out=out, lse=lse)
+                g8.replay()
+                n8 = max(1, steps // 8)
+
+                def run8():
+                    for _ in range(n8):
+                        g8.replay()
+                us8 = time_calls(run8, 8 * n8, reps)[0]
+                sel_buf, cu_buf = sel_banks[0].clone(), cu_banks[0].clone()
+                g1 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1):
+                    qsa.decode(q, kd, vd, sel_buf, cu_buf, out=out, lse=lse)
+                g1.replay()
+
+                def run1():
+                    for r in range(steps):
+                        sel_buf.copy_(sel_banks[r % 8])
+                        cu_buf.copy_(cu_banks[r % 8])
+                        g1.replay()
+                us1 = time_calls(run1, steps, reps)[0]
+                mean_b = float(np.mean([gathered_bytes(np.diff(c), hkv) for _, c in banks]))
+                table[str(bs)] = {"us_per_call": round(us8, 2),
+                                  "GBps": round(mean_b / (us8 * 1e-6) / 1e9, 1),
+                                  "us_per_replay_with_rewrite": round(us1, 2)}
+                del g8, g1
+            print(json.dumps({"mode": "configs", "config": f"graph_sweep_{'tp1' if hkv == 2 else 'tp2'}_{kind}",
+                              "workload": f"{'TP1 (24Q/2KV)' if hkv == 2 else 'TP2 (12Q/1KV)'} bf16 pools "
+                                          f"[262144,{hkv},256], {kind} lists with duplicate runs, "
+                                          "8 banks per bs",
+                              "counters_at_rest": all(c == 0 for c in qsa.debug_counters()),
+                              "by_bs": table}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,7 +611,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
-    ap.add_argument("--mode", choices=["decode", "copy", "store", "index"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs"], default="decode")
     ap.add_argument("--ctx", type=int, default=8192, help="index mode: context tokens per row")
     ap.add_argument("--compress", type=int, default=4, help="index mode: compression ratio")
     ap.add_argument("--budget", type=int, default=2048, help="index mode: token budget")
@@ -451,6 +645,9 @@ def main():
         return
     if args.mode == "index":
         index_mode(args)
+        return
+    if args.mode == "configs":
+        configs_mode(args)
         return
 
     import numpy as np

@@ -459,7 +459,18 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
     }
   }
   __syncthreads();
+  // Q's B operands do not change over the loop: instances with register
+  // room (no per-group K scales) keep all 8 in registers (32 VGPRs), which
+  // takes 8 KB of LDS reads off every tile; the others re-read them from LDS
+  constexpr bool QREG = NG <= 1 && !TIER;
+  bf16x8 qreg[QREG ? 8 : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qreg[kk] = as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
+  }
   auto qfrag = [&](int kk) -> bf16x8 {
+    if constexpr (QREG) return qreg[kk];
     return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
   };
   // K operand: channel chunk 4*kk + qg of row r16
