@@ -48,13 +48,14 @@ std::atomic<int64_t> g_waves{0};  // 0: chosen per call (waves_for)
 // options only -- never on live lengths -- so captured graphs stay valid.
 //
 // Default: a cost model of one launch with every list at full capacity on
-// a 256-CU MI355X, fitted to measured per-workgroup timelines.  With n
-// splits the pairs' P*n workgroups are dealt round-robin over the CUs (two
-// resident per CU); the busiest CU gathers ceil(P*n/256) * ceil(2055/n)
-// entries at ~30 entries/us, a split pair adds ~6 us of merge latency, and
-// each workgroup per CU beyond the two resident ones adds ~20 us (it starts
-// only when a resident one has finished, and pays its own start-up and
-// merge).
+// a 256-CU MI355X (8 XCDs of 32 CUs), fitted to measured per-workgroup
+// timelines.  Every split of pair p runs on XCD p % 8 (the launch gives
+// them workgroup ids congruent mod 8), so the busiest XCD holds
+// ceil(P/8) pairs and ceil(P/8)*n workgroups on its 32 CUs; its busiest
+// CU gathers ceil(ceil(P/8)*n/32) * ceil(2055/n) entries at ~30 entries/us,
+// a split pair adds ~6 us of merge latency, and each workgroup per CU
+// beyond the two resident ones adds ~20 us (it starts only when a resident
+// one has finished, and pays its own start-up and merge).
 // split_target > 0 replaces the model by "about split_target workgroups".
 int plan_splits(int bs, int hkv) {
   const int64_t npairs = static_cast<int64_t>(bs) * hkv;
@@ -67,10 +68,16 @@ int plan_splits(int bs, int hkv) {
     if (s < 1) s = 1;
     return static_cast<int>(s);
   }
+  // a row never activates more than ceil(2055 / min_split_keys) splits, so
+  // the model only prices split counts that can all be active (a larger
+  // grid would be costed for short workgroups that never run)
+  const int64_t msk = g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load();
+  const int64_t sact = (qsa::kMaxSel + msk - 1) / msk;
+  const int64_t nmax = smax < sact ? smax : sact;
   int best = 1;
   double best_cost = 1e30;
-  for (int n = 1; n <= smax; ++n) {
-    const int64_t per_cu = (npairs * n + 255) / 256;
+  for (int n = 1; n <= nmax; ++n) {
+    const int64_t per_cu = (((npairs + 7) / 8) * n + 31) / 32;
     const double cost = static_cast<double>(per_cu) * ((qsa::kMaxSel + n - 1) / n) / 30.0 +
                         (n > 1 ? 6.0 : 0.0) + 20.0 * static_cast<double>(per_cu > 2 ? per_cu - 2 : 0);
     if (cost < best_cost - 1e-9) {

@@ -59,14 +59,28 @@ def test_plan_and_options():
     assert qsa.plan(128, 2) == (1, 256)
     assert qsa.plan(64, 2) == (2, 256)
     assert qsa.plan(32, 2) == (4, 256)
-    assert qsa.plan(16, 1) == (16, 256)
+    assert qsa.plan(16, 1) == (9, 144)         # at most ceil(2055 / 256) splits are ever active
+    assert qsa.plan(17, 2) == (6, 240)         # 5 pairs x 6 splits = 30 workgroups on the busiest XCD
+    assert qsa.plan(85, 2) == (1, 176)         # 22 pairs per XCD: unsplit beats a second workgroup per CU
     assert qsa.plan(48, 2) == (5, 480)
     assert qsa.plan(96, 2) == (1, 192)        # a third workgroup per CU costs more
     assert qsa.plan(96, 1) == (5, 480)
     for bs in range(1, 129):
         for hkv in (1, 2):
             s, w = qsa.plan(bs, hkv)
-            assert 1 <= s <= 16 and w == ((bs * hkv + 7) // 8) * 8 * s
+            assert 1 <= s <= 9 and w == ((bs * hkv + 7) // 8) * 8 * s
+    # all splits of pair p run on XCD p % 8 (32 CUs each): no plan puts more
+    # than two workgroups on a CU of the busiest XCD
+    for bs in range(1, 129):
+        for hkv in (1, 2):
+            s, _ = qsa.plan(bs, hkv)
+            assert -(-bs * hkv // 8) * s <= 2 * 32, (bs, hkv, s)
+    # the cap follows min_split_keys: with 128 keys per split up to 16 can be active
+    qsa.set_option("min_split_keys", 128)
+    try:
+        assert qsa.plan(1, 2)[0] == 16
+    finally:
+        qsa.set_option("min_split_keys", 256)
     with pytest.raises(qsa.QsaError, match="unknown option"):
         qsa.set_option("nope", 3)
     with pytest.raises(qsa.QsaError, match="bs must be"):
