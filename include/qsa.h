@@ -327,6 +327,8 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
  *   "waves_per_workgroup" 4 or 8, or 0 (default): 8 for int4 pools without
  *                    splits and for tiered pools when the grid has at most
  *                    one workgroup per CU (256), else 4
+ *   "splits"         0 (default): as above; k >= 1: exactly k splits per
+ *                    (row, KV head), at most max_splits
  * Changing them affects later launches and later reservations. */
 qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);

@@ -43,24 +43,31 @@ std::atomic<int64_t> g_split_target{0};  // 0: cost model below
 std::atomic<int64_t> g_max_splits{16};
 std::atomic<int64_t> g_min_split_keys{256};
 std::atomic<int64_t> g_waves{0};  // 0: chosen per call (waves_for)
+std::atomic<int64_t> g_splits{0};     // > 0: exactly this many splits (tuning)
 
 // Splits per (row, KV head) pair.  The plan depends on (bs, hkv) and the
 // options only -- never on live lengths -- so captured graphs stay valid.
 //
 // Default: a cost model of one launch with every list at full capacity on
-// a 256-CU MI355X (8 XCDs of 32 CUs), fitted to measured per-workgroup
-// timelines.  Every split of pair p runs on XCD p % 8 (the launch gives
-// them workgroup ids congruent mod 8), so the busiest XCD holds
-// ceil(P/8) pairs and ceil(P/8)*n workgroups on its 32 CUs; its busiest
-// CU gathers ceil(ceil(P/8)*n/32) * ceil(2055/n) entries at ~30 entries/us,
-// a split pair adds ~6 us of merge latency, and each workgroup per CU
-// beyond the two resident ones adds ~20 us (it starts only when a resident
-// one has finished, and pays its own start-up and merge).
-// split_target > 0 replaces the model by "about split_target workgroups".
+// a 256-CU MI355X (8 XCDs of 32 CUs), fitted to graph-replayed saturated
+// calls at every bs 1..128 in both layouts and every split count.  All
+// splits of pair p run on XCD p % 8 (the launch gives them workgroup ids
+// congruent mod 8), so the busiest XCD holds ceil(P/8) pairs and
+// ceil(P/8)*n workgroups on its 32 CUs.  With n splits a launch costs
+//   max(busiest CU's entries / 40 per us, P * 2055 * 1 KB / 7 TB/s)
+//   + (6 + 0.5 n) us of split merge when n > 1
+//   + 20 us for each workgroup per CU beyond the two resident ones,
+// where the busiest CU's entries are ceil(ceil(P/8)*n/32) * ceil(2055/n):
+// more splits shorten each workgroup's dependent chain of tiles until the
+// gather is bound by HBM, and each one lengthens the merge.  Only split
+// counts a full row can activate are priced.
+// split_target > 0 replaces the model by "about split_target workgroups";
+// splits > 0 fixes the split count.
 int plan_splits(int bs, int hkv) {
   const int64_t npairs = static_cast<int64_t>(bs) * hkv;
   const int64_t smax = g_max_splits.load();
   const int64_t target = g_split_target.load();
+  if (g_splits.load() > 0) return static_cast<int>(g_splits.load() < smax ? g_splits.load() : smax);
   if (target > 0) {
     const int64_t npairs8 = ((npairs + 7) / 8) * 8;
     int64_t s = (target + npairs8 - 1) / npairs8;
@@ -76,10 +83,12 @@ int plan_splits(int bs, int hkv) {
   const int64_t nmax = smax < sact ? smax : sact;
   int best = 1;
   double best_cost = 1e30;
+  const double hbm_us = static_cast<double>(npairs) * qsa::kMaxSel * 1024.0 / 7.0e6;
   for (int n = 1; n <= nmax; ++n) {
     const int64_t per_cu = (((npairs + 7) / 8) * n + 31) / 32;
-    const double cost = static_cast<double>(per_cu) * ((qsa::kMaxSel + n - 1) / n) / 30.0 +
-                        (n > 1 ? 6.0 : 0.0) + 20.0 * static_cast<double>(per_cu > 2 ? per_cu - 2 : 0);
+    const double lat_us = static_cast<double>(per_cu) * ((qsa::kMaxSel + n - 1) / n) / 40.0;
+    const double cost = (lat_us > hbm_us ? lat_us : hbm_us) + (n > 1 ? 6.0 + 0.5 * n : 0.0) +
+                        20.0 * static_cast<double>(per_cu > 2 ? per_cu - 2 : 0);
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = n;
@@ -651,7 +660,8 @@ const char *qsa_last_error(void) { return g_last_error.c_str(); }
 
 qsa_status qsa_set_option(const char *name, int64_t value) {
   if (name == nullptr) return fail(QSA_ERR_ARG, "qsa_set_option: name is NULL");
-  if (value < 0 || (value == 0 && strcmp(name, "split_target") != 0 && strcmp(name, "waves_per_workgroup") != 0))
+  if (value < 0 || (value == 0 && strcmp(name, "split_target") != 0 && strcmp(name, "waves_per_workgroup") != 0 &&
+                     strcmp(name, "splits") != 0))
     return fail(QSA_ERR_ARG, "qsa_set_option: %s must be >= 1", name);
   if (!strcmp(name, "split_target")) {
     g_split_target = value;  // 0 restores the cost model
@@ -663,6 +673,9 @@ qsa_status qsa_set_option(const char *name, int64_t value) {
   } else if (!strcmp(name, "waves_per_workgroup")) {
     if (value != 0 && value != 4 && value != 8) return fail(QSA_ERR_ARG, "qsa_set_option: waves_per_workgroup must be 0, 4 or 8");
     g_waves = value;
+  } else if (!strcmp(name, "splits")) {
+    if (value > 64) return fail(QSA_ERR_ARG, "qsa_set_option: splits must be <= 64");
+    g_splits = value;
   } else {
     return fail(QSA_ERR_ARG, "qsa_set_option: unknown option '%s'", name);
   }
@@ -675,6 +688,7 @@ qsa_status qsa_get_option(const char *name, int64_t *value) {
   else if (!strcmp(name, "max_splits")) *value = g_max_splits;
   else if (!strcmp(name, "min_split_keys")) *value = g_min_split_keys;
   else if (!strcmp(name, "waves_per_workgroup")) *value = g_waves;
+  else if (!strcmp(name, "splits")) *value = g_splits;
   else return fail(QSA_ERR_ARG, "qsa_get_option: unknown option '%s'", name);
   return ok();
 }

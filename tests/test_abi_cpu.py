@@ -54,17 +54,17 @@ def test_abi_version():
 
 def test_plan_and_options():
     assert qsa.get_option("split_target") == 0          # cost model
-    # one workgroup per CU when the pairs fill the chip; fractional fills
-    # pick the split count that balances the busiest CU
+    # one workgroup per CU when the pairs fill the chip; below that, splits
+    # until the gather is bound by HBM, weighed against the merge per split
     assert qsa.plan(128, 2) == (1, 256)
     assert qsa.plan(64, 2) == (2, 256)
-    assert qsa.plan(32, 2) == (4, 256)
+    assert qsa.plan(32, 2) == (3, 192)        # HBM-bound already at 3 splits: more only add merge
     assert qsa.plan(16, 1) == (9, 144)         # at most ceil(2055 / 256) splits are ever active
-    assert qsa.plan(17, 2) == (6, 240)         # 5 pairs x 6 splits = 30 workgroups on the busiest XCD
+    assert qsa.plan(17, 2) == (5, 200)         # 5 pairs x 5 splits = 25 workgroups on the busiest XCD
     assert qsa.plan(85, 2) == (1, 176)         # 22 pairs per XCD: unsplit beats a second workgroup per CU
-    assert qsa.plan(48, 2) == (5, 480)
-    assert qsa.plan(96, 2) == (1, 192)        # a third workgroup per CU costs more
-    assert qsa.plan(96, 1) == (5, 480)
+    assert qsa.plan(48, 2) == (2, 192)
+    assert qsa.plan(96, 2) == (1, 192)
+    assert qsa.plan(96, 1) == (2, 192)
     for bs in range(1, 129):
         for hkv in (1, 2):
             s, w = qsa.plan(bs, hkv)
@@ -75,12 +75,21 @@ def test_plan_and_options():
         for hkv in (1, 2):
             s, _ = qsa.plan(bs, hkv)
             assert -(-bs * hkv // 8) * s <= 2 * 32, (bs, hkv, s)
-    # the cap follows min_split_keys: with 128 keys per split up to 16 can be active
+    # the cap follows min_split_keys: with 128 keys per split up to 16 can be
+    # active, and a single row then takes more than 9
     qsa.set_option("min_split_keys", 128)
     try:
-        assert qsa.plan(1, 2)[0] == 16
+        assert 9 < qsa.plan(1, 2)[0] <= 16
     finally:
         qsa.set_option("min_split_keys", 256)
+    # "splits" fixes the split count (bounded by max_splits)
+    qsa.set_option("splits", 5)
+    try:
+        assert qsa.plan(128, 2) == (5, 1280)
+        assert qsa.get_option("splits") == 5
+    finally:
+        qsa.set_option("splits", 0)
+    assert qsa.plan(128, 2) == (1, 256)
     with pytest.raises(qsa.QsaError, match="unknown option"):
         qsa.set_option("nope", 3)
     with pytest.raises(qsa.QsaError, match="bs must be"):
