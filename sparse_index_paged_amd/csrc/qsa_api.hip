@@ -101,21 +101,24 @@ int64_t plan_workgroups(int bs, int hkv, int splits) {
   return ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8 * splits;
 }
 
-// Waves per workgroup.  4-wave workgroups leave two resident per CU; when
-// the grid has at most one workgroup per CU that is one wave per SIMD, and
-// the formats bound by per-tile ALU work (int4; the tiered pool, which also
-// selects a tier per row) then run faster as 8-wave workgroups: two waves
-// per SIMD overlap one wave's dequantization with the other's memory wait.
-// Measured on MI355X: bs=128 TP1 int4 72.8 -> 62.9 us, tiered 85.9 ->
-// 67.9 us; bf16, fp8 and int8 are faster with 4.  With splits, int4 keeps 4
-// (its 8-wave form was slower at bs=32 and 48).
+// Waves per workgroup.  4-wave workgroups leave two resident per CU, which
+// with at most one workgroup per CU is one wave per SIMD.  The quantized
+// formats are bound by per-tile ALU work (dequantization, and for the
+// tiered pool the tier selection), so they run as 8-wave workgroups: two
+// waves per SIMD overlap one wave's dequantization with the other's memory
+// wait, and each wave keeps half as many tiles in flight, so a CU holds the
+// same bytes in flight.  Measured on MI355X (bs=128 / 96 / 64 / 32 TP1,
+// 4 -> 8 waves): fp8 59.8 -> 60.1 / 53.6 -> 48.5 / 36.7 -> 36.4 / 25.8 -> 24.3 us,
+// int8 g64 68.7 -> 65.1 / 64.3 -> 52.1 / 40.6 -> 39.6 / 29.3 -> 26.0 us,
+// int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 -> 27.9 us; bf16
+// is faster with 4.  The tiered pool keeps 8 only while the grid has at most
+// one workgroup per CU.
 int waves_for(int fmt, int64_t workgroups, int splits) {
+  (void)splits;
   const int64_t forced = g_waves.load();
   if (forced == 4 || forced == 8) return static_cast<int>(forced);
-  if (workgroups <= 256) {
-    if (fmt == qsa::kFmtTIERED) return 8;
-    if (fmt == qsa::kFmtINT4 && splits == 1) return 8;
-  }
+  if (fmt == qsa::kFmtFP8 || fmt == qsa::kFmtINT8 || fmt == qsa::kFmtINT4) return 8;
+  if (fmt == qsa::kFmtTIERED && workgroups <= 256) return 8;
   return 4;
 }
 
