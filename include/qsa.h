@@ -325,8 +325,8 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
  *   "min_split_keys" fewest list entries a split is given before another
  *                    split is used (default 256)
  *   "waves_per_workgroup" 4 or 8, or 0 (default): 8 for fp8 / int8 / int4
- *                    pools, and for tiered pools when the grid has at most
- *                    one workgroup per CU (256); 4 for bf16 pools
+ *                    and tiered pools when the grid has at most one
+ *                    workgroup per CU (256), else 4; 4 for bf16 pools
  *   "splits"         0 (default): as above; k >= 1: exactly k splits per
  *                    (row, KV head), at most max_splits
  * Changing them affects later launches and later reservations. */

@@ -111,14 +111,13 @@ int64_t plan_workgroups(int bs, int hkv, int splits) {
 // 4 -> 8 waves): fp8 59.8 -> 60.1 / 53.6 -> 48.5 / 36.7 -> 36.4 / 25.8 -> 24.3 us,
 // int8 g64 68.7 -> 65.1 / 64.3 -> 52.1 / 40.6 -> 39.6 / 29.3 -> 26.0 us,
 // int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 -> 27.9 us; bf16
-// is faster with 4.  The tiered pool keeps 8 only while the grid has at most
-// one workgroup per CU.
+// is faster with 4.  An 8-wave workgroup takes 151 KB of LDS, so only one
+// fits on a CU: grids of more than 256 workgroups (two per CU) keep 4 waves.
 int waves_for(int fmt, int64_t workgroups, int splits) {
   (void)splits;
   const int64_t forced = g_waves.load();
   if (forced == 4 || forced == 8) return static_cast<int>(forced);
-  if (fmt == qsa::kFmtFP8 || fmt == qsa::kFmtINT8 || fmt == qsa::kFmtINT4) return 8;
-  if (fmt == qsa::kFmtTIERED && workgroups <= 256) return 8;
+  if (fmt != qsa::kFmtBF16 && workgroups <= 256) return 8;
   return 4;
 }
 
