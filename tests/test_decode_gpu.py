@@ -25,6 +25,7 @@ def _default_options():
     qsa.set_option("max_splits", 16)
     qsa.set_option("min_split_keys", 256)
     qsa.set_option("waves_per_workgroup", 0)
+    qsa.set_option("splits", 0)
 
 
 def test_bs1_tp1_l128():
@@ -85,6 +86,28 @@ def test_quantized_group_sizes(fmt, group, hkv, waves):
     kc, ks = quant.quantize(case.k_pool, fmt, group)
     vc, vs = quant.quantize(case.v_pool, fmt, group)
     run_and_compare(case, f"{fmt} g{group} hkv{hkv}", quant=(fmt, group, kc, ks, vc, vs))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+def test_every_split_count(splits, fmt):
+    """Any partition of a list into contiguous splits merges to the same
+    attention (page "fix(qsa): restore SM121 correctness with Humanize and
+    Kernel Design Agent", section "Optimized kernel": splits combined by a
+    stable fp32 log-sum-exp merge in the final split): each forced split
+    count against the oracle, rows of every length class, counters at rest."""
+    qsa.set_option("splits", splits)
+    lens = [2055, 1, 257, 0, 1500, 2055, 768, 31]
+    case = synth.make_case(lengths=lens, slots=8192, hkv=2, seed=300 + splits, dup_prob=0.1)
+    assert qsa.plan(case.bs, 2)[0] == splits
+    if fmt == "bf16":
+        run_and_compare(case, f"splits={splits} bf16")
+    else:
+        kc, ks = quant.quantize(case.k_pool, "int4", 32, "f16")
+        vc, vs = quant.quantize(case.v_pool, "int4", 32, "f16")
+        run_and_compare(case, f"splits={splits} int4", quant=("int4", 32, kc, ks, vc, vs),
+                        scale_dtype=torch.float16)
+    assert all(v == 0 for v in qsa.debug_counters())
 
 
 EDGE_LENGTHS = [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 2054, 2055, 0, 3, 511]
