@@ -397,8 +397,12 @@ def index_mode(args):
                    "bs": bs, "ctx": args.ctx, "compress_ratio": c, "budget": budget,
                    "index_heads": hi, "index_dim": di, "launches_per_call": 2,
                    "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": byts},
+        # fp32 vector peak: 256 CUs x 128 FMA lanes per clock (packed fp32
+        # issues two per lane) x 2 flops x 2.4 GHz = 157.3 TFLOP/s; the build
+        # emits no packed fp32 forms, so single-issue FMAs top out at half
         "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": 157.3, "unit": "TFLOP/s",
                      "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "peak_single_issue_fma": 78.6, "frac_single_issue_fma": round(tflops / 78.6, 4),
                      "hbm_GBps": round(byts / (ms * 1e-3) / 1e9, 2),
                      "kernel": "qsa_index_score_kernel + qsa_index_select_kernel"},
     }), flush=True)
