@@ -67,7 +67,8 @@ int plan_splits(int bs, int hkv) {
   const int64_t npairs = static_cast<int64_t>(bs) * hkv;
   const int64_t smax = g_max_splits.load();
   const int64_t target = g_split_target.load();
-  if (g_splits.load() > 0) return static_cast<int>(g_splits.load() < smax ? g_splits.load() : smax);
+  const int64_t forced = g_splits.load();
+  if (forced > 0) return static_cast<int>(forced < smax ? forced : smax);
   if (target > 0) {
     const int64_t npairs8 = ((npairs + 7) / 8) * 8;
     int64_t s = (target + npairs8 - 1) / npairs8;
@@ -113,8 +114,7 @@ int64_t plan_workgroups(int bs, int hkv, int splits) {
 // int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 -> 27.9 us; bf16
 // is faster with 4.  An 8-wave workgroup takes 151 KB of LDS, so only one
 // fits on a CU: grids of more than 256 workgroups (two per CU) keep 4 waves.
-int waves_for(int fmt, int64_t workgroups, int splits) {
-  (void)splits;
+int waves_for(int fmt, int64_t workgroups) {
   const int64_t forced = g_waves.load();
   if (forced == 4 || forced == 8) return static_cast<int>(forced);
   if (fmt != qsa::kFmtBF16 && workgroups <= 256) return 8;
@@ -731,7 +731,7 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   p.scale_f16 = pd.scale_f16;
   p.a32 = addresses_fit_32(pd, k_pool, v_pool) ? 1 : 0;
   p.slots = pd.slots;
-  p.waves = waves_for(pd.fmt, plan_workgroups(p.bs, p.hkv, p.nsplit), p.nsplit);
+  p.waves = waves_for(pd.fmt, plan_workgroups(p.bs, p.hkv, p.nsplit));
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -777,7 +777,7 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.ring.owner = static_cast<const int32_t *>(pool->owner.data);
   p.ring.mask = static_cast<uint32_t>(td.ring.slots - 1);
   p.a32 = tiered_fits_32(pool, td, &p) ? 1 : 0;
-  p.waves = waves_for(qsa::kFmtTIERED, plan_workgroups(p.bs, p.hkv, p.nsplit), p.nsplit);
+  p.waves = waves_for(qsa::kFmtTIERED, plan_workgroups(p.bs, p.hkv, p.nsplit));
   const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
