@@ -438,7 +438,9 @@ def configs_mode(args):
     TP2, every bs 1..16 plus 17/24/32/48/64/96/128, short / medium /
     saturated lists with duplicate runs), timed as (a) a captured graph of 8
     calls over 8 resident index banks and (b) per replay of one captured
-    call with its cu_seqlens and indices rewritten on the device before it."""
+    call with its cu_seqlens and indices rewritten on the device before it.
+    Every configuration's eager timing runs before any graph is captured.
+    --only selects configurations by substrings of their names."""
     import torch
 
     import sparse_index_paged_amd as qsa
@@ -468,14 +470,14 @@ def configs_mode(args):
         rng = np.random.default_rng(seed)
         return synth.pack([synth.draw_indices(rng, n, slots) for n in lengths])[0]
 
-    def eager_and_graph(call):
-        """Eager launches (which at small sizes measure the host's submission
-        rate) and a captured graph of 8 calls replayed (device time)."""
+    def eager_us(call):
         def run():
             for i in range(steps):
                 call(i)
         run()
-        us = time_calls(run, steps, reps)
+        return time_calls(run, steps, reps)
+
+    def graph_us(call):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(8):
@@ -488,10 +490,17 @@ def configs_mode(args):
                 g.replay()
         med, p10, p90 = time_calls(run8, 8 * n8, reps)
         del g
-        return us, {"graph_us_per_call": round(med, 3), "graph_us_p10": round(p10, 3),
-                    "graph_us_p90": round(p90, 3)}
+        return {"graph_us_per_call": round(med, 3), "graph_us_p10": round(p10, 3),
+                "graph_us_p90": round(p90, 3)}
 
-    def bf16_case(case, bank_seed, name, workload):
+    # Every configuration is set up first and timed eagerly (the figure that
+    # matches the default line), then replayed from captured graphs: once a
+    # graph has been captured and replayed in a process, later eager launches
+    # of the same kernel run about 3 us slower per call on this stack.
+    jobs = []  # (name, workload, gathered bytes, call(i), extra fields)
+    keep = []  # device tensors the calls use
+
+    def bf16_job(case, bank_seed, name, workload):
         slots = case.k_pool.shape[0]
         sels = [case.sel] + [bank_sel(bank_seed + i, case.lengths, slots) for i in range(1, 4)]
         q, k, v = case.q.cuda(), case.k_pool.cuda(), case.v_pool.cuda()
@@ -502,26 +511,34 @@ def configs_mode(args):
 
         def call(i):
             qsa.decode(q, k, v, sd[i % 4], cu, out=out, lse=lse)
-        b_kv = gathered_bytes(case.lengths, case.hkv)
-        us, us_graph = eager_and_graph(call)
-        emit(name, workload, b_kv, us, {"splits": qsa.plan(case.bs, case.hkv)[0], **us_graph})
+        jobs.append((name, workload, gathered_bytes(case.lengths, case.hkv), call,
+                     {"splits": qsa.plan(case.bs, case.hkv)[0]}))
+        keep.append((q, k, v, cu, sd, out, lse))
         return k, v
 
-    log("bs=1 TP1")
-    bf16_case(synth.case_bs1_tp1(), 101_000, "bs1_tp1_L128",
-              "bs=1 TP1 (24Q/2KV) bf16 pools [4096,2,256], 128 uniform indices")
-    log("bs=16 TP2 mixed")
-    bf16_case(synth.case_bs16_tp2_mixed(), 102_000, "bs16_tp2_mixed",
-              "bs=16 TP2 (12Q/1KV) bf16 pools [65536,1,256], 8 rows L~U[1,64], 4 rows 2055, "
-              "4 rows L~U[65,2054]")
-    log("bs=128 TP1 saturated")
-    k_big, v_big = bf16_case(synth.case_bs128_tp1_saturated(), 103_000, "bs128_tp1_saturated",
-                             "bs=128 TP1 (24Q/2KV) bf16 pools [262144,2,256], 2055 entries per "
-                             "row, 5% keys x8")
+    only = [o for o in (args.only or "").split(",") if o]
 
-    # ---- quantized pools, warm and cold
+    def want(name):
+        return not only or any(o in name for o in only)
+
+    k_big = v_big = None
+    if want("bs1_tp1_L128"):
+        bf16_job(synth.case_bs1_tp1(), 101_000, "bs1_tp1_L128",
+                 "bs=1 TP1 (24Q/2KV) bf16 pools [4096,2,256], 128 uniform indices")
+    if want("bs16_tp2_mixed"):
+        bf16_job(synth.case_bs16_tp2_mixed(), 102_000, "bs16_tp2_mixed",
+                 "bs=16 TP2 (12Q/1KV) bf16 pools [65536,1,256], 8 rows L~U[1,64], 4 rows 2055, "
+                 "4 rows L~U[65,2054]")
+    if want("bs128_tp1_saturated"):
+        k_big, v_big = bf16_job(synth.case_bs128_tp1_saturated(), 103_000, "bs128_tp1_saturated",
+                                "bs=128 TP1 (24Q/2KV) bf16 pools [262144,2,256], 2055 entries per "
+                                "row, 5% keys x8")
+
+    # ---- quantized pools, warm (one pool) and cold (4 copies rotating)
     for fmt, group, seed in (("fp8", 256, 1041), ("int8", 256, 1042), ("int4", 32, 1043)):
-        log(f"bs=64 TP1 {fmt}")
+        if not want(f"bs64_tp1_{fmt}_warm") and not want(f"bs64_tp1_{fmt}_cold"):
+            continue
+        log(f"bs=64 TP1 {fmt}: pools")
         case = synth.case_bs64_tp1_quantsrc(seed)
         kc, vc, ks, vs = quantized_pools(case.k_pool.cuda(), case.v_pool.cuda(), fmt, group,
                                          torch.float32)
@@ -533,22 +550,36 @@ def configs_mode(args):
         sd = [torch.from_numpy(s).cuda() for s in sels]
         out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
         lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
+        keep.append((copies, q, cu, sd, out, lse))
         b_kv = gathered_bytes(case.lengths, case.hkv, row_bytes(fmt, group, 4))
         for variant, ncopy in (("warm", 1), ("cold", 4)):
-            def call(i):
+            def call(i, fmt=fmt, group=group, ncopy=ncopy, copies=copies, q=q, cu=cu, sd=sd,
+                     out=out, lse=lse):
                 k_, v_, ks_, vs_ = copies[i % ncopy]
                 qsa.decode(q, k_, v_, sd[i % 4], cu, out=out, lse=lse, kv_format=fmt,
                            k_scale=ks_, v_scale=vs_, group_size=group)
-            us, us_graph = eager_and_graph(call)
-            emit(f"bs64_tp1_{fmt}_{variant}",
-                 f"bs=64 TP1 (24Q/2KV) {fmt} pools [131072,2,{FORMATS[fmt][0]}] + f32 scales per "
-                 f"{group} channels (written by qsa_kv_store), L~U[256,2055], "
-                 f"{ncopy} pool cop{'y' if ncopy == 1 else 'ies'} rotating", b_kv, us,
-                 {"kv_format": fmt, "group": group, "pool_copies": ncopy, **us_graph})
-        del copies, kc, vc, ks, vs
-        torch.cuda.empty_cache()
+            jobs.append((f"bs64_tp1_{fmt}_{variant}",
+                         f"bs=64 TP1 (24Q/2KV) {fmt} pools [131072,2,{FORMATS[fmt][0]}] + f32 scales "
+                         f"per {group} channels (written by qsa_kv_store), L~U[256,2055], "
+                         f"{ncopy} pool cop{'y' if ncopy == 1 else 'ies'} rotating", b_kv, call,
+                         {"kv_format": fmt, "group": group, "pool_copies": ncopy}))
+
+    eager = []
+    for name, _, _, call, _ in jobs:
+        log(f"{name}: eager")
+        eager.append(eager_us(call))
+    for (name, workload, b_kv, call, extra), us in zip(jobs, eager):
+        log(f"{name}: graph")
+        emit(name, workload, b_kv, us, {**extra, **graph_us(call)})
+    del keep, jobs
+    torch.cuda.empty_cache()
 
     # ---- graph-replay sweep over the bench's bf16 pools (TP2 uses KV head 0)
+    if not want("graph_sweep"):
+        return
+    if k_big is None:
+        case = synth.case_bs128_tp1_saturated()
+        k_big, v_big = case.k_pool.cuda(), case.v_pool.cuda()
     slots = k_big.shape[0]
     for hkv in (2, 1):
         kd, vd = (k_big, v_big) if hkv == 2 else (k_big[:, :1], v_big[:, :1])
@@ -632,6 +663,8 @@ def main():
     ap.add_argument("--split-target", type=int, default=None)
     ap.add_argument("--min-split-keys", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
+    ap.add_argument("--only", default=None,
+                    help="configs mode: comma-separated substrings of the configuration names to run")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
