@@ -188,8 +188,15 @@ __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthre
   if (tid < kGqa) p.lse[b * p.l_sb + (g * kGqa + tid) * p.l_sh] = __builtin_nanf("");
 }
 
+// The values the first loads depend on (the cu_seqlens and slot-id arrays,
+// the sizes that map a workgroup to its row) come as leading scalar
+// arguments, which the build asks the dispatcher to preload into scalar
+// registers at wave launch: the cu_seqlens -> slot ids chain then starts
+// at once, while the rest of the argument block is still being fetched.
 template <int FMT, int G, int W, bool SF16, bool A32>
-__global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params p) {
+__global__ void __launch_bounds__(64 * W, 8 / W)
+    qsa_decode_kernel(const int32_t *__restrict__ cu_lead, const int32_t *__restrict__ sel_lead, int bs_lead,
+                      int hkv_lead, int nsplit_lead, int msk_lead, int nsel_lead, const Params p) {
   using Part = typename Fmt<FMT>::Part;
   using GEO = Geo<FMT>;
   using LDS = Lds<W>;
@@ -218,29 +225,29 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   const int lchunk = lane % GEO::kLPR;       // its 16-byte chunk of each row
 
   // ---- workgroup -> (pair, split); splits of a pair share blockIdx % 8
-  const int npairs = p.bs * p.hkv;
+  const int npairs = bs_lead * hkv_lead;
   const int wg = blockIdx.x;
   const int local = wg >> 3;
-  const int pp = local / p.nsplit;
-  const int split = local - pp * p.nsplit;
+  const int pp = local / nsplit_lead;
+  const int split = local - pp * nsplit_lead;
   const int pair = pp * 8 + (wg & 7);
   if (pair >= npairs) return;
-  const int b = pair / p.hkv;
-  const int g = pair - b * p.hkv;
+  const int b = pair / hkv_lead;
+  const int g = pair - b * hkv_lead;
 
   // ---- live row length from device cu_seqlens
-  const int c0 = p.cu[b];
-  const int c1 = p.cu[b + 1];
+  const int c0 = cu_lead[b];
+  const int c1 = cu_lead[b + 1];
   const int L = c1 - c0;
-  if (c0 < 0 || L < 0 || L > kMaxSel || static_cast<int64_t>(c1) > p.n_sel) {
+  if (c0 < 0 || L < 0 || L > kMaxSel || c1 > nsel_lead) {
     if (split == 0) {
       write_nan_rows(p, b, g, tid, kThr);
       if (tid == 0) atomicOr(p.err, kErrRowRange);
     }
     return;
   }
-  int n_active = (L + p.min_split_keys - 1) / p.min_split_keys;
-  n_active = n_active < 1 ? 1 : (n_active > p.nsplit ? p.nsplit : n_active);
+  int n_active = (L + msk_lead - 1) / msk_lead;
+  n_active = n_active < 1 ? 1 : (n_active > nsplit_lead ? nsplit_lead : n_active);
   if (split >= n_active) return;
 
   // ---- this wave's contiguous slice of the list
@@ -276,7 +283,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   const uint8_t *vsbase = (NG > 0) ? vspool + sgrp * sizeof(Scale) : nullptr;
   const uint32_t ks_ss32 = static_cast<uint32_t>(p.ks_ss), vs_ss32 = static_cast<uint32_t>(p.vs_ss);
   const uint32_t sgrpb = static_cast<uint32_t>(sgrp * sizeof(Scale));
-  const int32_t *selw = p.sel + c0 + k0;
+  const int32_t *selw = sel_lead + c0 + k0;
   const uint32_t slots = static_cast<uint32_t>(p.slots > 0x7FFFFFFF ? 0x7FFFFFFF : p.slots);
   // tiered: ring rows of KV head g; a cold lane reads the 16 bytes at
   // 16 * (lchunk / 2) of the int4 row and a hot lane 16 * lchunk of the ring
@@ -345,7 +352,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // load in flight: tiles past the end re-read the last entry (cache hits),
   // and a wave with no entries reads cu[0] as its "slot id" (checked below
   // without raising the error bit; its rows are never processed).
-  const int32_t *ids = (nkeys > 0) ? selw : p.cu;
+  const int32_t *ids = (nkeys > 0) ? selw : cu_lead;
   const int jmax = (nkeys > 0) ? nkeys - 1 : 0;
   auto fetch_slots = [&](int t, int32_t (&sl)[NI]) {
 #pragma unroll
@@ -795,9 +802,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W) qsa_decode_kernel(const Params 
   // sees count n_active - 1 is the last one.
   auto st = [](float *ptr, float x) { __hip_atomic_store(ptr, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  const float *pbase = p.part + static_cast<int64_t>(pair) * p.nsplit * kPartFloats;
+  const float *pbase = p.part + static_cast<int64_t>(pair) * nsplit_lead * kPartFloats;
   if (wv < 4) {
-    float *part = p.part + (static_cast<int64_t>(pair) * p.nsplit + split) * kPartFloats;
+    float *part = p.part + (static_cast<int64_t>(pair) * nsplit_lead + split) * kPartFloats;
     if (wv == 0 && lane < 16) {
       st(part + lane, Mw);
       st(part + 16 + lane, sw);
@@ -951,10 +958,13 @@ __global__ void audit_kernel(const uint32_t *ctr, int n, uint32_t *accum) {
 
 template <int FMT, int G, bool SF16, bool A32>
 void launch_waves(const Params &p, dim3 grid, hipStream_t stream) {
+  const int nsel = p.n_sel > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(p.n_sel);
   if (p.waves == 8)
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16, A32>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16, A32>), grid, dim3(512), 0, stream, p.cu, p.sel,
+                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p);
   else
-    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16, A32>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16, A32>), grid, dim3(256), 0, stream, p.cu, p.sel,
+                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p);
 }
 
 template <int FMT, int G, bool SF16>
