@@ -11,8 +11,9 @@
 //
 // Two launches:
 //   * scores: a workgroup per 64 blocks of a row.  A lane holds its block's
-//     key row in registers; the heads are spread over the 4 waves, 8
-//     independent dot products per lane at a time, with the queries read
+//     key row in registers; the heads are spread over the waves (8 when
+//     the grid has at most one workgroup per CU, else 4), 8 independent
+//     dot products per lane at a time, with the queries read
 //     from LDS (broadcast).  The score is evaluated in the order the
 //     contract fixes -- per head one fused multiply-add per element in
 //     element order, then the weighted heads in head order -- so that the
@@ -30,7 +31,6 @@
 namespace qsa {
 namespace {
 
-constexpr int kScoreThreads = 256;
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kMaxIndexHeads = 64;
@@ -48,16 +48,17 @@ __device__ __forceinline__ int row_length(const IndexParams &p, int32_t t) {
 }
 
 // A workgroup scores 64 consecutive blocks of one row: lane l of every wave
-// takes block 64*blockIdx.x + l, and wave w the heads w, w + 4, ..., in
+// takes block 64*blockIdx.x + l, and wave w of W the heads w, w + W, ..., in
 // groups of 8 independent dot products (each one a fused multiply-add chain
 // in element order).  The row's queries are converted to fp32 once into
 // LDS (read back as broadcasts, 4 elements per read), and each key element
 // is converted once for 8 heads.  The per-head results meet in LDS, where
 // the first wave adds them up in head order.
-template <int DI>
-__global__ void __launch_bounds__(kScoreThreads) qsa_index_score_kernel(const IndexParams p) {
+template <int DI, int W>
+__global__ void __launch_bounds__(64 * W) qsa_index_score_kernel(const IndexParams p) {
   constexpr int NC = DI / 8;  // 16-byte chunks of a bf16 row
-  constexpr int kWaves = kScoreThreads / 64;
+  constexpr int kScoreThreads = 64 * W;
+  constexpr int kWaves = W;
   constexpr int kGroup = 8;   // dot products in flight per lane
   const int b = blockIdx.y;
   const int32_t t = p.ctx[b];
@@ -295,10 +296,20 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
 
 hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
   const dim3 sgrid(static_cast<unsigned>((p.max_blocks + 63) / 64), static_cast<unsigned>(p.bs));
+  // with at most one workgroup per CU the waves' LDS-latency-bound chains
+  // are the time, so 8 waves (8 heads each) halve them; larger grids keep
+  // 4 waves (16 heads each), which were faster there (MI355X, 8K-token rows,
+  // 64 heads of dim 128: 4 / 8 rows 34.2 / 34.9 -> 25.7 / 26.3 us; 32 rows
+  // 56.4 us with 4 waves against 64.7 with 8)
+  // (full 64-block columns only: the grid's last column is often empty and
+  // its workgroups return at once)
+  const bool eight = static_cast<int64_t>(p.max_blocks / 64) * p.bs <= 256;
   if (p.max_blocks > 0) {
-    switch (p.di) {
-      case 64: hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(kScoreThreads), 0, stream, p); break;
-      case 128: hipLaunchKernelGGL(qsa_index_score_kernel<128>, sgrid, dim3(kScoreThreads), 0, stream, p); break;
+    switch (p.di * 2 + (eight ? 1 : 0)) {
+      case 64 * 2: hipLaunchKernelGGL((qsa_index_score_kernel<64, 4>), sgrid, dim3(256), 0, stream, p); break;
+      case 64 * 2 + 1: hipLaunchKernelGGL((qsa_index_score_kernel<64, 8>), sgrid, dim3(512), 0, stream, p); break;
+      case 128 * 2: hipLaunchKernelGGL((qsa_index_score_kernel<128, 4>), sgrid, dim3(256), 0, stream, p); break;
+      case 128 * 2 + 1: hipLaunchKernelGGL((qsa_index_score_kernel<128, 8>), sgrid, dim3(512), 0, stream, p); break;
       default: return hipErrorInvalidValue;
     }
   }
