@@ -303,7 +303,10 @@ hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
   // 56.4 us with 4 waves against 64.7 with 8)
   // (full 64-block columns only: the grid's last column is often empty and
   // its workgroups return at once)
-  const bool eight = static_cast<int64_t>(p.max_blocks / 64) * p.bs <= 256;
+  // (64-dim heads hold half the key registers, so their 8-wave instance
+  // keeps more waves resident and stays ahead up to two workgroups per CU:
+  // 16 rows of dim 64, 26.0 -> 23.0 us)
+  const bool eight = static_cast<int64_t>(p.max_blocks / 64) * p.bs <= (p.di == 64 ? 512 : 256);
   if (p.max_blocks > 0) {
     switch (p.di * 2 + (eight ? 1 : 0)) {
       case 64 * 2: hipLaunchKernelGGL((qsa_index_score_kernel<64, 4>), sgrid, dim3(256), 0, stream, p); break;
