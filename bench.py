@@ -212,6 +212,115 @@ def copy_rate(nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / sec / 1e9
 
 
+_PROBE = None
+
+
+def probe_lib():
+    """libqsa_probe.so (the bare gather), or None if it was not built."""
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "sparse_index_paged_amd", "libqsa_probe.so")
+        if not os.path.exists(path):
+            return None
+        lib = ctypes.CDLL(path)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        lib.qsa_probe_gather.restype = ctypes.c_int
+        lib.qsa_probe_gather.argtypes = [P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, I64, I64, I64,
+                                         P, I64, P]
+        _PROBE = lib
+    return _PROBE
+
+
+def probe_time(pools, sels, hkv, row_b, steps, repeats, per_wave=64):
+    """Median us per call of the bare gather over `sels` (rotating) and
+    `pools` ([(k, v)] rotating, byte strides from the tensors)."""
+    import ctypes
+    import torch
+    lib = probe_lib()
+    n_max = max(int(s_.numel()) for s_ in sels)
+    blocks = -(-(-(-n_max // per_wave)) // 4)
+    sink = torch.zeros(blocks + 1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(i):
+        k_, v_ = pools[i % len(pools)]
+        s_ = sels[i % len(sels)]
+        eb = k_.element_size()
+        rc = lib.qsa_probe_gather(k_.data_ptr(), v_.data_ptr(), k_.stride(0) * eb, k_.stride(1) * eb, hkv,
+                                  row_b, s_.data_ptr(), s_.numel(), k_.shape[0], per_wave,
+                                  sink.data_ptr(), sink.numel(), stream)
+        if rc != 0:
+            raise RuntimeError(f"qsa_probe_gather failed ({rc})")
+
+    for i in range(len(pools) * len(sels)):
+        call(i)
+    torch.cuda.synchronize()
+
+    def run():
+        for i in range(steps):
+            call(i)
+    return time_calls(run, steps, repeats)[0]
+
+
+def gather_ceiling(args, k, v, sels, case, copies):
+    """The bench's own rows (bf16 pools, its index banks) read by the bare
+    gather: warm (one pool) and cold (the pool copies in turn)."""
+    if probe_lib() is None:
+        return None
+    b = gathered_bytes(case.lengths, case.hkv)
+    warm = probe_time([(k, v)], sels, case.hkv, 512, args.steps, args.repeats)
+    rec = {"kernel": "qsa_probe_gather (libqsa_probe.so)", "bytes_per_call": b,
+           "warm_us": round(warm, 3), "warm_GBps": round(b / (warm * 1e-6) / 1e9, 2)}
+    if len(copies) > 1:
+        cold = probe_time([(c_[0], c_[1]) for c_ in copies], sels, case.hkv, 512, args.steps,
+                          args.repeats)
+        rec.update(cold_us=round(cold, 3), cold_GBps=round(b / (cold * 1e-6) / 1e9, 2),
+                   pool_copies=len(copies))
+    return rec
+
+
+def gather_mode(args):
+    """The bare random-row gather (libqsa_probe.so) on the bench workload's
+    lists: rows of 512 B (bf16), 256 B (fp8 / int8) and 128 B (int4) from
+    [262144, hkv, row] pools, warm (one pool) and cold (--pool-copies pools
+    in turn), for a few entries-per-wave settings.  One JSON line each."""
+    import torch
+    import synth
+    if probe_lib() is None:
+        raise SystemExit("libqsa_probe.so is not built")
+    torch.cuda.set_device(0)
+    case = synth.case_bs128_tp1_saturated(bs=args.bs, hkv=args.hkv)
+    slots = case.k_pool.shape[0]
+    sels = [torch.from_numpy(case.sel).cuda()]
+    for i in range(1, args.banks):
+        rng = np.random.default_rng(103_000 + i)
+        sels.append(torch.from_numpy(synth.pack([synth.draw_indices(rng, n, slots)
+                                                 for n in case.lengths])[0]).cuda())
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for row_b in (512, 256, 128):
+        pools = [(torch.randint(0, 256, (slots, case.hkv, row_b), dtype=torch.uint8, device="cuda",
+                                generator=gen),
+                  torch.randint(0, 256, (slots, case.hkv, row_b), dtype=torch.uint8, device="cuda",
+                                generator=gen)) for _ in range(max(1, args.pool_copies))]
+        b = gathered_bytes(case.lengths, case.hkv, row_b)
+        for per_wave in (32, 64, 128, 256):
+            for variant, ps in (("warm", pools[:1]), ("cold", pools)):
+                if variant == "cold" and len(pools) < 2:
+                    continue
+                us = probe_time(ps, sels, case.hkv, row_b, args.steps, args.repeats, per_wave)
+                gbs = b / (us * 1e-6) / 1e9
+                print(json.dumps({"mode": "gather", "row_bytes": row_b, "per_wave": per_wave,
+                                  "variant": variant, "pool_copies": len(ps), "us_per_call": round(us, 3),
+                                  "bytes_per_call": b, "GBps": round(gbs, 1),
+                                  "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "workload": f"bs={case.bs} hkv={case.hkv}, 2055 uniform entries per "
+                                              f"row over {slots} slots, {len(sels)} index banks"}),
+                      flush=True)
+        del pools
+        torch.cuda.empty_cache()
+
+
 def copy_mode(args):
     """Plain device copy of known size (calibrates rocprofv3 byte counters)."""
     import torch
@@ -646,7 +755,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
-    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs"], default="decode")
+    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather"],
+                    default="decode")
     ap.add_argument("--ctx", type=int, default=8192, help="index mode: context tokens per row")
     ap.add_argument("--compress", type=int, default=4, help="index mode: compression ratio")
     ap.add_argument("--budget", type=int, default=2048, help="index mode: token budget")
@@ -663,6 +773,11 @@ def main():
     ap.add_argument("--split-target", type=int, default=None)
     ap.add_argument("--min-split-keys", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
+    ap.add_argument("--pool-copies", type=int, default=4,
+                    help="decode: also time the calls over this many pool copies in turn (cold); "
+                         "0 or 1 skips it")
+    ap.add_argument("--no-graph", action="store_true", help="decode: skip the graph-replay timing")
+    ap.add_argument("--no-probe", action="store_true", help="decode: skip the bare-gather ceiling")
     ap.add_argument("--only", default=None,
                     help="configs mode: comma-separated substrings of the configuration names to run")
     args = ap.parse_args()
@@ -685,6 +800,9 @@ def main():
         return
     if args.mode == "configs":
         configs_mode(args)
+        return
+    if args.mode == "gather":
+        gather_mode(args)
         return
 
     import numpy as np
@@ -773,17 +891,56 @@ def main():
     # banks rotating as in the eager loop) are also captured once into a HIP
     # graph and replayed, and that timing is reported instead
     eager_ms = timed(eager_steps)
-    reps_ms = eager_ms
-    timing_mode = "eager"
-    if args.timing == "graph":
+    warm_us = float(np.median(eager_ms)) * 1e3
+
+    # cold: the same calls over `pool_copies` copies of the pools, one copy
+    # per call in turn, so that consecutive calls read different pools (a
+    # model's layers each have their own pool) and the Infinity Cache cannot
+    # hold what a call re-reads from the previous ones
+    cold = None
+    copies = []
+    if args.pool_copies > 1 and tiered is None:
+        base = (k, v, qkw.get("k_scale"), qkw.get("v_scale"))
+        copies = [base] + [tuple(None if t is None else t.clone() for t in base)
+                           for _ in range(args.pool_copies - 1)]
+        torch.cuda.synchronize()
+
+        def cold_steps():
+            for i in range(args.steps):
+                kk, vv, ks_, vs_ = copies[i % len(copies)]
+                kw = dict(qkw)
+                if ks_ is not None:
+                    kw.update(k_scale=ks_, v_scale=vs_)
+                qsa.decode(q, kk, vv, sels[i % len(sels)], cu, out=out, lse=lse, **kw)
+        cold_steps()
+        cold_ms = timed(cold_steps)
+        cold = {"us_per_call": round(float(np.median(cold_ms)) * 1e3, 3),
+                "us_p10": round(float(np.percentile(cold_ms, 10)) * 1e3, 3),
+                "us_p90": round(float(np.percentile(cold_ms, 90)) * 1e3, 3),
+                "pool_copies": len(copies),
+                "pool_bytes_rotated": int(sum(t.numel() * t.element_size() for c_ in copies
+                                              for t in c_ if t is not None))}
+
+    # bare-gather ceiling (libqsa_probe.so): the same rows, nothing computed
+    probe = gather_ceiling(args, k, v, sels, case, copies) if (
+        fmt == "bf16" and not args.no_probe) else None
+
+    # graph replay of the same steps (after every eager timing: once a graph
+    # has been captured in a process, later eager launches run slower)
+    graph_ms = None
+    if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             eager_steps()
         graph.replay()
         torch.cuda.synchronize()
-        reps_ms = timed(graph.replay)
-        timing_mode = "graph"
+        graph_ms = timed(graph.replay)
         del graph
+    reps_ms = eager_ms
+    timing_mode = "eager"
+    if args.timing == "graph":
+        reps_ms = graph_ms
+        timing_mode = "graph"
     ms_per_step = float(np.median(reps_ms))
     counters_ok = all(c == 0 for c in qsa.debug_counters())
 
@@ -806,7 +963,23 @@ def main():
                      f"{hot_share:.1%} of entries read the ring)")
     else:
         pool_desc = f"{fmt} pools (group {group}, {args.scale_dtype} scales, written by qsa_kv_store)"
+    if cold is not None:
+        cg = b_kv / (cold["us_per_call"] * 1e-6) / 1e9
+        cold.update(GBps=round(cg, 2), frac=round(cg / HBM_PEAK_GBS, 4))
 
+    timing = {"mode": timing_mode, "repeats": len(reps_ms), "steps_per_repeat": args.steps,
+              "us_per_call_eager_median": round(warm_us, 3),
+              "us_per_call_p10": round(float(np.percentile(reps_ms, 10)) * 1e3, 3),
+              "us_per_call_median": round(ms_per_step * 1e3, 3),
+              "us_per_call_p90": round(float(np.percentile(reps_ms, 90)) * 1e3, 3)}
+    if graph_ms is not None:
+        timing["us_per_call_graph_median"] = round(float(np.median(graph_ms)) * 1e3, 3)
+        timing["graph_GBps"] = round(b_kv / (float(np.median(graph_ms)) * 1e-3) / 1e9, 2)
+    # the bf16 path is bound by the gather (committed counters: traffic equal
+    # to the algorithmic bytes, MFMA busy a few percent); the quantized and
+    # tiered paths are bound by per-tile work, not established as a single
+    # unit's roofline
+    bound = "hbm" if fmt == "bf16" else None
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -816,11 +989,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_call": round(ms_per_step * 1e3, 3),
-        "timing": {"mode": timing_mode, "repeats": len(reps_ms), "steps_per_repeat": args.steps,
-                   "us_per_call_eager_median": round(float(np.median(eager_ms)) * 1e3, 3),
-                   "us_per_call_p10": round(float(np.percentile(reps_ms, 10)) * 1e3, 3),
-                   "us_per_call_median": round(ms_per_step * 1e3, 3),
-                   "us_per_call_p90": round(float(np.percentile(reps_ms, 90)) * 1e3, 3)},
+        "timing": timing,
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -838,18 +1007,30 @@ def main():
             "gathered_kv_bytes_per_call": b_kv, "counters_at_rest": counters_ok,
         },
         "roofline": {
-            "bound": "hbm",
+            "bound": bound,
             "achieved": round(gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_source": (f"{os.path.relpath(TRAFFIC_FILE, ROOT)} (rocprofv3 --pmc FETCH_SIZE / "
+                               f"WRITE_SIZE, copy-calibrated) for kernel source sha {kernel_sha()}"
+                               if traffic is not None else None),
             "mfma_busy_pct": committed_mfma_busy() if fmt == "bf16" else None,
+            "mfma_busy_source": (f"{os.path.relpath(COUNTERS_FILE, ROOT)} for kernel source sha "
+                                 f"{kernel_sha()}" if fmt == "bf16" and committed_mfma_busy() is not None
+                                 else None),
             "algorithmic_bytes_per_launch": b_kv,
             "kernel": f"qsa_decode_kernel<{fmt}>",
+            "cold": cold,
+            "gather_ceiling": probe,
         },
         "cpu_baseline": None,
     }
+    if probe is not None:
+        line["roofline"]["frac_of_gather_ceiling"] = round(gbs / probe["warm_GBps"], 4)
+        if cold is not None and probe.get("cold_GBps"):
+            cold["frac_of_gather_ceiling"] = round(cold["GBps"] / probe["cold_GBps"], 4)
     if not args.no_copy:
         cr = copy_rate()
         line["roofline"]["copy_GBps"] = round(cr, 1)

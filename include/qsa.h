@@ -48,6 +48,12 @@
  *     or grown on first use; under capture it must already be large enough
  *     (qsa_workspace_reserve / qsa_index_reserve on the capturing stream,
  *     QSA_ERR_WORKSPACE otherwise).  The error word is per workspace.
+ *     A workspace never frees memory that a captured graph may still use:
+ *     its counters and error word never move, and when its partials or
+ *     index scores grow (a larger call, or a larger reservation) the old
+ *     buffer is kept until qsa_workspace_detach / qsa_workspace_release.
+ *     Graphs captured before a growth therefore replay correctly; graphs
+ *     that use a workspace must not be replayed after it is released.
  *     (Page "[Kernel][WIP] Integrate native FlashInfer SM70 batch GDN and
  *     QSA probes", change summary: scratch stays local to the call rather
  *     than shared between callers; here a stream's own workspace is that.)
@@ -281,10 +287,11 @@ qsa_status qsa_index(const qsa_tensor *q_index, const qsa_tensor *head_weights,
 qsa_status qsa_index_reserve(int max_bs, int max_blocks, hipStream_t stream);
 
 /* Create (or grow) the workspace `stream` uses for calls with up to max_bs
- * rows and the given head layout, and zero its counters and error word.
- * Call it on the capturing stream before capturing a graph that contains
- * qsa_decode.  Replacing an existing workspace synchronises `stream` (a
- * private workspace) or the device (the shared one). */
+ * rows and the given head layout, and zero its counters and error word
+ * (one small kernel on `stream`).  Call it on the capturing stream before
+ * capturing a graph that contains qsa_decode.  Growing keeps the old
+ * partials allocated (see the conventions above) and does not
+ * synchronise. */
 qsa_status qsa_workspace_reserve(int max_bs, int hq, int hkv, hipStream_t stream);
 
 /* Give `stream` a private workspace on the current device, so that its
@@ -310,7 +317,10 @@ qsa_status qsa_workspace_release(void);
 /* Bytes held by the current device's workspaces, shared and private. */
 int64_t qsa_workspace_bytes(void);
 
-/* Thread-local message describing the last failed call ("" if none). */
+/* Thread-local message describing the last failed call ("" if none): the
+ * descriptive contract error of page "fix(qsa): restore SM121 correctness
+ * with Humanize and Kernel Design Agent", section "Changes" (an unsupported
+ * call names the field it violates instead of silently running). */
 const char *qsa_last_error(void);
 
 /* Split plan qsa_decode uses for (bs, hkv): number of splits per (row, KV
@@ -334,7 +344,12 @@ qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);
 
 /* Device pointer and count of the split counters (uint32, zero between
- * calls) of the workspace `stream` uses, for audits after a launch. */
+ * calls) of the workspace `stream` uses, for audits after a launch.  The
+ * counters are the ones of page "fix(qsa): restore SM121 correctness with
+ * Humanize and Kernel Design Agent", section "Optimized kernel": the final
+ * split of a (row, KV head) resets its counter in the same launch, so every
+ * counter reads zero between calls.  The pointer stays valid until the
+ * workspace is detached or released. */
 qsa_status qsa_debug_counters(const uint32_t **dev_ptr, int *n, hipStream_t stream);
 
 /* Copy the first n split counters of the workspace `stream` uses to host

@@ -44,9 +44,21 @@ ERRORS = {1: "bad arguments", 2: "bad cu_seqlens", 3: "row longer than 2055",
           6: "block table entry out of range"}
 
 
-def build() -> str:
+def build(sanitize: bool = False) -> str:
     """Compile qsa_oracle.c and qsa_index_oracle.c with gcc (-O2, no
-    fast-math, no floating-point contraction, OpenMP)."""
+    fast-math, no floating-point contraction, OpenMP) into liboracle.so.
+    With sanitize=True compile them instead into one object file with
+    AddressSanitizer and UndefinedBehaviorSanitizer (for a checking driver
+    to link) and return its path."""
+    if sanitize:
+        out_dir = os.path.join(os.path.dirname(_HERE), "_build", "sanitize")
+        os.makedirs(out_dir, exist_ok=True)
+        obj = os.path.join(out_dir, "oracle_asan.o")
+        cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=undefined", "-fopenmp", "-std=c11", "-ffp-contract=off",
+               "-r", "-nostdlib", "-o", obj, _SRC, _SRC_INDEX]
+        subprocess.run(cmd, check=True)
+        return obj
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off",
            "-o", _LIB + ".tmp", _SRC, _SRC_INDEX, "-lm"]
     subprocess.run(cmd, check=True)

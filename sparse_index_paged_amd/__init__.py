@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     QsaError,
     abi_version,
     debug_audit_counters,
+    debug_counter_ptr,
     debug_counters,
     debug_device_error,
     decode,
@@ -38,7 +39,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "decode", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_attach",
     "workspace_detach", "workspace_reset", "workspace_release",
-    "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_audit_counters",
+    "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_counter_ptr", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",
     "ABI_VERSION",
 ]

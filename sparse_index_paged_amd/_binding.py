@@ -352,6 +352,15 @@ def debug_counters(stream=None) -> list[int]:
     return list(buf)
 
 
+def debug_counter_ptr(stream=None) -> tuple[int, int]:
+    """(device address, count) of the split counters of the workspace
+    `stream` uses."""
+    ptr, n = ctypes.c_void_p(), ctypes.c_int()
+    _check(load_library().qsa_debug_counters(ctypes.byref(ptr), ctypes.byref(n),
+                                             _stream_handle(stream)))
+    return int(ptr.value or 0), n.value
+
+
 def debug_audit_counters(accum, stream=None):
     """Enqueue: accum[0] += sum(counters).  accum is a 1-element int32 /
     uint32 device tensor."""

@@ -28,7 +28,42 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# Host-side sanitizer build of the library's host code (contract checks,
+# plan, workspace bookkeeping): AddressSanitizer and UndefinedBehavior-
+# Sanitizer on the host compilation only; the device pass is unchanged.
+SANITIZE_DIR = os.path.join(ROOT, "_build", "sanitize")
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def build_sanitize(verbose: bool = False) -> str:
+    """Compile the host API (qsa_api.hip) with the host sanitizers into an
+    object file that a driver links against; returns its path."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    obj = os.path.join(SANITIZE_DIR, "qsa_api_host.o")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++20", "-fPIC", "-Wall",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), *SANITIZE_FLAGS, "-c",
+           os.path.join(CSRC, "qsa_api.hip"), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the sanitizer object of qsa_api.hip")
+    return obj
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libqsa.so; with sanitize=True build the host-sanitizer object
+    of the host API instead (see build_sanitize)."""
+    if sanitize:
+        return build_sanitize(verbose)
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *SOURCES]
@@ -45,7 +80,26 @@ def build(verbose: bool = False) -> str:
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
+
+
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Build the measurement helper libqsa_probe.so (the bare gather)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, os.path.join(CSRC, "qsa_probe.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libqsa_probe.so")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

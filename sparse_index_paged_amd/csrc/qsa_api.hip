@@ -128,8 +128,20 @@ int waves_for(int fmt, int64_t workgroups) {
 // kMaxAttached private workspaces, each bound to one stream by
 // qsa_workspace_attach.  Calls on different streams run concurrently only
 // when their workspaces differ.
+//
+// Captured graphs keep the device addresses of the buffers their calls
+// used, so nothing a capture may reference is freed before the workspace
+// itself goes (qsa_workspace_detach / qsa_workspace_release):
+//   * the counters and the error word are one fixed-size allocation made
+//     when the workspace is created; they never move, so the error word
+//     stays sticky and an audit pointer stays valid;
+//   * when the partials or the index scores grow, the new buffer replaces
+//     the old one for later calls and the old one is retired, not freed.
+// Growth is geometric (at least doubling), so a workspace retires at most
+// a few dozen buffers over its life.
 constexpr int kMaxDevices = 64;
 constexpr int kMaxAttached = 64;
+constexpr int kMaxRetired = 64;
 
 struct Workspace {
   float *part = nullptr;
@@ -138,6 +150,9 @@ struct Workspace {
   int64_t n_ctr = 0;
   float *iscores = nullptr;   // indexer block scores
   int64_t iscore_floats = 0;
+  void *retired[kMaxRetired] = {};  // replaced buffers, freed with the workspace
+  int n_retired = 0;
+  int64_t retired_bytes = 0;
 };
 
 struct DeviceWorkspaces {
@@ -184,20 +199,43 @@ Workspace &workspace_of(int dev, hipStream_t stream, bool *own = nullptr) {
   return i >= 0 ? g_ws[dev].own[i] : g_ws[dev].shared;
 }
 
+// Free every buffer of a workspace, retired ones included (the caller has
+// synchronised whatever could still use it).
 void free_workspace(Workspace &ws) {
   if (ws.part) (void)hipFree(ws.part);
   if (ws.words) (void)hipFree(ws.words);
   if (ws.iscores) (void)hipFree(ws.iscores);
+  for (int i = 0; i < ws.n_retired; ++i) (void)hipFree(ws.retired[i]);
   ws = Workspace{};
 }
 
-// Wait until nothing can still use a workspace that is about to be replaced:
-// its own stream for a private one, the whole device for the shared one.
-hipError_t quiesce(bool own, hipStream_t stream) {
-  return own ? hipStreamSynchronize(stream) : hipDeviceSynchronize();
+// Replace *buf (of *have floats) by a new buffer of at least `need` floats,
+// retiring the old one.  Growth at least doubles the size.
+template <typename T>
+qsa_status grow_buffer(Workspace &ws, T **buf, int64_t *have, int64_t need, const char *fn,
+                       const char *what) {
+  if (*buf != nullptr && ws.n_retired >= kMaxRetired)
+    return fail(QSA_ERR_WORKSPACE, "%s: the workspace has replaced its %s %d times; "
+                "call qsa_workspace_reserve with the largest size first", fn, what, kMaxRetired);
+  int64_t n = need;
+  if (*buf != nullptr && n < 2 * *have) n = 2 * *have;
+  void *ptr = nullptr;
+  if (hipMalloc(&ptr, static_cast<size_t>(n) * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(QSA_ERR_HIP, "%s: hipMalloc of %lld bytes for the %s failed", fn,
+                static_cast<long long>(n * static_cast<int64_t>(sizeof(T))), what);
+  }
+  if (*buf != nullptr) {
+    ws.retired[ws.n_retired++] = *buf;
+    ws.retired_bytes += *have * static_cast<int64_t>(sizeof(T));
+  }
+  *buf = static_cast<T *>(ptr);
+  *have = n;
+  return QSA_OK;
 }
 
-// Ensure the workspace `stream` uses on `dev` holds `floats` partial floats.
+// Ensure the workspace `stream` uses on `dev` exists (counters and error
+// word) and holds `floats` partial floats.
 qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool allow_alloc,
                             Workspace **out, const char *fn = "qsa_decode") {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -213,30 +251,21 @@ qsa_status ensure_workspace(int dev, int64_t floats, hipStream_t stream, bool al
                 "partial floats, %lld needed; call qsa_workspace_reserve before capture",
                 fn, own ? "stream's own" : "shared", dev, static_cast<long long>(ws.part_floats),
                 static_cast<long long>(floats));
-  if (ws.words != nullptr) {
-    if (quiesce(own, stream) != hipSuccess) return fail(QSA_ERR_HIP, "workspace: synchronisation failed");
-    (void)hipFree(ws.part);
-    (void)hipFree(ws.words);
-    float *keep = ws.iscores;
-    const int64_t keep_n = ws.iscore_floats;
-    ws = Workspace{};
-    ws.iscores = keep;
-    ws.iscore_floats = keep_n;
+  if (ws.words == nullptr) {
+    void *words = nullptr;
+    if (hipMalloc(&words, static_cast<size_t>(kCtrWords + 1) * sizeof(uint32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(QSA_ERR_HIP, "%s: hipMalloc of the workspace counters failed", fn);
+    }
+    ws.words = static_cast<uint32_t *>(words);
+    ws.n_ctr = kCtrWords;
+    if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
+      return fail(QSA_ERR_HIP, "%s: zeroing the workspace counters failed", fn);
   }
-  void *part = nullptr, *words = nullptr;
-  if (hipMalloc(&part, static_cast<size_t>(floats) * sizeof(float)) != hipSuccess)
-    return fail(QSA_ERR_HIP, "workspace: hipMalloc of %lld bytes failed",
-                static_cast<long long>(floats * 4));
-  if (hipMalloc(&words, static_cast<size_t>(kCtrWords + 1) * sizeof(uint32_t)) != hipSuccess) {
-    (void)hipFree(part);
-    return fail(QSA_ERR_HIP, "workspace: hipMalloc of the counters failed");
+  if (ws.part_floats < floats) {
+    qsa_status st = grow_buffer(ws, &ws.part, &ws.part_floats, floats, fn, "split partials");
+    if (st != QSA_OK) return st;
   }
-  ws.part = static_cast<float *>(part);
-  ws.part_floats = floats;
-  ws.words = static_cast<uint32_t *>(words);
-  ws.n_ctr = kCtrWords;
-  if (qsa::launch_fill_u32(ws.words, kCtrWords + 1, 0u, stream) != hipSuccess)
-    return fail(QSA_ERR_HIP, "workspace: zeroing the counters failed");
   *out = &ws;
   return QSA_OK;
 }
@@ -257,17 +286,8 @@ qsa_status ensure_index_scores(int dev, int64_t floats, hipStream_t stream, bool
                 "score floats, %lld needed; call qsa_index_reserve before capture", fn,
                 own ? "stream's own" : "shared", dev, static_cast<long long>(ws.iscore_floats),
                 static_cast<long long>(floats));
-  if (ws.iscores != nullptr) {
-    if (quiesce(own, stream) != hipSuccess) return fail(QSA_ERR_HIP, "%s: synchronisation failed", fn);
-    (void)hipFree(ws.iscores);
-    ws.iscores = nullptr;
-    ws.iscore_floats = 0;
-  }
-  void *ptr = nullptr;
-  if (hipMalloc(&ptr, static_cast<size_t>(floats) * sizeof(float)) != hipSuccess)
-    return fail(QSA_ERR_HIP, "%s: hipMalloc of %lld bytes failed", fn, static_cast<long long>(floats * 4));
-  ws.iscores = static_cast<float *>(ptr);
-  ws.iscore_floats = floats;
+  if ((st = grow_buffer(ws, &ws.iscores, &ws.iscore_floats, floats, fn, "index scores")) != QSA_OK)
+    return st;
   *out = &ws;
   return QSA_OK;
 }
@@ -1023,7 +1043,8 @@ int64_t qsa_workspace_bytes(void) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   auto bytes = [](const Workspace &ws) {
-    return ws.part_floats * 4 + (ws.words ? (kCtrWords + 1) * 4 : 0) + ws.iscore_floats * 4;
+    return ws.part_floats * 4 + (ws.words ? (kCtrWords + 1) * 4 : 0) + ws.iscore_floats * 4 +
+           ws.retired_bytes;
   };
   const DeviceWorkspaces &d = g_ws[dev];
   int64_t total = bytes(d.shared);

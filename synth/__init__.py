@@ -179,17 +179,33 @@ def sweep_lengths(rng: np.random.Generator, bs: int, kind: str) -> list[int]:
     raise ValueError(kind)
 
 
+def sweep_empty_rows(bank: int, bs: int) -> list[int]:
+    """Rows a sweep bank leaves empty: none, except in every fourth bank
+    (bank % 4 == 3), which empties row 7*bank mod bs and, from bs = 4, also
+    the row half a batch further.  At bs = 1 such a bank is an all-empty
+    call."""
+    if bank % 4 != 3:
+        return []
+    rows = {(7 * bank) % bs}
+    if bs >= 4:
+        rows.add((7 * bank + bs // 2) % bs)
+    return sorted(rows)
+
+
 def sweep_bank(seed: int, bs: int, kind: str, slots: int, banks: int = 8,
                dup_prob: float = 0.1):
     """``banks`` different (sel, cu) packings for one sweep point, each with
-    duplicate runs (probability 0.1 per entry, runs of 2..8).  All banks are
-    padded to the same sel length so they can be copied into one captured
-    buffer."""
+    duplicate runs (probability 0.1 per entry, runs of 2..8), and with the
+    zero-length rows of sweep_empty_rows (the lists are drawn first and then
+    emptied, so the other rows keep their draws).  All banks are padded to
+    the same sel length so they can be copied into one captured buffer."""
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(banks):
+    for i in range(banks):
         lens = sweep_lengths(rng, bs, kind)
         lists = [draw_indices(rng, n, slots, dup_prob) for n in lens]
+        for j in sweep_empty_rows(i, bs):
+            lists[j] = lists[j][:0]
         out.append(pack(lists))
     cap = max(s.shape[0] for s, _ in out)
     padded = []
