@@ -172,6 +172,35 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool,
                       qsa_tensor *out, qsa_tensor *lse, hipStream_t stream);
 
 /*
+ * qsa_decode_noalloc -- qsa_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, same contract and the same kernel as
+ * qsa_decode; the split partials, split counters and error word live in a
+ * fixed scratch array compiled into the library (one per device, 8 MiB of
+ * partials), so no call allocates anything, the library's workspaces are
+ * never created or used, and the stream needs no reservation.
+ *
+ *   - A call whose split plan needs more than 8 MiB of partials (only
+ *     possible with tuning options that force many splits; the default plan
+ *     needs at most 6.2 MB) returns QSA_ERR_WORKSPACE; nothing is launched.
+ *   - The first call on a device takes the scratch's device address and
+ *     zeroes its counters (one small kernel on `stream`); it must not be
+ *     made while `stream` is capturing (QSA_ERR_WORKSPACE).  Later calls,
+ *     captured or not, launch exactly one kernel.
+ *   - Every call on a device shares that device's scratch: calls that may
+ *     overlap in time (different streams without ordering between them)
+ *     race on it and must not be made.  Each split counter is zero again
+ *     when its launch ends, as with qsa_decode.
+ *   - Device-side errors (a row longer than 2055, a bad cu_seqlens entry,
+ *     a slot id out of range) give NaN rows as with qsa_decode; their error
+ *     bits go to the scratch's own word, which no debug call reads.
+ */
+qsa_status qsa_decode_noalloc(const qsa_tensor *q, const qsa_tensor *k_pool,
+                              const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
+                              const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                              qsa_tensor *out, qsa_tensor *lse, hipStream_t stream);
+
+/*
  * qsa_kv_store -- quantize new K/V rows and scatter them into the pools
  * (one kernel launch; page "feat(qsa): quantized KV pools with
  * dequant-on-gather (fp8/int8/int4)", part 4 "Modifications": the write is

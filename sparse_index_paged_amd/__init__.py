@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     debug_counters,
     debug_device_error,
     decode,
+    decode_noalloc,
     decode_tiered,
     get_option,
     index,
@@ -37,7 +38,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "decode", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_attach",
+    "decode", "decode_noalloc", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_attach",
     "workspace_detach", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_counter_ptr", "debug_audit_counters",
     "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError",

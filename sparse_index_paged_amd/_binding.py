@@ -16,7 +16,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_CONTRACT", 2: "QSA_ERR_ARG", 3: "QSA_ERR_WORK
           4: "QSA_ERR_HIP"}
 
 EXPORTS = (
-    "qsa_decode", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_index",
+    "qsa_decode", "qsa_decode_noalloc", "qsa_kv_store", "qsa_decode_tiered", "qsa_kv_store_tiered", "qsa_index",
     "qsa_index_reserve", "qsa_workspace_reserve", "qsa_workspace_attach", "qsa_workspace_detach",
     "qsa_workspace_reset",
     "qsa_workspace_release", "qsa_workspace_bytes", "qsa_last_error", "qsa_plan", "qsa_set_option", "qsa_get_option",
@@ -72,6 +72,8 @@ def load_library():
     T = P(QsaTensor)
     lib.qsa_decode.restype = ctypes.c_int
     lib.qsa_decode.argtypes = [T, T, T, P(QsaKvScales), T, T, T, T, ctypes.c_void_p]
+    lib.qsa_decode_noalloc.restype = ctypes.c_int
+    lib.qsa_decode_noalloc.argtypes = [T, T, T, P(QsaKvScales), T, T, T, T, ctypes.c_void_p]
     lib.qsa_kv_store.restype = ctypes.c_int
     lib.qsa_kv_store.argtypes = [T, T, T, T, T, P(QsaKvScales), ctypes.c_void_p]
     lib.qsa_decode_tiered.restype = ctypes.c_int
@@ -169,7 +171,8 @@ def _stream_handle(stream):
 
 
 def decode(q, k_pool, v_pool, sel, cu_seqlens, *, out=None, lse=None, kv_format: str = "bf16",
-           k_scale=None, v_scale=None, group_size: int | None = None, stream=None):
+           k_scale=None, v_scale=None, group_size: int | None = None, stream=None,
+           _noalloc: bool = False):
     """Packed QSA decode (one kernel launch on `stream`, default torch's
     current stream).  Returns (out [bs, Hq, 256] bf16, lse [bs, Hq] fp32).
 
@@ -189,12 +192,23 @@ def decode(q, k_pool, v_pool, sel, cu_seqlens, *, out=None, lse=None, kv_format:
     vd = describe(v_pool, kv_format)
     sd, cd = describe(sel), describe(cu_seqlens)
     scales = _scales(kv_format, k_scale, v_scale, group_size)
-    st = lib.qsa_decode(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
-                        ctypes.byref(scales) if scales is not None else None,
-                        ctypes.byref(sd), ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
-                        _stream_handle(stream))
+    entry = lib.qsa_decode_noalloc if _noalloc else lib.qsa_decode
+    st = entry(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+               ctypes.byref(scales) if scales is not None else None,
+               ctypes.byref(sd), ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
+               _stream_handle(stream))
     _check(st)
     return out, lse
+
+
+def decode_noalloc(q, k_pool, v_pool, sel, cu_seqlens, *, out, lse, kv_format: str = "bf16",
+                   k_scale=None, v_scale=None, group_size: int | None = None, stream=None):
+    """qsa_decode_noalloc: the same decode with the split scratch in the
+    library's fixed per-device array (nothing is allocated, by the library
+    or here: out and lse must be given)."""
+    return decode(q, k_pool, v_pool, sel, cu_seqlens, out=out, lse=lse, kv_format=kv_format,
+                  k_scale=k_scale, v_scale=v_scale, group_size=group_size, stream=stream,
+                  _noalloc=True)
 
 
 def _scales(kv_format, k_scale, v_scale, group_size):

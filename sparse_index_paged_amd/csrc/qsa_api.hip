@@ -13,28 +13,27 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
-#include <string>
 
 #include "../../include/qsa.h"
 #include "qsa_internal.h"
 
 namespace {
 
-thread_local std::string g_last_error;
+// The message of the last failed call on this thread (a fixed buffer, so
+// reporting an error allocates nothing).
+thread_local char g_last_error[512];
 
 qsa_status fail(qsa_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 qsa_status fail(qsa_status st, const char *fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
 qsa_status ok() {
-  g_last_error.clear();
+  g_last_error[0] = '\0';
   return QSA_OK;
 }
 
@@ -465,11 +464,12 @@ qsa_status check_query(const char *fn, const qsa_tensor *q) {
   return QSA_OK;
 }
 
-// Query, outputs, index lists, workspace and the pool-independent launch
-// parameters of one decode call (the pool fields are left to the caller).
+// Query, outputs and index lists of one decode call and the pool- and
+// scratch-independent launch parameters (pool fields are left to the
+// caller, the split scratch to attach_workspace / the scratch array).
 qsa_status prepare_decode(const char *fn, const qsa_tensor *q, int64_t hkv,
                           const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
-                          qsa_tensor *out, qsa_tensor *lse, hipStream_t stream, qsa::Params *pp) {
+                          qsa_tensor *out, qsa_tensor *lse, qsa::Params *pp) {
   qsa_status st;
   if ((st = check_query(fn, q)) != QSA_OK) return st;
   const int64_t bs = q->shape[0], hq = q->shape[1];
@@ -496,14 +496,6 @@ qsa_status prepare_decode(const char *fn, const qsa_tensor *q, int64_t hkv,
     return fail(QSA_ERR_CONTRACT, "%s: cu_seqlens must have bs + 1 = %lld entries, got %lld", fn,
                 static_cast<long long>(bs + 1), static_cast<long long>(cu_seqlens->shape[0]));
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
-  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
-  const int splits = plan_splits(static_cast<int>(bs), static_cast<int>(hkv));
-  const int64_t need = bs * hkv * splits * static_cast<int64_t>(qsa::kPartFloats);
-  Workspace *ws = nullptr;
-  if ((st = ensure_workspace(dev, need, stream, !stream_capturing(stream), &ws, fn)) != QSA_OK) return st;
-
   qsa::Params &p = *pp;
   p.q = static_cast<const __bf16 *>(q->data);
   p.q_sb = q->stride[0];
@@ -519,11 +511,28 @@ qsa_status prepare_decode(const char *fn, const qsa_tensor *q, int64_t hkv,
   p.l_sh = lse->stride[1];
   p.bs = static_cast<int>(bs);
   p.hkv = static_cast<int>(hkv);
-  p.nsplit = splits;
+  p.nsplit = plan_splits(p.bs, p.hkv);
   p.min_split_keys = static_cast<int>(g_min_split_keys.load() > 4096 ? 4096 : g_min_split_keys.load());
-  p.part = ws->part;
-  p.ctr = ws->words;
-  p.err = ws->words + kCtrWords;
+  return QSA_OK;
+}
+
+// Split partials the plan of a prepared call needs.
+int64_t partial_floats_of(const qsa::Params &p) {
+  return static_cast<int64_t>(p.bs) * p.hkv * p.nsplit * qsa::kPartFloats;
+}
+
+// The split scratch of the workspace `stream` uses (created or grown
+// outside capture) into a prepared call.
+qsa_status attach_workspace(const char *fn, hipStream_t stream, qsa::Params *p) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  Workspace *ws = nullptr;
+  qsa_status st = ensure_workspace(dev, partial_floats_of(*p), stream, !stream_capturing(stream), &ws, fn);
+  if (st != QSA_OK) return st;
+  p->part = ws->part;
+  p->ctr = ws->words;
+  p->err = ws->words + kCtrWords;
   return QSA_OK;
 }
 
@@ -672,13 +681,84 @@ bool tiered_fits_32(const qsa_tiered_pool *tp, const TieredDesc &td, qsa::Params
   return true;
 }
 
+// Validated pools + the prepared call of qsa_decode / qsa_decode_noalloc
+// (everything but the split scratch).
+qsa_status prepare_pooled_decode(const char *fn, const qsa_tensor *q, const qsa_tensor *k_pool,
+                                 const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
+                                 const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                                 qsa_tensor *out, qsa_tensor *lse, qsa::Params *pp, PoolDesc *pd) {
+  qsa_status st;
+  if ((st = check_query(fn, q)) != QSA_OK) return st;
+  if ((st = check_pools(fn, k_pool, v_pool, kv_scales, pd)) != QSA_OK) return st;
+  if ((st = prepare_decode(fn, q, pd->hkv, sel_indices, cu_seqlens, out, lse, pp)) != QSA_OK) return st;
+  qsa::Params &p = *pp;
+  p.k = static_cast<const uint8_t *>(k_pool->data);
+  p.v = static_cast<const uint8_t *>(v_pool->data);
+  p.k_ss = k_pool->stride[0] * pd->eb;
+  p.k_sh = k_pool->stride[1] * pd->eb;
+  p.v_ss = v_pool->stride[0] * pd->eb;
+  p.v_sh = v_pool->stride[1] * pd->eb;
+  p.ks = pd->ks;
+  p.vs = pd->vs;
+  p.ks_ss = pd->ks_ss;
+  p.ks_sh = pd->ks_sh;
+  p.vs_ss = pd->vs_ss;
+  p.vs_sh = pd->vs_sh;
+  p.scale_f16 = pd->scale_f16;
+  p.a32 = addresses_fit_32(*pd, k_pool, v_pool) ? 1 : 0;
+  p.slots = pd->slots;
+  p.waves = waves_for(pd->fmt, plan_workgroups(p.bs, p.hkv, p.nsplit));
+  return QSA_OK;
+}
+
+// ---- the scratch of qsa_decode_noalloc -------------------------------------
+// A file-scope device array: split partials for at most kScratchPartFloats
+// floats (8 MiB, enough for the default split plan of every bs and head
+// layout: at most 6.2 MB), then the split counters and an error word.  The
+// loader zero-fills it on every device, each split's counter is back at zero
+// when its launch ends, and the first call on a device zeroes the words once
+// more.  In host code `scratch` only names the array: its device address on
+// each device comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to kernels.
+constexpr int64_t kScratchPartFloats = int64_t{2} << 20;
+constexpr int64_t kScratchBytes = kScratchPartFloats * 4 + (kCtrWords + 1) * 4;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+uint8_t *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (taken, and its words
+// zeroed on `stream`, on the first call per device; refused under capture).
+qsa_status scratch_of_device(const char *fn, hipStream_t stream, uint8_t **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_HIP, "%s: no HIP device", fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(QSA_ERR_HIP, "%s: device id out of range", fn);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (stream_capturing(stream))
+      return fail(QSA_ERR_WORKSPACE, "%s: the first call on device %d must not be captured "
+                  "(it sets up the device's scratch); call it once outside capture", fn, dev);
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(QSA_ERR_HIP, "%s: hipGetSymbolAddress of the scratch failed on device %d: %s", fn,
+                  dev, hipGetErrorString(e));
+    uint32_t *words = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ptr) + kScratchPartFloats * 4);
+    if (qsa::launch_fill_u32(words, kCtrWords + 1, 0u, stream) != hipSuccess)
+      return fail(QSA_ERR_HIP, "%s: zeroing the scratch counters failed", fn);
+    g_scratch_ptr[dev] = static_cast<uint8_t *>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int qsa_abi_version(void) { return QSA_ABI_VERSION; }
 
-const char *qsa_last_error(void) { return g_last_error.c_str(); }
+const char *qsa_last_error(void) { return g_last_error; }
 
 qsa_status qsa_set_option(const char *name, int64_t value) {
   if (name == nullptr) return fail(QSA_ERR_ARG, "qsa_set_option: name is NULL");
@@ -729,29 +809,39 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
                       const qsa_tensor *cu_seqlens, qsa_tensor *out, qsa_tensor *lse,
                       hipStream_t stream) {
   static const char *fn = "qsa_decode";
-  qsa_status st;
-  if ((st = check_query(fn, q)) != QSA_OK) return st;
-  PoolDesc pd;
-  if ((st = check_pools(fn, k_pool, v_pool, kv_scales, &pd)) != QSA_OK) return st;
   qsa::Params p{};
-  if ((st = prepare_decode(fn, q, pd.hkv, sel_indices, cu_seqlens, out, lse, stream, &p)) != QSA_OK)
-    return st;
-  p.k = static_cast<const uint8_t *>(k_pool->data);
-  p.v = static_cast<const uint8_t *>(v_pool->data);
-  p.k_ss = k_pool->stride[0] * pd.eb;
-  p.k_sh = k_pool->stride[1] * pd.eb;
-  p.v_ss = v_pool->stride[0] * pd.eb;
-  p.v_sh = v_pool->stride[1] * pd.eb;
-  p.ks = pd.ks;
-  p.vs = pd.vs;
-  p.ks_ss = pd.ks_ss;
-  p.ks_sh = pd.ks_sh;
-  p.vs_ss = pd.vs_ss;
-  p.vs_sh = pd.vs_sh;
-  p.scale_f16 = pd.scale_f16;
-  p.a32 = addresses_fit_32(pd, k_pool, v_pool) ? 1 : 0;
-  p.slots = pd.slots;
-  p.waves = waves_for(pd.fmt, plan_workgroups(p.bs, p.hkv, p.nsplit));
+  PoolDesc pd;
+  qsa_status st = prepare_pooled_decode(fn, q, k_pool, v_pool, kv_scales, sel_indices, cu_seqlens,
+                                        out, lse, &p, &pd);
+  if (st != QSA_OK) return st;
+  if ((st = attach_workspace(fn, stream, &p)) != QSA_OK) return st;
+  const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+qsa_status qsa_decode_noalloc(const qsa_tensor *q, const qsa_tensor *k_pool,
+                              const qsa_tensor *v_pool, const qsa_kv_scales *kv_scales,
+                              const qsa_tensor *sel_indices, const qsa_tensor *cu_seqlens,
+                              qsa_tensor *out, qsa_tensor *lse, hipStream_t stream) {
+  static const char *fn = "qsa_decode_noalloc";
+  qsa::Params p{};
+  PoolDesc pd;
+  qsa_status st = prepare_pooled_decode(fn, q, k_pool, v_pool, kv_scales, sel_indices, cu_seqlens,
+                                        out, lse, &p, &pd);
+  if (st != QSA_OK) return st;
+  const int64_t need = partial_floats_of(p);
+  if (need > kScratchPartFloats)
+    return fail(QSA_ERR_WORKSPACE,
+                "%s: the split plan (bs %d, %d KV heads, %d splits) needs %lld bytes of split "
+                "partials, more than the %lld-byte scratch of this entry point; use qsa_decode",
+                fn, p.bs, p.hkv, p.nsplit, static_cast<long long>(need * 4),
+                static_cast<long long>(kScratchPartFloats * 4));
+  uint8_t *base = nullptr;
+  if ((st = scratch_of_device(fn, stream, &base)) != QSA_OK) return st;
+  p.part = reinterpret_cast<float *>(base);
+  p.ctr = reinterpret_cast<uint32_t *>(base + kScratchPartFloats * sizeof(float));
+  p.err = p.ctr + kCtrWords;
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -766,8 +856,9 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   TieredDesc td;
   if ((st = check_tiered(fn, pool, false, &td)) != QSA_OK) return st;
   qsa::Params p{};
-  if ((st = prepare_decode(fn, q, td.cold.hkv, sel_indices, cu_seqlens, out, lse, stream, &p)) != QSA_OK)
+  if ((st = prepare_decode(fn, q, td.cold.hkv, sel_indices, cu_seqlens, out, lse, &p)) != QSA_OK)
     return st;
+  if ((st = attach_workspace(fn, stream, &p)) != QSA_OK) return st;
   p.k = static_cast<const uint8_t *>(pool->cold_k.data);
   p.v = static_cast<const uint8_t *>(pool->cold_v.data);
   p.k_ss = pool->cold_k.stride[0];

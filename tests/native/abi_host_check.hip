@@ -126,6 +126,34 @@ static void decode_contract() {
   }
 }
 
+// qsa_decode_noalloc validates exactly like qsa_decode, and refuses plans
+// whose partials exceed its fixed scratch.
+static void noalloc_contract() {
+  Decode d;
+  qsa_status st = qsa_decode_noalloc(&d.q, &d.k, &d.v, nullptr, &d.sel, &d.cu, &d.out, &d.lse, nullptr);
+  EXPECT(accepted(st), "noalloc valid call: %d %s", st, qsa_last_error());
+  d.q.shape[0] = 0;
+  expect_status(qsa_decode_noalloc(&d.q, &d.k, &d.v, nullptr, &d.sel, &d.cu, &d.out, &d.lse, nullptr),
+                QSA_ERR_CONTRACT, "noalloc bs 0", "bs must be");
+  Decode big;
+  big.q = T({128, 24, 256}, QSA_DTYPE_BF16);
+  big.out = T({128, 24, 256}, QSA_DTYPE_BF16);
+  big.lse = T({128, 24}, QSA_DTYPE_F32);
+  big.cu = T({129}, QSA_DTYPE_I32);
+  EXPECT(qsa_set_option("splits", 64) == QSA_OK && qsa_set_option("max_splits", 64) == QSA_OK, "options");
+  expect_status(qsa_decode_noalloc(&big.q, &big.k, &big.v, nullptr, &big.sel, &big.cu, &big.out, &big.lse, nullptr),
+                QSA_ERR_WORKSPACE, "noalloc over the scratch", "scratch");
+  EXPECT(qsa_set_option("splits", 0) == QSA_OK && qsa_set_option("max_splits", 16) == QSA_OK, "options");
+  // the default plan of every bs fits the scratch
+  for (int bs = 1; bs <= 128; ++bs)
+    for (int hkv = 1; hkv <= 2; ++hkv) {
+      int s = 0;
+      EXPECT(qsa_plan(bs, hkv, &s, nullptr) == QSA_OK, "plan");
+      EXPECT(static_cast<int64_t>(bs) * hkv * s * qsa::kPartFloats <= (int64_t{2} << 20),
+             "default plan bs %d hkv %d exceeds the noalloc scratch", bs, hkv);
+    }
+}
+
 static void store_contract() {
   qsa_tensor kn = T({8, 2, 256}, QSA_DTYPE_BF16), vn = kn;
   qsa_tensor kp = T({64, 2, 256}, QSA_DTYPE_I8), vp = kp;
@@ -262,6 +290,7 @@ static void thread_local_errors() {
 
 int main() {
   decode_contract();
+  noalloc_contract();
   store_contract();
   tiered_contract();
   index_contract();
