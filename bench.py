@@ -776,6 +776,9 @@ def main():
     ap.add_argument("--pool-copies", type=int, default=4,
                     help="decode: also time the calls over this many pool copies in turn (cold); "
                          "0 or 1 skips it")
+    ap.add_argument("--cold", action="store_true",
+                    help="decode: every timed step (warm-up included) uses the pool copies in turn, "
+                         "so the reported value is the cold rate")
     ap.add_argument("--no-graph", action="store_true", help="decode: skip the graph-replay timing")
     ap.add_argument("--no-probe", action="store_true", help="decode: skip the bare-gather ceiling")
     ap.add_argument("--only", default=None,
@@ -857,9 +860,30 @@ def main():
     qsa.workspace_reserve(case.bs, case.hq, case.hkv)
     torch.cuda.synchronize()
 
+    # pool copies for the cold timing (a model's layers each have their own
+    # pool, so consecutive calls read different pools); with --cold every
+    # timed step, warm-up included, uses them in turn
+    copies = []
+    if args.pool_copies > 1 and tiered is None:
+        base = (k, v, qkw.get("k_scale"), qkw.get("v_scale"))
+        copies = [base] + [tuple(None if t is None else t.clone() for t in base)
+                           for _ in range(args.pool_copies - 1)]
+        torch.cuda.synchronize()
+    if args.cold and not copies:
+        raise SystemExit("--cold needs --pool-copies >= 2 and a single-tier pool")
+
+    def cold_step(i):
+        kk, vv, ks_, vs_ = copies[i % len(copies)]
+        kw = dict(qkw)
+        if ks_ is not None:
+            kw.update(k_scale=ks_, v_scale=vs_)
+        qsa.decode(q, kk, vv, sels[i % len(sels)], cu, out=out, lse=lse, **kw)
+
     if tiered is not None:
         def step(i):
             qsa.decode_tiered(q, tiered, sels[i % len(sels)], cu, out=out, lse=lse)
+    elif args.cold:
+        step = cold_step
     else:
         def step(i):
             qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
@@ -893,27 +917,18 @@ def main():
     eager_ms = timed(eager_steps)
     warm_us = float(np.median(eager_ms)) * 1e3
 
-    # cold: the same calls over `pool_copies` copies of the pools, one copy
-    # per call in turn, so that consecutive calls read different pools (a
-    # model's layers each have their own pool) and the Infinity Cache cannot
-    # hold what a call re-reads from the previous ones
+    # cold: the same calls over the pool copies in turn, so that the
+    # Infinity Cache cannot hold what a call re-reads from the previous ones
     cold = None
-    copies = []
-    if args.pool_copies > 1 and tiered is None:
-        base = (k, v, qkw.get("k_scale"), qkw.get("v_scale"))
-        copies = [base] + [tuple(None if t is None else t.clone() for t in base)
-                           for _ in range(args.pool_copies - 1)]
-        torch.cuda.synchronize()
-
-        def cold_steps():
-            for i in range(args.steps):
-                kk, vv, ks_, vs_ = copies[i % len(copies)]
-                kw = dict(qkw)
-                if ks_ is not None:
-                    kw.update(k_scale=ks_, v_scale=vs_)
-                qsa.decode(q, kk, vv, sels[i % len(sels)], cu, out=out, lse=lse, **kw)
-        cold_steps()
-        cold_ms = timed(cold_steps)
+    if copies:
+        if args.cold:
+            cold_ms = eager_ms
+        else:
+            def cold_steps():
+                for i in range(args.steps):
+                    cold_step(i)
+            cold_steps()
+            cold_ms = timed(cold_steps)
         cold = {"us_per_call": round(float(np.median(cold_ms)) * 1e3, 3),
                 "us_p10": round(float(np.percentile(cold_ms, 10)) * 1e3, 3),
                 "us_p90": round(float(np.percentile(cold_ms, 90)) * 1e3, 3),
@@ -937,7 +952,7 @@ def main():
         graph_ms = timed(graph.replay)
         del graph
     reps_ms = eager_ms
-    timing_mode = "eager"
+    timing_mode = "eager, pool copies in turn (cold)" if args.cold else "eager"
     if args.timing == "graph":
         reps_ms = graph_ms
         timing_mode = "graph"
@@ -1003,6 +1018,7 @@ def main():
             "bs": case.bs, "hq": case.hq, "hkv": case.hkv, "head_dim": 256,
             "sel_per_row": int(case.lengths.max()), "pool_slots": int(case.k_pool.shape[0]),
             "index_banks": len(sels), "splits": splits, "workgroups": wgs,
+            "pool_copies_timed": len(copies) if args.cold else 1,
             **({"ring_rows": args.ring_rows, "hot_share": hot_share} if tiered is not None else {}),
             "gathered_kv_bytes_per_call": b_kv, "counters_at_rest": counters_ok,
         },

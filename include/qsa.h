@@ -272,10 +272,12 @@ qsa_status qsa_kv_store_tiered(const qsa_tensor *k_new, const qsa_tensor *v_new,
  *   Row b has T_b = context_lens[b] tokens.  Logical block j < n_b =
  *   T_b / c (c = compress_ratio) covers tokens j*c .. j*c + c - 1 and has
  *   one compressed index key, row block_table[b][j] of k_index_pool.  Its
- *   score is s_j = sum_h w_h (q_h . k_j) over the row's index heads (w_h =
+ *   score is s_j = sum_h w_h (q_h . k_j) = qt . k_j over the row's index
+ *   heads, with the weighted query qt = sum_h w_h q_h (w_h =
  *   head_weights[b][h], or 1 without weights), in fp32 in this order: per
- *   head, a = 0 then a = fma(q_h[d], k_j[d], a) for d = 0, 1, ...; then
- *   s = 0 and s = fma(w_h, a_h, s) for h = 0, 1, ...; -0 reads as +0.
+ *   element d, qt[d] = 0 then qt[d] = fma(w_h, q_h[d], qt[d]) for h = 0, 1,
+ *   ...; then s = 0 and s = fma(qt[d], k_j[d], s) for d = 0, 1, ...; -0
+ *   reads as +0.
  *   The row keeps the K = budget / c blocks with the largest scores (a tie
  *   goes to the lower block index; every block when n_b <= K), and lists,
  *   in ascending block order, each kept block's c tokens, then the

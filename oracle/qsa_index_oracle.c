@@ -24,12 +24,13 @@
  *   covers tokens j*c .. j*c + c - 1 and has one compressed index key,
  *   stored in pool row block_table[b][j].  MQA scoring: the row's hi index
  *   query heads share that key, and block j scores
- *       s_j = sum_h w_h * (q_h . k_j)
- *   evaluated in fp32 exactly as written below: for each head in order, the
- *   dot product is one fused multiply-add per element in element order
- *   starting from 0, and the weighted head terms are added the same way in
- *   head order (w_h = 1 when no weights are given); -0 is read as +0.
- *   Both this oracle and the GPU evaluate it in that order, so they take the
+ *       s_j = sum_h w_h * (q_h . k_j) = (sum_h w_h q_h) . k_j
+ *   (w_h = 1 when no weights are given), evaluated in fp32 exactly as
+ *   written below: the row's weighted query qt = sum_h w_h q_h first,
+ *   element by element, one fused multiply-add per head in head order
+ *   starting from 0; then the dot product qt . k_j, one fused multiply-add
+ *   per element in element order starting from 0; -0 is read as +0.  Both
+ *   this oracle and the GPU evaluate it in that order, so they take the
  *   same top-k decisions.
  *
  *   Exact top-k: the K = budget / c blocks with the largest scores, a tie
@@ -54,14 +55,19 @@ static float bf16_to_float(uint16_t bits) {
   return f;
 }
 
-/* Block score of the reading above. */
-static float block_score(int hi, int di, const uint16_t *q, const float *w, const uint16_t *k) {
-  float s = 0.0f;
-  for (int h = 0; h < hi; ++h) {
+/* The row's weighted query qt[d] = sum_h w_h q[h][d] of the reading above. */
+static void weighted_query(int hi, int di, const uint16_t *q, const float *w, float *qt) {
+  for (int d = 0; d < di; ++d) {
     float a = 0.0f;
-    for (int d = 0; d < di; ++d) a = fmaf(bf16_to_float(q[h * di + d]), bf16_to_float(k[d]), a);
-    s = fmaf(w ? w[h] : 1.0f, a, s);
+    for (int h = 0; h < hi; ++h) a = fmaf(w ? w[h] : 1.0f, bf16_to_float(q[h * di + d]), a);
+    qt[d] = a;
   }
+}
+
+/* Block score of the reading above: qt . k in element order. */
+static float block_score(int di, const float *qt, const uint16_t *k) {
+  float s = 0.0f;
+  for (int d = 0; d < di; ++d) s = fmaf(qt[d], bf16_to_float(k[d]), s);
   return s + 0.0f; /* -0 -> +0 */
 }
 
@@ -119,15 +125,22 @@ int oracle_qsa_index(int bs, int hi, int di, const uint16_t *q, const float *w,
       free(take);
       return 1;
     }
+    float *qt = malloc(sizeof *qt * (size_t)di);
+    if (!qt) {
+      free(sc);
+      free(take);
+      return 1;
+    }
+    weighted_query(hi, di, q + (int64_t)b * hi * di, w ? w + (int64_t)b * hi : NULL, qt);
     for (int j = 0; j < n; ++j) {
       const int32_t row = block_table[(int64_t)b * max_blocks + j];
       if (row < 0 || row >= n_kpool) {
         free(sc);
         free(take);
+        free(qt);
         return 6;
       }
-      sc[j].s = block_score(hi, di, q + (int64_t)b * hi * di, w ? w + (int64_t)b * hi : NULL,
-                            kpool + (int64_t)row * di);
+      sc[j].s = block_score(di, qt, kpool + (int64_t)row * di);
       sc[j].j = j;
       if (scores_out) scores_out[(int64_t)b * max_blocks + j] = sc[j].s;
     }
@@ -146,6 +159,7 @@ int oracle_qsa_index(int bs, int hi, int di, const uint16_t *q, const float *w,
     for (int64_t pos = (int64_t)n * c; pos < t; ++pos) out[o++] = r2t[pos];
     free(sc);
     free(take);
+    free(qt);
   }
   return 0;
 }

@@ -10,14 +10,15 @@
 // dequant-on-gather (fp8/int8/int4)", part 4, decode routing paragraph).
 //
 // Two launches:
-//   * scores: a workgroup per 64 blocks of a row.  A lane holds its block's
-//     key row in registers; the heads are spread over the waves (8 when
-//     the grid has at most one workgroup per CU, else 4), 8 independent
-//     dot products per lane at a time, with the queries read
-//     from LDS (broadcast).  The score is evaluated in the order the
-//     contract fixes -- per head one fused multiply-add per element in
-//     element order, then the weighted heads in head order -- so that the
-//     top-k decisions are reproducible exactly.
+//   * scores: a workgroup per 128 blocks of a row, one thread per block.
+//     The weighted sum over the index heads is taken on the query side
+//     first (qt = sum_h w_h q_h, which the heads' shared key makes exact),
+//     so a block costs one dot product of its key row with qt: the kernel
+//     reads each key row once and is bound by that gather.  The score is
+//     evaluated in the order the contract fixes -- qt element by element
+//     over the heads in head order, then one fused multiply-add per key
+//     element in element order -- so that the top-k decisions are
+//     reproducible exactly.
 //   * select: one 1024-thread workgroup per row.  Its offset in the packed
 //     output depends only on the context lengths, so every workgroup
 //     computes its own; an exact radix select (4 passes of 8 bits over
@@ -47,85 +48,99 @@ __device__ __forceinline__ int row_length(const IndexParams &p, int32_t t) {
   return (n < k ? n : k) * p.c + t % p.c;
 }
 
-// A workgroup scores 64 consecutive blocks of one row: lane l of every wave
-// takes block 64*blockIdx.x + l, and wave w of W the heads w, w + W, ..., in
-// groups of 8 independent dot products (each one a fused multiply-add chain
-// in element order).  The row's queries are converted to fp32 once into
-// LDS (read back as broadcasts, 4 elements per read), and each key element
-// is converted once for 8 heads.  The per-head results meet in LDS, where
-// the first wave adds them up in head order.
-template <int DI, int W>
-__global__ void __launch_bounds__(64 * W) qsa_index_score_kernel(const IndexParams p) {
-  constexpr int NC = DI / 8;  // 16-byte chunks of a bf16 row
-  constexpr int kScoreThreads = 64 * W;
-  constexpr int kWaves = W;
-  constexpr int kGroup = 8;   // dot products in flight per lane
+// A workgroup scores 128 consecutive blocks of one row, one thread per
+// block.  The contract's score is s_j = qt . k_j with the row's weighted
+// query qt = sum_h w_h q_h, in fp32: qt element by element as a fused
+// multiply-add chain over the heads in head order, then one fused
+// multiply-add per element of k_j in element order.  Prologue: every
+// thread issues the block-table loads of the key rows it stages (16-byte
+// pieces, so that each key row is read by consecutive lanes), its share of
+// the row's queries and the head weights; the key rows follow as soon as
+// their table entries arrive.  Queries, weights and key rows go to LDS,
+// thread d forms qt[d], and each thread then runs its block's dot product
+// against qt read as broadcasts.
+template <int DI>
+__global__ void __launch_bounds__(128, 1) qsa_index_score_kernel(const IndexParams p) {
+  constexpr int kThreads = 128;          // = blocks per workgroup
+  constexpr int NC = DI / 8;             // 16-byte pieces of a key row
+  constexpr int kPitch = DI * 2 + 16;    // LDS key-row pitch: rows start 16 B apart in the banks
+  constexpr int kQPieces = kMaxIndexHeads * NC / kThreads;  // query pieces per thread (at most)
   const int b = blockIdx.y;
   const int32_t t = p.ctx[b];
   const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
   const int n = row_ok ? t / p.c : 0;
-  if (static_cast<int>(blockIdx.x) * 64 >= n) return;  // uniform
+  const int j0 = static_cast<int>(blockIdx.x) * kThreads;
+  if (j0 >= n) return;  // uniform
+  const int tid = threadIdx.x;
 
-  __shared__ float4 qf[kMaxIndexHeads * DI / 4];   // [hi][DI] fp32
-  __shared__ float dots[kMaxIndexHeads][64];
-  for (int i = threadIdx.x; i < p.hi * NC; i += kScoreThreads) {
-    const int h = i / NC, c8 = i - h * NC;
-    const uint4 v = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[c8];
-    qf[2 * i] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
-    qf[2 * i + 1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
+  __shared__ __attribute__((aligned(16))) unsigned char keys[kThreads * kPitch];
+  __shared__ __attribute__((aligned(16))) uint4 qs[kMaxIndexHeads * NC];  // [hi][DI] bf16
+  __shared__ __attribute__((aligned(16))) float qt[DI];
+  __shared__ float ws[kMaxIndexHeads];
+
+  // piece i of this thread: key row r = (i * kThreads + tid) / NC of the
+  // workgroup's blocks, 16-byte chunk ch of it
+  const int ch = tid % NC;
+  int32_t krow[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int j = j0 + (i * kThreads + tid) / NC;
+    krow[i] = p.bt[b * p.bt_sb + (j < n ? j : n - 1)];
+  }
+  uint4 qv[kQPieces];
+#pragma unroll
+  for (int i = 0; i < kQPieces; ++i) {
+    const int pi = i * kThreads + tid;
+    const int h = pi / NC;
+    qv[i] = make_uint4(0, 0, 0, 0);
+    if (h < p.hi) qv[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[pi % NC];
+  }
+  const float wv = (tid < p.hi) ? (p.w ? p.w[b * p.w_sb + tid] : 1.0f) : 0.0f;
+  uint4 kv[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int32_t r = krow[i];
+    const int64_t rr = (r >= 0 && r < p.n_k) ? r : 0;
+    kv[i] = reinterpret_cast<const uint4 *>(p.k + rr * p.k_ss)[ch];
+  }
+#pragma unroll
+  for (int i = 0; i < kQPieces; ++i) qs[i * kThreads + tid] = qv[i];
+  if (tid < kMaxIndexHeads) ws[tid] = wv;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    *reinterpret_cast<uint4 *>(keys + ((i * kThreads + tid) / NC) * kPitch + ch * 16) = kv[i];
+  __syncthreads();
+  if (tid < DI) {
+    const uint16_t *qh = reinterpret_cast<const uint16_t *>(qs) + tid;
+    float a = 0.0f;
+    for (int h = 0; h < p.hi; ++h)
+      a = __builtin_fmaf(ws[h], __uint_as_float(static_cast<uint32_t>(qh[h * DI]) << 16), a);
+    qt[tid] = a;
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int j = blockIdx.x * 64 + lane;
-  const bool live = j < n;
-  const int32_t row = live ? p.bt[b * p.bt_sb + j] : 0;
-  const bool row_in = row >= 0 && row < p.n_k;
-  if (live && !row_in && wave == 0) atomicOr(p.err, kErrIndexRow);
-  uint4 kr[NC];
-  const uint4 *kp = reinterpret_cast<const uint4 *>(p.k + static_cast<int64_t>(row_in ? row : 0) * p.k_ss);
-#pragma unroll
-  for (int i = 0; i < NC; ++i) kr[i] = kp[i];
-
-  for (int h0 = wave; h0 < p.hi; h0 += kWaves * kGroup) {
-    float a[kGroup];
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u) a[u] = 0.0f;
-    // heads h0, h0 + 4, ..., (those < hi)
-    const int nh = min(kGroup, (p.hi - h0 + kWaves - 1) / kWaves);
+  const int j = j0 + tid;
+  if (j < n) {
+    const int32_t row = p.bt[b * p.bt_sb + j];
+    const bool row_in = row >= 0 && row < p.n_k;
+    if (!row_in) atomicOr(p.err, kErrIndexRow);
+    const unsigned char *kr = keys + tid * kPitch;
+    const float4 *q4 = reinterpret_cast<const float4 *>(qt);
+    float sc = 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const float kf[8] = {bf_lo(kr[i].x), bf_hi(kr[i].x), bf_lo(kr[i].y), bf_hi(kr[i].y),
-                           bf_lo(kr[i].z), bf_hi(kr[i].z), bf_lo(kr[i].w), bf_hi(kr[i].w)};
-#pragma unroll
-      for (int u = 0; u < kGroup; ++u) {
-        if (u < nh) {
-          const float4 q0 = qf[((h0 + kWaves * u) * DI) / 4 + 2 * i];
-          const float4 q1 = qf[((h0 + kWaves * u) * DI) / 4 + 2 * i + 1];
-          a[u] = __builtin_fmaf(q0.x, kf[0], a[u]);
-          a[u] = __builtin_fmaf(q0.y, kf[1], a[u]);
-          a[u] = __builtin_fmaf(q0.z, kf[2], a[u]);
-          a[u] = __builtin_fmaf(q0.w, kf[3], a[u]);
-          a[u] = __builtin_fmaf(q1.x, kf[4], a[u]);
-          a[u] = __builtin_fmaf(q1.y, kf[5], a[u]);
-          a[u] = __builtin_fmaf(q1.z, kf[6], a[u]);
-          a[u] = __builtin_fmaf(q1.w, kf[7], a[u]);
-        }
-      }
+      const uint4 v = *reinterpret_cast<const uint4 *>(kr + i * 16);
+      const float4 q0 = q4[2 * i], q1 = q4[2 * i + 1];
+      sc = __builtin_fmaf(q0.x, bf_lo(v.x), sc);
+      sc = __builtin_fmaf(q0.y, bf_hi(v.x), sc);
+      sc = __builtin_fmaf(q0.z, bf_lo(v.y), sc);
+      sc = __builtin_fmaf(q0.w, bf_hi(v.y), sc);
+      sc = __builtin_fmaf(q1.x, bf_lo(v.z), sc);
+      sc = __builtin_fmaf(q1.y, bf_hi(v.z), sc);
+      sc = __builtin_fmaf(q1.z, bf_lo(v.w), sc);
+      sc = __builtin_fmaf(q1.w, bf_hi(v.w), sc);
     }
-#pragma unroll
-    for (int u = 0; u < kGroup; ++u)
-      if (u < nh) dots[h0 + kWaves * u][lane] = a[u];
-  }
-  __syncthreads();
-  if (wave == 0 && live) {
-    float s = 0.0f;
-    for (int h = 0; h < p.hi; ++h) {
-      const float wh = p.w ? p.w[b * p.w_sb + h] : 1.0f;
-      s = __builtin_fmaf(wh, dots[h][lane], s);
-    }
-    p.scores[static_cast<int64_t>(b) * p.max_blocks + j] = row_in ? s + 0.0f : -INFINITY;  // -0 -> +0
+    p.scores[static_cast<int64_t>(b) * p.max_blocks + j] = row_in ? sc + 0.0f : -INFINITY;  // -0 -> +0
   }
 }
 
@@ -295,26 +310,14 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
 }  // namespace
 
 hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
-  const dim3 sgrid(static_cast<unsigned>((p.max_blocks + 63) / 64), static_cast<unsigned>(p.bs));
-  // with at most one workgroup per CU the waves' LDS-latency-bound chains
-  // are the time, so 8 waves (8 heads each) halve them; larger grids keep
-  // 4 waves (16 heads each), which were faster there (MI355X, 8K-token rows,
-  // 64 heads of dim 128: 4 / 8 rows 34.2 / 34.9 -> 25.7 / 26.3 us; 32 rows
-  // 56.4 us with 4 waves against 64.7 with 8)
-  // (full 64-block columns only: the grid's last column is often empty and
-  // its workgroups return at once)
-  // (64-dim heads hold half the key registers, so their 8-wave instance
-  // keeps more waves resident and stays ahead up to two workgroups per CU:
-  // 16 rows of dim 64, 26.0 -> 23.0 us)
-  const bool eight = static_cast<int64_t>(p.max_blocks / 64) * p.bs <= (p.di == 64 ? 512 : 256);
+  const dim3 sgrid(static_cast<unsigned>((p.max_blocks + 127) / 128), static_cast<unsigned>(p.bs));
   if (p.max_blocks > 0) {
-    switch (p.di * 2 + (eight ? 1 : 0)) {
-      case 64 * 2: hipLaunchKernelGGL((qsa_index_score_kernel<64, 4>), sgrid, dim3(256), 0, stream, p); break;
-      case 64 * 2 + 1: hipLaunchKernelGGL((qsa_index_score_kernel<64, 8>), sgrid, dim3(512), 0, stream, p); break;
-      case 128 * 2: hipLaunchKernelGGL((qsa_index_score_kernel<128, 4>), sgrid, dim3(256), 0, stream, p); break;
-      case 128 * 2 + 1: hipLaunchKernelGGL((qsa_index_score_kernel<128, 8>), sgrid, dim3(512), 0, stream, p); break;
-      default: return hipErrorInvalidValue;
-    }
+    if (p.di == 64)
+      hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(128), 0, stream, p);
+    else if (p.di == 128)
+      hipLaunchKernelGGL(qsa_index_score_kernel<128>, sgrid, dim3(128), 0, stream, p);
+    else
+      return hipErrorInvalidValue;
   }
   if (p.max_blocks <= kMaxRegKeys * kSelectThreads)
     hipLaunchKernelGGL(qsa_index_select_kernel<true>, dim3(static_cast<unsigned>(p.bs)), dim3(kSelectThreads), 0,

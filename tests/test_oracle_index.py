@@ -104,6 +104,33 @@ def test_topk_is_numpy_top_k_and_expansion_is_ordered(c, budget):
             np.testing.assert_array_equal(chosen, np.arange(n))
 
 
+def test_kept_blocks_are_a_top_k_under_float64_scores():
+    """Whatever fp32 order the scores are evaluated in, the kept set must be
+    a top-k of the exact (float64) scores up to the fp32 error bound
+    (hi + di + 2) 2^-24 sum_h |w_h| |q_h| . |k_j| of each block: no dropped
+    block may beat a kept one by more than their two bounds."""
+    rng = np.random.default_rng(68)
+    for hi, di in ((8, 128), (64, 64), (1, 128)):
+        ctx = [8192, 3001, 2048 * 4 + 3]
+        inp = make_inputs(rng, ctx, hi=hi, di=di, c=4)
+        sel, cu = run(inp, 2048, 4)
+        q = inp["q"].double()
+        k = inp["k_pool"].double()
+        w = torch.from_numpy(inp["weights"]).double()
+        for b, t in enumerate(ctx):
+            n, kb = t // 4, 512
+            if n <= kb:
+                continue
+            keys = k[torch.from_numpy(inp["block_table"][b, :n].astype(np.int64))]
+            exact = ((keys @ q[b].T) * w[b]).sum(-1).numpy()
+            bound = (hi + di + 2) * 2.0 ** -24 * ((keys.abs() @ q[b].abs().T) * w[b].abs()).sum(-1).numpy()
+            pos = positions(sel[cu[b]:cu[b + 1]], inp["req_to_token"][b])
+            kept = np.zeros(n, bool)
+            kept[pos[: kb * 4: 4] // 4] = True
+            assert kept.sum() == kb
+            assert (exact[kept] + bound[kept]).min() >= (exact[~kept] - bound[~kept]).max()
+
+
 def test_ties_go_to_the_lower_block_index():
     rng = np.random.default_rng(63)
     inp = make_inputs(rng, [4096, 4096], c=4, hi=2, di=32)
