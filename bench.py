@@ -492,9 +492,14 @@ def index_mode(args):
     ms = float(np.median(reps))
     n = args.ctx // c
     listed = min(n, budget // c) * c + args.ctx % c
-    flops = bs * n * hi * di * 2
+    # algorithmic work: the weighted query (hi * di multiply-adds per row),
+    # one di-element dot product per block, and the gather of what the step
+    # must read and write: the compressed keys and block-table entries of
+    # every block, the queries and weights, the token-table entries and slot
+    # ids of every listed token
+    flops = bs * (hi * di + n * di) * 2
     byts = bs * (n * (di * 2 + 4) + listed * 8 + hi * di * 2 + hi * 4)
-    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = byts / (ms * 1e-3) / 1e9
     print(json.dumps({
         "metric": "qsa_index us/call (MQA block scores + exact top-k + expansion)",
         "value": round(ms * 1e3, 3), "unit": "us/call", "higher_is_better": False,
@@ -506,13 +511,14 @@ def index_mode(args):
                    "bs": bs, "ctx": args.ctx, "compress_ratio": c, "budget": budget,
                    "index_heads": hi, "index_dim": di, "launches_per_call": 2,
                    "algorithmic_flops_per_call": flops, "algorithmic_bytes_per_call": byts},
-        # fp32 vector peak: 256 CUs x 128 FMA lanes per clock (packed fp32
-        # issues two per lane) x 2 flops x 2.4 GHz = 157.3 TFLOP/s; the build
-        # emits no packed fp32 forms, so single-issue FMAs top out at half
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(tflops / 157.3, 4), "traffic": None,
-                     "peak_single_issue_fma": 78.6, "frac_single_issue_fma": round(tflops / 78.6, 4),
-                     "hbm_GBps": round(byts / (ms * 1e-3) / 1e9, 2),
+        # the step reads each compressed key once and does di multiply-adds
+        # per block: an HBM-side gather, far below both the HBM and the fp32
+        # roofline at these sizes -- both kernels are bound by latency chains
+        # (score: block table -> key rows -> dot products; select: radix
+        # passes separated by workgroup barriers)
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "tflops": round(flops / (ms * 1e-3) / 1e12, 4),
                      "kernel": "qsa_index_score_kernel + qsa_index_select_kernel"},
     }), flush=True)
 
@@ -771,6 +777,7 @@ def main():
     ap.add_argument("--tokens", type=int, default=32768, help="tokens per store call")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--split-target", type=int, default=None)
+    ap.add_argument("--splits", type=int, default=None, help="force this many splits per (row, KV head)")
     ap.add_argument("--min-split-keys", type=int, default=None)
     ap.add_argument("--waves", type=int, default=None)
     ap.add_argument("--pool-copies", type=int, default=4,
@@ -815,6 +822,8 @@ def main():
 
     if args.split_target:
         qsa.set_option("split_target", args.split_target)
+    if args.splits:
+        qsa.set_option("splits", args.splits)
     if args.min_split_keys:
         qsa.set_option("min_split_keys", args.min_split_keys)
     if args.waves:

@@ -36,6 +36,7 @@ constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kMaxIndexHeads = 64;
 constexpr int kMaxRegKeys = 16;  // keys per thread held in registers by the select kernel
+constexpr int kSpeculate = 4096; // score kernel: block tables up to this size are read before the lengths
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -48,44 +49,55 @@ __device__ __forceinline__ int row_length(const IndexParams &p, int32_t t) {
   return (n < k ? n : k) * p.c + t % p.c;
 }
 
-// A workgroup scores 128 consecutive blocks of one row, one thread per
-// block.  The contract's score is s_j = qt . k_j with the row's weighted
-// query qt = sum_h w_h q_h, in fp32: qt element by element as a fused
+// A workgroup of 256 threads scores 128 consecutive blocks of one row.
+// The contract's score is s_j = qt . k_j with the row's weighted query
+// qt = sum_h w_h q_h, in fp32: qt element by element as a fused
 // multiply-add chain over the heads in head order, then one fused
-// multiply-add per element of k_j in element order.  Prologue: every
-// thread issues the block-table loads of the key rows it stages (16-byte
-// pieces, so that each key row is read by consecutive lanes), its share of
-// the row's queries and the head weights; the key rows follow as soon as
-// their table entries arrive.  Queries, weights and key rows go to LDS,
-// thread d forms qt[d], and each thread then runs its block's dot product
-// against qt read as broadcasts.
+// multiply-add per element of k_j in element order.  Every global load is
+// issued first: the block-table entries of the key rows a thread stages
+// (16-byte pieces, consecutive lanes on one row), then those pieces, its
+// share of the row's queries and the head weights.  Queries, weights and
+// key rows go to LDS; thread d < DI forms qt[d] (LDS reads in batches of 8
+// heads, so the chain waits for LDS once per batch); thread t < 128 then
+// runs block j0 + t's chain over its key row against qt (broadcast reads).
 template <int DI>
-__global__ void __launch_bounds__(128, 1) qsa_index_score_kernel(const IndexParams p) {
-  constexpr int kThreads = 128;          // = blocks per workgroup
+__global__ void __launch_bounds__(256) qsa_index_score_kernel(const IndexParams p) {
+  constexpr int kThreads = 256;
+  constexpr int kBlocks = 128;           // blocks per workgroup
   constexpr int NC = DI / 8;             // 16-byte pieces of a key row
+  constexpr int KP = kBlocks * NC / kThreads;               // key pieces per thread
   constexpr int kPitch = DI * 2 + 16;    // LDS key-row pitch: rows start 16 B apart in the banks
-  constexpr int kQPieces = kMaxIndexHeads * NC / kThreads;  // query pieces per thread (at most)
+  constexpr int kQPieces = kMaxIndexHeads * NC / kThreads;  // query pieces per thread
+  constexpr int kHB = 8;                 // heads per batch of LDS reads in the qt chain
+  static_assert(kThreads % NC == 0 && KP * kThreads == kBlocks * NC, "piece mapping");
   const int b = blockIdx.y;
-  const int32_t t = p.ctx[b];
-  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
-  const int n = row_ok ? t / p.c : 0;
-  const int j0 = static_cast<int>(blockIdx.x) * kThreads;
-  if (j0 >= n) return;  // uniform
+  const int j0 = static_cast<int>(blockIdx.x) * kBlocks;  // < max_blocks (the grid's width)
   const int tid = threadIdx.x;
 
-  __shared__ __attribute__((aligned(16))) unsigned char keys[kThreads * kPitch];
-  __shared__ __attribute__((aligned(16))) uint4 qs[kMaxIndexHeads * NC];  // [hi][DI] bf16
+  __shared__ __attribute__((aligned(16))) unsigned char keys[kBlocks * kPitch];
+  __shared__ __attribute__((aligned(16))) uint4 qs[kMaxIndexHeads * NC];  // [64][DI] bf16
   __shared__ __attribute__((aligned(16))) float qt[DI];
   __shared__ float ws[kMaxIndexHeads];
 
-  // piece i of this thread: key row r = (i * kThreads + tid) / NC of the
-  // workgroup's blocks, 16-byte chunk ch of it
+  // With a block table of at most kSpeculate blocks per row, every load is
+  // issued before the row's length arrives: the block-table row has
+  // max_blocks entries whatever the length, so entries up to max_blocks - 1
+  // are read and the blocks past the row's end go unused (at most 32
+  // workgroups per row).  Larger tables wait for the length first, so that
+  // short rows do not read keys they do not have.
+  // Key piece i of this thread: row (i * kThreads + tid) / NC of the
+  // workgroup's blocks, 16-byte chunk ch.
+  const int32_t t = p.ctx[b];
+  if (p.max_blocks > kSpeculate) {
+    const bool ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
+    if (j0 >= (ok ? t / p.c : 0)) return;  // uniform
+  }
   const int ch = tid % NC;
-  int32_t krow[NC];
+  int32_t krow[KP];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int j = j0 + (i * kThreads + tid) / NC;
-    krow[i] = p.bt[b * p.bt_sb + (j < n ? j : n - 1)];
+    krow[i] = p.bt[b * p.bt_sb + (j < p.max_blocks ? j : p.max_blocks - 1)];
   }
   uint4 qv[kQPieces];
 #pragma unroll
@@ -96,31 +108,43 @@ __global__ void __launch_bounds__(128, 1) qsa_index_score_kernel(const IndexPara
     if (h < p.hi) qv[i] = reinterpret_cast<const uint4 *>(p.q + b * p.q_sb + h * p.q_sh)[pi % NC];
   }
   const float wv = (tid < p.hi) ? (p.w ? p.w[b * p.w_sb + tid] : 1.0f) : 0.0f;
-  uint4 kv[NC];
+  uint4 kv[KP];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
+  for (int i = 0; i < KP; ++i) {
     const int32_t r = krow[i];
     const int64_t rr = (r >= 0 && r < p.n_k) ? r : 0;
     kv[i] = reinterpret_cast<const uint4 *>(p.k + rr * p.k_ss)[ch];
   }
+  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
+  const int n = row_ok ? t / p.c : 0;
+  if (j0 >= n) return;  // uniform
 #pragma unroll
   for (int i = 0; i < kQPieces; ++i) qs[i * kThreads + tid] = qv[i];
   if (tid < kMaxIndexHeads) ws[tid] = wv;
 #pragma unroll
-  for (int i = 0; i < NC; ++i)
+  for (int i = 0; i < KP; ++i)
     *reinterpret_cast<uint4 *>(keys + ((i * kThreads + tid) / NC) * kPitch + ch * 16) = kv[i];
   __syncthreads();
   if (tid < DI) {
     const uint16_t *qh = reinterpret_cast<const uint16_t *>(qs) + tid;
     float a = 0.0f;
-    for (int h = 0; h < p.hi; ++h)
-      a = __builtin_fmaf(ws[h], __uint_as_float(static_cast<uint32_t>(qh[h * DI]) << 16), a);
+    for (int h0 = 0; h0 < p.hi; h0 += kHB) {
+      float qx[kHB], wx[kHB];
+#pragma unroll
+      for (int u = 0; u < kHB; ++u) {  // rows past hi hold zeros and weight 0 (read, unused)
+        qx[u] = __uint_as_float(static_cast<uint32_t>(qh[(h0 + u) * DI]) << 16);
+        wx[u] = ws[h0 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < kHB; ++u)
+        if (h0 + u < p.hi) a = __builtin_fmaf(wx[u], qx[u], a);
+    }
     qt[tid] = a;
   }
   __syncthreads();
 
   const int j = j0 + tid;
-  if (j < n) {
+  if (tid < kBlocks && j < n) {
     const int32_t row = p.bt[b * p.bt_sb + j];
     const bool row_in = row >= 0 && row < p.n_k;
     if (!row_in) atomicOr(p.err, kErrIndexRow);
@@ -165,14 +189,37 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2][256];  // double-buffered: pass r counts in hist[r & 1]
   __shared__ int32_t wsum[2][kSelectWaves];
   __shared__ uint32_t s_prefix;
   __shared__ int32_t s_krem;
 
+  // The row's own length, the lengths of the rows before it (one per
+  // thread: bs <= 128 <= kSelectThreads) and then its scores are loaded in
+  // that order, so that the offset sum below waits for the lengths only
+  // while the score loads are still in flight.
+  const int32_t t = p.ctx[b];
+  const int32_t tprev = p.ctx[tid < b ? tid : b];
+  const float *sc = p.scores + static_cast<int64_t>(b) * p.max_blocks;
+  constexpr int kRegKeys = KEYS_IN_REGS ? kMaxRegKeys : 1;
+  uint32_t keys[kRegKeys];
+  if constexpr (KEYS_IN_REGS) {
+    // the row's score slots exist up to max_blocks whatever its length:
+    // read them before the length arrives (entries past the row's blocks
+    // are masked below)
+#pragma unroll
+    for (int i = 0; i < kRegKeys; ++i) {
+      const int j = i * kSelectThreads + tid;
+      keys[i] = (j < p.max_blocks) ? __float_as_uint(sc[j]) : 0u;  // float bits; keyed below
+    }
+  }
+  int part = tid < b ? row_length(p, tprev) : 0;
+  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
+  const int n = row_ok ? t / p.c : 0, k = p.budget / p.c, c = p.c;
+  const bool select = n > k;
+  if (tid < 256) hist[0][tid] = 0;
+
   // ---- this row's offset in the packed output
-  int part = 0;
-  for (int i = tid; i < b; i += kSelectThreads) part += row_length(p, p.ctx[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
   if (lane == 0) wsum[0][wave] = part;
@@ -180,8 +227,6 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
   int off = 0;
 #pragma unroll
   for (int w = 0; w < kSelectWaves; ++w) off += wsum[0][w];
-  const int32_t t = p.ctx[b];
-  const bool row_ok = t >= 0 && t <= p.max_tokens && t / p.c <= p.max_blocks;
   const int len = row_length(p, t);
   if (tid == 0) {
     p.cu[b + 1] = off + len;
@@ -189,21 +234,17 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
     if (!row_ok) atomicOr(p.err, kErrIndexRow);
   }
   if (!row_ok) return;  // uniform; the row lists nothing
-  const int n = t / p.c, k = p.budget / p.c, c = p.c;
   int32_t *out = p.sel + off;
   const int32_t *r2t = p.r2t + b * p.r2t_sb;
-  if (n <= k) {  // every block is taken: the row is every token in order
+  if (!select) {  // every block is taken: the row is every token in order
     for (int i = tid; i < t; i += kSelectThreads) out[i] = r2t[i];
     return;
   }
-  const float *sc = p.scores + static_cast<int64_t>(b) * p.max_blocks;
-  constexpr int kRegKeys = KEYS_IN_REGS ? kMaxRegKeys : 1;
-  uint32_t keys[kRegKeys];
   if constexpr (KEYS_IN_REGS) {
 #pragma unroll
     for (int i = 0; i < kRegKeys; ++i) {
       const int j = i * kSelectThreads + tid;
-      keys[i] = (j < n) ? order_key(sc[j]) : 0u;
+      keys[i] = (j < n) ? order_key(__uint_as_float(keys[i])) : 0u;
     }
   }
   const int nchunk = (n + kSelectThreads - 1) / kSelectThreads;
@@ -224,14 +265,15 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
     }
   };
 
-  // ---- radix select of the k-th largest key
+  // ---- radix select of the k-th largest key.  Pass r counts into
+  // hist[r & 1] while the other buffer was cleared during pass r - 1's scan
+  // (hist[0] before the first pass), so a pass takes two barriers.
   uint32_t prefix = 0, mask = 0;
   int krem = k;  // keys still to take among those matching `prefix` under `mask`
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  for (int shift = 24, r = 0; shift >= 0; shift -= 8, ++r) {
+    uint32_t *h = hist[r & 1];
     each_chunk([&](int j, uint32_t key) {
-      if (j < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      if (j < n && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
     });
     __syncthreads();
     if (wave == 0) {
@@ -240,7 +282,7 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
       int c4 = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        h4[i] = hist[255 - 4 * lane - i];
+        h4[i] = h[255 - 4 * lane - i];
         c4 += static_cast<int>(h4[i]);
       }
       int incl = c4;
@@ -262,6 +304,8 @@ __global__ void __launch_bounds__(kSelectThreads) qsa_index_select_kernel(const 
           run += static_cast<int>(h4[i]);
         }
       }
+    } else if (tid >= 256 && tid < 512) {
+      hist[(r + 1) & 1][tid - 256] = 0;
     }
     __syncthreads();
     prefix = s_prefix;
@@ -313,9 +357,9 @@ hipError_t launch_index(const IndexParams &p, hipStream_t stream) {
   const dim3 sgrid(static_cast<unsigned>((p.max_blocks + 127) / 128), static_cast<unsigned>(p.bs));
   if (p.max_blocks > 0) {
     if (p.di == 64)
-      hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL(qsa_index_score_kernel<64>, sgrid, dim3(256), 0, stream, p);
     else if (p.di == 128)
-      hipLaunchKernelGGL(qsa_index_score_kernel<128>, sgrid, dim3(128), 0, stream, p);
+      hipLaunchKernelGGL(qsa_index_score_kernel<128>, sgrid, dim3(256), 0, stream, p);
     else
       return hipErrorInvalidValue;
   }
