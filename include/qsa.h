@@ -210,7 +210,10 @@ qsa_status qsa_decode_noalloc(const qsa_tensor *q, const qsa_tensor *k_pool,
  *   loc          [n] int32 or int64 slot ids, contiguous: row t of k_new /
  *                v_new is written to pool slot loc[t] (all Hkv heads).  The
  *                ids of one call must be distinct; with a repeated id the
- *                slot holds an unspecified mix of the rows written to it.
+ *                slot holds an unspecified mix of the rows written to it
+ *                (each scale is one of theirs; codes may mix) and must not
+ *                be read until a later call writes it again.  Every other
+ *                slot is written exactly.
  *   k_pool, v_pool, kv_scales  as for qsa_decode; written in place.
  *
  * Per (token, KV head, group of group_size channels), in fp32 with ties to

@@ -291,3 +291,41 @@ def test_store_quotients_near_rounding_boundaries(fmt, group, scale_dtype):
     torch.cuda.synchronize()
     exp = _expected(*host, xk, xv, loc, fmt, group, scale_dtype)
     _check_pools(dev, exp, label)
+
+
+@pytest.mark.parametrize("fmt,group", [("int8", 64), ("int4", 32), ("fp8", 256)])
+def test_store_repeated_slot_leaves_every_other_slot_exact(fmt, group):
+    """qsa.h: the slot ids of one call must be distinct; a repeated id leaves
+    that slot holding an unspecified mix of the rows written to it.  The
+    rest of the call stays exact: every other written slot equals the
+    oracle's quantization, every unwritten slot keeps its bytes, and each
+    scale of the repeated slot is the one of the two tokens' (a scale is a
+    single store)."""
+    rng = np.random.default_rng(zlib.crc32(f"dup/{fmt}/{group}".encode()))
+    slots, n, hkv = 2000, 300, 2
+    host, dev = _pools(rng, slots, hkv, fmt, group, "f16")
+    xk = _source_rows(rng, n, hkv, fmt, group)
+    xv = _source_rows(rng, n, hkv, fmt, group)
+    loc = rng.permutation(slots)[:n].astype(np.int64)
+    loc[200] = loc[17]                              # tokens 17 and 200 both name one slot
+    dup = int(loc[17])
+    say(f"[gpu] store {fmt} g{group}: slot {dup} named twice")
+    qsa.kv_store(xk.cuda(), xv.cuda(), torch.from_numpy(loc.astype(np.int32)).cuda(), dev[0], dev[1],
+                 kv_format=fmt, k_scale=dev[2], v_scale=dev[3], group_size=group)
+    torch.cuda.synchronize()
+    keep = np.ones(n, bool)
+    keep[[17, 200]] = False
+    kt = torch.from_numpy(keep)
+    ek, ev, eks, evs = _expected(*host, xk[kt], xv[kt], loc[keep], fmt, group, "f16")
+    other = np.arange(slots) != dup
+    for name, got, want in (("k codes", dev[0].cpu().numpy().view(np.uint8), ek.view(np.uint8)),
+                            ("v codes", dev[1].cpu().numpy().view(np.uint8), ev.view(np.uint8)),
+                            ("k scales", dev[2].float().cpu().numpy().view(np.uint32),
+                             eks.astype(np.float32).view(np.uint32)),
+                            ("v scales", dev[3].float().cpu().numpy().view(np.uint32),
+                             evs.astype(np.float32).view(np.uint32))):
+        assert np.array_equal(got[other], want[other]), f"{fmt}: {name} of other slots differ"
+    for name, x, d in (("k", xk, dev[2]), ("v", xv, dev[3])):
+        tok = quant.quantize(x[[17, 200]], fmt, group, "f16")[1]
+        s_dup = d[dup].float().cpu().numpy()
+        assert np.all((s_dup == tok[0]) | (s_dup == tok[1])), f"{fmt}: {name} scale of the repeated slot"
