@@ -157,6 +157,19 @@ constexpr int kLdsRow = kHeadDim * 2 + 16;
 // (unpadded, rows 1 KB apart put all 16 into the same banks)
 constexpr int kAccRow = kHeadDim + 4;
 
+// Maximum of x over the four 16-lane groups of the wave (lanes l, l ^ 16,
+// l ^ 32, l ^ 48), with the gfx950 row-swap permutes instead of LDS
+// permutes: with both operands x, v_permlane16_swap returns rows (0,0,2,2)
+// and (1,1,3,3) of x, and v_permlane32_swap halves (0,0) and (1,1).
+__device__ __forceinline__ float max_over_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m16 = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t v = __float_as_uint(m16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -537,10 +550,15 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     wave_lds_fence();
     f32x4 s;
     if constexpr (NG <= 1) {
-      s = f32x4{0.f, 0.f, 0.f, 0.f};
+      // two accumulation chains of 4 products (even and odd channel
+      // blocks) instead of one of 8, added at the end
+      f32x4 s_even = f32x4{0.f, 0.f, 0.f, 0.f}, s_odd = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk), qfrag(kk), s, 0, 0, 0);
+      for (int kk = 0; kk < 8; kk += 2) {
+        s_even = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk), qfrag(kk), s_even, 0, 0, 0);
+        s_odd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk + 1), qfrag(kk + 1), s_odd, 0, 0, 0);
+      }
+      s = s_even + s_odd;
     }
     if constexpr (NG == 1) {
       const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ksc + 4 * qg);
@@ -566,9 +584,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     float s2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) s2[e] = (jbase + e < nkeys) ? s[e] * kScaleLog2 : -INFINITY;
-    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = max_over_groups(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float pr[4];
