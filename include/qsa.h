@@ -358,8 +358,11 @@ int64_t qsa_workspace_bytes(void);
 const char *qsa_last_error(void);
 
 /* Split plan qsa_decode uses for (bs, hkv): number of splits per (row, KV
- * head) and the launch's workgroup count.  It depends on (bs, hkv) and the
- * options only, never on live lengths. */
+ * head) and the launch's workgroup count over bf16 pools,
+ * ceil(bs * hkv / 8) * 8 * splits.  Quantized and tiered pools place every
+ * KV head of a row on one XCD and launch ceil(bs / 8) * 8 * hkv * splits
+ * workgroups (the same count unless hkv = 2 and bs mod 8 is 1..4).  The plan
+ * depends on (bs, hkv) and the options only, never on live lengths. */
 qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
 
 /* Tuning knobs (bench and tests only):

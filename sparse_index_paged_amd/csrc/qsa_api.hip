@@ -60,6 +60,9 @@ std::atomic<int64_t> g_splits{0};     // > 0: exactly this many splits (tuning)
 // more splits shorten each workgroup's dependent chain of tiles until the
 // gather is bound by HBM, and each one lengthens the merge.  Only split
 // counts a full row can activate are priced.
+// (Quantized pools place rows, not pairs, on the XCDs: with Hkv = 2 and bs
+// mod 8 in 1..4 their busiest XCD holds one pair more than the model's
+// ceil(P/8); the plan is the same for every format.)
 // split_target > 0 replaces the model by "about split_target workgroups";
 // splits > 0 fixes the split count.
 int plan_splits(int bs, int hkv) {
@@ -97,8 +100,9 @@ int plan_splits(int bs, int hkv) {
   return best;
 }
 
+// Workgroups of a launch over bf16 pools (quantized pools: decode_workgroups)
 int64_t plan_workgroups(int bs, int hkv, int splits) {
-  return ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8 * splits;
+  return qsa::decode_workgroups(qsa::kFmtBF16, bs, hkv, splits);
 }
 
 // Waves per workgroup.  4-wave workgroups leave two resident per CU, which
@@ -111,8 +115,11 @@ int64_t plan_workgroups(int bs, int hkv, int splits) {
 // 4 -> 8 waves): fp8 59.8 -> 60.1 / 53.6 -> 48.5 / 36.7 -> 36.4 / 25.8 -> 24.3 us,
 // int8 g64 68.7 -> 65.1 / 64.3 -> 52.1 / 40.6 -> 39.6 / 29.3 -> 26.0 us,
 // int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 -> 27.9 us; bf16
-// is faster with 4.  An 8-wave workgroup takes 151 KB of LDS, so only one
-// fits on a CU: grids of more than 256 workgroups (two per CU) keep 4 waves.
+// is faster with 4.  Keeping the full depth of tiles in flight with 8 waves
+// (twice the bytes per CU) was slower at every measured point (bs=128 TP1
+// fp8 59.3 -> 60.8, int4 55.8 -> 61.0 us).  An 8-wave workgroup takes 151 KB
+// of LDS, so only one fits on a CU: grids of more than 256 workgroups (two
+// per CU) keep 4 waves.
 int waves_for(int fmt, int64_t workgroups) {
   const int64_t forced = g_waves.load();
   if (forced == 4 || forced == 8) return static_cast<int>(forced);
@@ -707,7 +714,7 @@ qsa_status prepare_pooled_decode(const char *fn, const qsa_tensor *q, const qsa_
   p.scale_f16 = pd->scale_f16;
   p.a32 = addresses_fit_32(*pd, k_pool, v_pool) ? 1 : 0;
   p.slots = pd->slots;
-  p.waves = waves_for(pd->fmt, plan_workgroups(p.bs, p.hkv, p.nsplit));
+  p.waves = waves_for(pd->fmt, qsa::decode_workgroups(pd->fmt, p.bs, p.hkv, p.nsplit));
   return QSA_OK;
 }
 
@@ -888,7 +895,7 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.ring.owner = static_cast<const int32_t *>(pool->owner.data);
   p.ring.mask = static_cast<uint32_t>(td.ring.slots - 1);
   p.a32 = tiered_fits_32(pool, td, &p) ? 1 : 0;
-  p.waves = waves_for(qsa::kFmtTIERED, plan_workgroups(p.bs, p.hkv, p.nsplit));
+  p.waves = waves_for(qsa::kFmtTIERED, qsa::decode_workgroups(qsa::kFmtTIERED, p.bs, p.hkv, p.nsplit));
   const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();

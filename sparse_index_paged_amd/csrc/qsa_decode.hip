@@ -48,7 +48,9 @@
 //     channels (a ring scale twice).
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
-//     one L2.
+//     one L2; with quantized pools all KV heads of a row share the XCD as
+//     well, so the scale lines they both read come from memory once
+//     (qsa_internal.h, decode_workgroups).
 #include <type_traits>
 
 #include "qsa_internal.h"
@@ -237,16 +239,26 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   const int ldrow = (lane / GEO::kLPR) * NI;  // first tile row this lane loads
   const int lchunk = lane % GEO::kLPR;       // its 16-byte chunk of each row
 
-  // ---- workgroup -> (pair, split); splits of a pair share blockIdx % 8
-  const int npairs = bs_lead * hkv_lead;
+  // ---- workgroup -> (row b, KV head g, split); the splits of a pair
+  // share blockIdx % 8 (the XCD), and with quantized pools so do all KV
+  // heads of a row (decode_workgroups)
   const int wg = blockIdx.x;
   const int local = wg >> 3;
   const int pp = local / nsplit_lead;
   const int split = local - pp * nsplit_lead;
-  const int pair = pp * 8 + (wg & 7);
-  if (pair >= npairs) return;
-  const int b = pair / hkv_lead;
-  const int g = pair - b * hkv_lead;
+  int b, g;
+  if constexpr (rows_share_xcd(FMT)) {
+    const int rb = (hkv_lead == 2) ? (pp >> 1) : pp;
+    g = pp - rb * hkv_lead;
+    b = rb * 8 + (wg & 7);
+    if (b >= bs_lead) return;
+  } else {
+    const int pair8 = pp * 8 + (wg & 7);
+    if (pair8 >= bs_lead * hkv_lead) return;
+    b = (hkv_lead == 2) ? (pair8 >> 1) : pair8;
+    g = pair8 - b * hkv_lead;
+  }
+  const int pair = b * hkv_lead + g;
 
   // ---- live row length from device cu_seqlens
   const int c0 = cu_lead[b];
@@ -993,8 +1005,7 @@ void launch_addr(const Params &p, dim3 grid, hipStream_t stream) {
 
 template <int FMT, int G>
 hipError_t launch_one(const Params &p, hipStream_t stream) {
-  const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
-  const dim3 grid(npairs8 * p.nsplit);
+  const dim3 grid(static_cast<unsigned>(decode_workgroups(FMT, p.bs, p.hkv, p.nsplit)));
   if constexpr (FMT == kFmtBF16) {
     launch_addr<FMT, G, false>(p, grid, stream);
   } else {
@@ -1025,11 +1036,10 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
       if (group == 64) return launch_one<kFmtINT4, 64>(p, stream);
       if (group == 32) return launch_one<kFmtINT4, 32>(p, stream);
       break;
-    case kFmtTIERED: {
-      const int npairs8 = ((p.bs * p.hkv + 7) / 8) * 8;
-      launch_addr<kFmtTIERED, 32, true>(p, dim3(npairs8 * p.nsplit), stream);
+    case kFmtTIERED:
+      launch_addr<kFmtTIERED, 32, true>(
+          p, dim3(static_cast<unsigned>(decode_workgroups(kFmtTIERED, p.bs, p.hkv, p.nsplit))), stream);
       return hipGetLastError();
-    }
     default: break;
   }
   return hipErrorInvalidValue;

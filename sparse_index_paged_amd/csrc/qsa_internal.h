@@ -22,6 +22,23 @@ constexpr int kPartFloats = 32 + kGqa * kHeadDim;
 // in the plain pool fields, the ring in Params::ring.
 enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3, kFmtTIERED = 4 };
 
+// Workgroup placement.  Workgroup w runs on XCD w % 8 (round-robin
+// dispatch), and every split of one (row, KV head) pair gets ids congruent
+// mod 8, so its partials stay in one L2.  bf16 pools deal the pairs out in
+// order: pair p = b * hkv + g on XCD p % 8.  Quantized pools put all KV
+// heads of row b on XCD b % 8: a slot's scales of every KV head share one
+// 128-byte line of the scale arrays, which the heads' workgroups then fetch
+// from that XCD's L2 once instead of from memory once per head.  The rows
+// are rounded up to a multiple of 8 for that, so the grid can hold up to
+// 8 * hkv idle pair slots more than the bf16 one.
+constexpr bool rows_share_xcd(int fmt) { return fmt != kFmtBF16; }
+
+inline int64_t decode_workgroups(int fmt, int bs, int hkv, int splits) {
+  const int64_t pairs8 = rows_share_xcd(fmt) ? ((static_cast<int64_t>(bs) + 7) / 8) * 8 * hkv
+                                             : ((static_cast<int64_t>(bs) * hkv + 7) / 8) * 8;
+  return pairs8 * splits;
+}
+
 // Device-side error bits (sticky, OR-ed into Params::err).
 constexpr uint32_t kErrRowRange = 1u;   // cu_seqlens out of range / row > 2055
 constexpr uint32_t kErrSlot = 2u;       // a slot id outside [0, slots)
