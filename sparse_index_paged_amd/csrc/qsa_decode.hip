@@ -493,9 +493,11 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   }
   __syncthreads();
   // Q's B operands do not change over the loop: instances with register
-  // room (no per-group K scales) keep all 8 in registers (32 VGPRs), which
-  // takes 8 KB of LDS reads off every tile; the others re-read them from LDS
-  constexpr bool QREG = NG <= 1 && !TIER;
+  // room keep all 8 in registers (32 VGPRs), which takes 8 KB of LDS reads
+  // off every tile -- those without per-group K scales, and every 8-wave
+  // instance (one tile in flight per wave leaves the room); the 4-wave
+  // group-scale and tiered instances re-read them from LDS
+  constexpr bool QREG = (NG <= 1 && !TIER) || W > 4;
   bf16x8 qreg[QREG ? 8 : 1];
   if constexpr (QREG) {
 #pragma unroll
