@@ -376,6 +376,14 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
  *                    workgroup per CU (256), else 4; 4 for bf16 pools
  *   "splits"         0 (default): as above; k >= 1: exactly k splits per
  *                    (row, KV head), at most max_splits
+ *   "xcc_lanes"      1 (default): bf16 workgroups take their (row, KV head)
+ *                    slot from the XCD they run on (XCC_ID) on a device that
+ *                    passed the dispatch check at its first call outside
+ *                    capture (8 XCDs, workgroup i of a launch on XCD
+ *                    (i + r) % 8); 0: from blockIdx only.  Outputs are
+ *                    bitwise the same either way.
+ *   "xcc_lanes_active" (read only) the current device's check: -1 not run
+ *                    yet, 0 failed (blockIdx placement), 1 passed
  * Changing them affects later launches and later reservations. */
 qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);

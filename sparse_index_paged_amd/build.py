@@ -20,10 +20,10 @@ HIPCC_FLAGS = [
     "-Wall",
     # no packed-fp32 VALU forms anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # leading scalar kernel arguments (up to 9 dwords) preloaded into scalar
+    # leading scalar kernel arguments (up to 10 dwords) preloaded into scalar
     # registers at wave launch; the code object keeps a prologue that loads
     # them itself where the dispatcher does not
-    "-mllvm", "-amdgpu-kernarg-preload-count=9",
+    "-mllvm", "-amdgpu-kernarg-preload-count=10",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -43,6 +43,7 @@ std::atomic<int64_t> g_max_splits{16};
 std::atomic<int64_t> g_min_split_keys{256};
 std::atomic<int64_t> g_waves{0};  // 0: chosen per call (waves_for)
 std::atomic<int64_t> g_splits{0};     // > 0: exactly this many splits (tuning)
+std::atomic<int64_t> g_xcc_lanes{1};  // 1: XCD-read bf16 placement where checked, 0: never
 
 // Splits per (row, KV head) pair.  The plan depends on (bs, hkv) and the
 // options only -- never on live lengths -- so captured graphs stay valid.
@@ -186,6 +187,57 @@ bool stream_capturing(hipStream_t stream) {
   hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
   return st != hipStreamCaptureStatusNone;
+}
+
+// ---- bf16 placement by the workgroup's own XCD (decode_workgroups) --------
+std::mutex g_xcc_mutex;
+int g_xcc_state[kMaxDevices];  // 0: not checked yet, 1: not used, 2: used
+
+// Every workgroup of a probe launch of n ran on XCD (i + r) % 8 for one r.
+bool xcc_round_robin(const int32_t *xcc, int n) {
+  const int r = xcc[0] & 7;
+  for (int i = 0; i < n; ++i)
+    if (xcc[i] != ((i + r) & 7)) return false;
+  return true;
+}
+
+// Whether device `dev` may place bf16 workgroups by their XCC_ID: it reports
+// 8 XCDs, and two probe launches of 1024 workgroups, one before and one after
+// a launch of 3 workgroups (which moves where the dispatcher starts), each
+// ran workgroup i on XCD (i + r) % 8 for a single r.  Runs once per device,
+// outside capture, allocating nothing; it synchronises `stream`.
+bool xcc_dispatch_check(int dev, hipStream_t stream) {
+  int nx = 0;
+  if (hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || nx != 8) {
+    (void)hipGetLastError();
+    return false;
+  }
+  constexpr int kN = 1024;
+  static_assert(2 * kN + 3 <= qsa::kXccProbeWords, "probe launches exceed the probe array");
+  static int32_t host[qsa::kXccProbeWords];
+  bool ok = qsa::launch_xcc_probe(0, kN, stream) == hipSuccess &&
+            qsa::launch_xcc_probe(2 * kN, 3, stream) == hipSuccess &&
+            qsa::launch_xcc_probe(kN, kN, stream) == hipSuccess &&
+            hipStreamSynchronize(stream) == hipSuccess &&
+            qsa::read_xcc_probe(host, 2 * kN) == hipSuccess;
+  ok = ok && xcc_round_robin(host, kN) && xcc_round_robin(host + kN, kN);
+  (void)hipGetLastError();
+  return ok;
+}
+
+// Params::xcc_lanes of a launch on `stream` (the device is checked at its
+// first call outside capture; a captured call before that one places
+// workgroups by blockIdx).
+int xcc_lanes_for(hipStream_t stream) {
+  if (g_xcc_lanes.load() == 0) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_xcc_mutex);
+  if (g_xcc_state[dev] == 0) {
+    if (stream_capturing(stream)) return 0;
+    g_xcc_state[dev] = xcc_dispatch_check(dev, stream) ? 2 : 1;
+  }
+  return g_xcc_state[dev] == 2 ? 1 : 0;
 }
 
 // Index of the private workspace bound to `stream` on `dev`, or -1 (the
@@ -770,7 +822,7 @@ const char *qsa_last_error(void) { return g_last_error; }
 qsa_status qsa_set_option(const char *name, int64_t value) {
   if (name == nullptr) return fail(QSA_ERR_ARG, "qsa_set_option: name is NULL");
   if (value < 0 || (value == 0 && strcmp(name, "split_target") != 0 && strcmp(name, "waves_per_workgroup") != 0 &&
-                     strcmp(name, "splits") != 0))
+                     strcmp(name, "splits") != 0 && strcmp(name, "xcc_lanes") != 0))
     return fail(QSA_ERR_ARG, "qsa_set_option: %s must be >= 1", name);
   if (!strcmp(name, "split_target")) {
     g_split_target = value;  // 0 restores the cost model
@@ -785,6 +837,9 @@ qsa_status qsa_set_option(const char *name, int64_t value) {
   } else if (!strcmp(name, "splits")) {
     if (value > 64) return fail(QSA_ERR_ARG, "qsa_set_option: splits must be <= 64");
     g_splits = value;
+  } else if (!strcmp(name, "xcc_lanes")) {
+    if (value > 1) return fail(QSA_ERR_ARG, "qsa_set_option: xcc_lanes must be 0 or 1");
+    g_xcc_lanes = value;
   } else {
     return fail(QSA_ERR_ARG, "qsa_set_option: unknown option '%s'", name);
   }
@@ -798,6 +853,14 @@ qsa_status qsa_get_option(const char *name, int64_t *value) {
   else if (!strcmp(name, "min_split_keys")) *value = g_min_split_keys;
   else if (!strcmp(name, "waves_per_workgroup")) *value = g_waves;
   else if (!strcmp(name, "splits")) *value = g_splits;
+  else if (!strcmp(name, "xcc_lanes")) *value = g_xcc_lanes;
+  else if (!strcmp(name, "xcc_lanes_active")) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+      return fail(QSA_ERR_HIP, "qsa_get_option: no HIP device");
+    std::lock_guard<std::mutex> lock(g_xcc_mutex);
+    *value = g_xcc_state[dev] - 1;  // -1: not checked yet, 0: not used, 1: used
+  }
   else return fail(QSA_ERR_ARG, "qsa_get_option: unknown option '%s'", name);
   return ok();
 }
@@ -822,6 +885,7 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
                                         out, lse, &p, &pd);
   if (st != QSA_OK) return st;
   if ((st = attach_workspace(fn, stream, &p)) != QSA_OK) return st;
+  p.xcc_lanes = xcc_lanes_for(stream);
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -849,6 +913,7 @@ qsa_status qsa_decode_noalloc(const qsa_tensor *q, const qsa_tensor *k_pool,
   p.part = reinterpret_cast<float *>(base);
   p.ctr = reinterpret_cast<uint32_t *>(base + kScratchPartFloats * sizeof(float));
   p.err = p.ctr + kCtrWords;
+  p.xcc_lanes = xcc_lanes_for(stream);
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -896,6 +961,7 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.ring.mask = static_cast<uint32_t>(td.ring.slots - 1);
   p.a32 = tiered_fits_32(pool, td, &p) ? 1 : 0;
   p.waves = waves_for(qsa::kFmtTIERED, qsa::decode_workgroups(qsa::kFmtTIERED, p.bs, p.hkv, p.nsplit));
+  p.xcc_lanes = xcc_lanes_for(stream);
   const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();

@@ -63,6 +63,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// s_getreg_b32 operand for the XCC_ID hardware register (hwreg 20, bits
+// 0..3): the XCD the wave runs on
+constexpr int kHwRegXccId = (3 << 11) | (0 << 6) | 20;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScaleLog2 = kLog2e / 16.0f;  // softmax scale 1/16 in log2 units
@@ -211,7 +215,8 @@ __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthre
 template <int FMT, int G, int W, bool SF16, bool A32>
 __global__ void __launch_bounds__(64 * W, 8 / W)
     qsa_decode_kernel(const int32_t *__restrict__ cu_lead, const int32_t *__restrict__ sel_lead, int bs_lead,
-                      int hkv_lead, int nsplit_lead, int msk_lead, int nsel_lead, const Params p) {
+                      int hkv_lead, int nsplit_lead, int msk_lead, int nsel_lead, int xcc_lead,
+                      const Params p) {
   using Part = typename Fmt<FMT>::Part;
   using GEO = Geo<FMT>;
   using LDS = Lds<W>;
@@ -253,7 +258,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     b = rb * 8 + (wg & 7);
     if (b >= bs_lead) return;
   } else {
-    const int pair8 = pp * 8 + (wg & 7);
+    const int x = xcc_lead ? (__builtin_amdgcn_s_getreg(kHwRegXccId) & 7) : (wg & 7);
+    const int pair8 = pp * 8 + x;
     if (pair8 >= bs_lead * hkv_lead) return;
     b = (hkv_lead == 2) ? (pair8 >> 1) : pair8;
     g = pair8 - b * hkv_lead;
@@ -968,6 +974,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// XCC_ID of every workgroup of the dispatch check's probe launches
+__device__ int32_t xcc_probe_out[kXccProbeWords];
+
+__global__ void xcc_probe_kernel(int base) {
+  if (threadIdx.x == 0) xcc_probe_out[base + blockIdx.x] = __builtin_amdgcn_s_getreg(kHwRegXccId) & 15;
+}
+
 __global__ void fill_u32_kernel(uint32_t *dst, int64_t n, uint32_t value) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = value;
@@ -991,10 +1004,10 @@ void launch_waves(const Params &p, dim3 grid, hipStream_t stream) {
   const int nsel = p.n_sel > 0x7FFFFFFF ? 0x7FFFFFFF : static_cast<int>(p.n_sel);
   if (p.waves == 8)
     hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 8, SF16, A32>), grid, dim3(512), 0, stream, p.cu, p.sel,
-                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p);
+                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p.xcc_lanes, p);
   else
     hipLaunchKernelGGL((qsa_decode_kernel<FMT, G, 4, SF16, A32>), grid, dim3(256), 0, stream, p.cu, p.sel,
-                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p);
+                       p.bs, p.hkv, p.nsplit, p.min_split_keys, nsel, p.xcc_lanes, p);
 }
 
 template <int FMT, int G, bool SF16>
@@ -1050,6 +1063,18 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
 hipError_t launch_audit(const uint32_t *ctr, int n, uint32_t *accum, hipStream_t stream) {
   hipLaunchKernelGGL(audit_kernel, dim3(1), dim3(256), 0, stream, ctr, n, accum);
   return hipGetLastError();
+}
+
+hipError_t launch_xcc_probe(int base, int blocks, hipStream_t stream) {
+  if (base < 0 || blocks <= 0 || base + blocks > kXccProbeWords) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, base);
+  return hipGetLastError();
+}
+
+hipError_t read_xcc_probe(int32_t *host, int n) {
+  if (n < 0 || n > kXccProbeWords) return hipErrorInvalidValue;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(xcc_probe_out), static_cast<size_t>(n) * sizeof(int32_t), 0,
+                             hipMemcpyDeviceToHost);
 }
 
 hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream) {

@@ -31,6 +31,16 @@ enum KvFormat : int { kFmtBF16 = 0, kFmtFP8 = 1, kFmtINT8 = 2, kFmtINT4 = 3, kFm
 // from that XCD's L2 once instead of from memory once per head.  The rows
 // are rounded up to a multiple of 8 for that, so the grid can hold up to
 // 8 * hkv idle pair slots more than the bf16 one.
+//
+// Which XCD a workgroup lands on depends on where the dispatcher starts its
+// round-robin, which differs between launches (graph replays start one XCD
+// further than eager launches here), while the bf16 order is fastest with
+// the two KV heads of a row on XCDs 2k and 2k + 1.  With Params::xcc_lanes
+// each bf16 workgroup therefore takes the pair slot of the XCD it reads from
+// its XCC_ID register instead of blockIdx % 8.  That stays a one-to-one
+// assignment only while every aligned block of 8 workgroups covers the 8
+// XCDs, so the library sets it only on a device that reports 8 XCDs and has
+// passed a dispatch check (xcc_dispatch_check).
 constexpr bool rows_share_xcd(int fmt) { return fmt != kFmtBF16; }
 
 inline int64_t decode_workgroups(int fmt, int bs, int hkv, int splits) {
@@ -79,6 +89,7 @@ struct Params {
   int nsplit;               // splits per (row, kv head) in the grid
   int waves;                // waves per workgroup: 4 or 8
   int min_split_keys;       // entries per split before another is used
+  int xcc_lanes;            // bf16 placement from the workgroup's own XCD (decode_workgroups)
   float *part;              // [npairs][nsplit][kPartFloats]
   uint32_t *ctr;            // [npairs], zero at rest
   uint32_t *err;            // sticky error word
@@ -144,6 +155,13 @@ hipError_t launch_index(const IndexParams &p, hipStream_t stream);
 
 // Launch the decode kernel for one call (grid = 8 * ceil(npairs/8) * nsplit).
 hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream);
+// Dispatch check probe (no allocation): `blocks` workgroups of 64 threads,
+// workgroup i writing the XCC_ID of its XCD to entry base + i of a
+// kXccProbeWords-entry device array, which read_xcc_probe copies to the host
+// (synchronously, from the current device).
+constexpr int kXccProbeWords = 2 * 1024 + 3;
+hipError_t launch_xcc_probe(int base, int blocks, hipStream_t stream);
+hipError_t read_xcc_probe(int32_t *host, int n);
 
 // Launch the quantize + scatter kernel (one wave per (token, kv head)).
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream);

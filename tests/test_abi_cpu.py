@@ -99,6 +99,15 @@ def test_plan_and_options():
         assert qsa.plan(128, 2)[0] == 8
     finally:
         qsa.set_option("split_target", 0)
+    # placement of bf16 workgroups by their XCD: on (1, the default) or off (0)
+    assert qsa.get_option("xcc_lanes") == 1
+    qsa.set_option("xcc_lanes", 0)
+    try:
+        assert qsa.get_option("xcc_lanes") == 0
+    finally:
+        qsa.set_option("xcc_lanes", 1)
+    with pytest.raises(qsa.QsaError, match="xcc_lanes must be 0 or 1"):
+        qsa.set_option("xcc_lanes", 2)
 
 
 # ---- contract rejection with fake (never dereferenced) device pointers ----

@@ -26,6 +26,7 @@ def _default_options():
     qsa.set_option("min_split_keys", 256)
     qsa.set_option("waves_per_workgroup", 0)
     qsa.set_option("splits", 0)
+    qsa.set_option("xcc_lanes", 1)
 
 
 def test_bs1_tp1_l128():
@@ -219,6 +220,51 @@ def test_bitwise_deterministic_and_plan_independent():
     torch.cuda.synchronize()
     diff = (o3.float() - o1.float()).norm() / o1.float().norm()
     assert diff < 2e-3 and (l3 - l1).abs().max() < 1e-4
+
+
+def test_xcd_placement_is_checked_and_changes_no_output():
+    """bf16 workgroups take their pair slot from the XCD they run on (XCC_ID)
+    once the device has passed the dispatch check: 8 XCDs, workgroup i on
+    XCD (i + r) % 8.  Which workgroup computes a (row, KV head, split) does
+    not enter its arithmetic, so the outputs with that placement, with the
+    blockIdx placement, and replayed from a captured graph are bitwise equal;
+    the oracle checks the rows once."""
+    qsa.set_option("xcc_lanes", 1)
+    case = synth.make_case(lengths=[2055] * 20 + [900] * 12 + [5] * 4, slots=20000, hkv=2, seed=43,
+                           dup_prob=0.05)
+    d = to_device(case)
+    o1, l1 = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+    torch.cuda.synchronize()
+    if qsa.get_option("xcc_lanes_active") != 1:
+        pytest.skip("this device did not pass the dispatch check (fewer than 8 XCDs or no "
+                    "round-robin dispatch); placement by blockIdx is used")
+    o_ref, l_ref = oracle_rows(case.q, case.k_pool, case.v_pool, case.sel, case.cu, None)
+    compare(o1, l1, o_ref, l_ref, case.lengths, label="XCD-read placement")
+    for splits in (0, 3):
+        qsa.set_option("splits", splits)
+        try:
+            qsa.set_option("xcc_lanes", 1)
+            oa, la = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+            qsa.set_option("xcc_lanes", 0)
+            ob, lb = qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"])
+            torch.cuda.synchronize()
+            assert torch.equal(oa, ob) and torch.equal(la, lb), f"splits={splits}"
+            qsa.set_option("xcc_lanes", 1)
+            out = torch.empty_like(oa)
+            lse = torch.empty_like(la)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                qsa.decode(d["q"], d["k"], d["v"], d["sel"], d["cu"], out=out, lse=lse)
+            for _ in range(3):
+                out.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                assert torch.equal(out, oa) and torch.equal(lse, la), f"graph, splits={splits}"
+            del g
+        finally:
+            qsa.set_option("xcc_lanes", 1)
+            qsa.set_option("splits", 0)
+    assert all(v == 0 for v in qsa.debug_counters())
 
 
 def test_controls_k_zero_v_zero():
