@@ -30,10 +30,12 @@
 //
 // x / scale must be the correctly rounded fp32 quotient, because the codes
 // round it once more.  The quotient is first taken as x * rcp(scale)
-// (within 2 ulp of the rounded quotient); only when that value lies within
-// 8 ulp of a rounding boundary of the code (a half-integer for int8 / int4,
-// a midpoint of the e4m3fn grid for fp8) is the full IEEE division done, so
-// the codes equal those of the division everywhere.
+// (within 2 ulp of the rounded quotient), and a cheap test shows whether a
+// rounding boundary of the code could lie between the two: for int8 / int4
+// the residual x - q * scale of the rounded code q (one fused multiply-add),
+// for fp8 the hardware e4m3fn conversion of the value moved by +-2^-20 of
+// itself (both must give one code).  Only where the test fails is the full
+// IEEE division done, so the codes equal those of the division everywhere.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -41,46 +43,19 @@ namespace {
 
 constexpr int kRowsPerWave = 4;
 
-// e4m3fn code of y with |y| <= 448, rounded to nearest even.  Normal codes
-// come from rounding the fp32 significand to 3 bits (a carry moves into the
-// exponent); below 2^-6 the code is the subnormal multiple of 2^-9.
-__device__ __forceinline__ uint32_t e4m3fn_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const float af = __uint_as_float(a);
-  uint32_t code;
-  if (af < 0x1p-6f)
-    code = static_cast<uint32_t>(__builtin_rintf(af * 512.0f));
-  else
-    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-  return sign | code;
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// OCP e4m3fn codes of a and b (|a|, |b| <= 448), rounded to nearest even by
+// the gfx950 conversion (scale 1): a in bits 0..7, b in bits 8..15.
+__device__ __forceinline__ uint32_t e4m3fn_pair(float a, float b) {
+  const i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, a, b, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
 }
 
-// True when rint(v) could change if v moved by up to 8 ulp (or v is not finite).
-__device__ __forceinline__ bool near_half_integer(float v) {
-  const float d = fabsf(v - floorf(v) - 0.5f);
-  return !(d > fmaxf(fabsf(v), 1.0f) * 0x1p-20f);
-}
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
-// Same for the e4m3fn rounding of clamp(v, -448, 448).
-__device__ __forceinline__ bool near_e4m3_boundary(float v) {
-  const float a = fabsf(v);
-  if (!(a <= 448.0f)) return !(a > 448.0f) || a < 456.0f;  // NaN, or just above the clamp
-  if (a < 0x1p-6f) return near_half_integer(a * 512.0f);
-  const int32_t m = static_cast<int32_t>(__float_as_uint(a) & 0xFFFFFu) - 0x80000;
-  return m >= -8 && m <= 8;
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t code_of(float y) {
-  if constexpr (FMT == kFmtINT8)
-    return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f))) & 0xFFu;
-  else if constexpr (FMT == kFmtINT4)
-    return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(__builtin_rintf(y), -7.0f), 7.0f)) + 8);
-  else
-    return e4m3fn_rne(fminf(fmaxf(y, -448.0f), 448.0f));
-}
+// x / sc rounded once (the IEEE quotient), 0 for a zero scale
+__device__ __forceinline__ float quotient(float x, float sc) { return sc > 0.f ? __fdiv_rn(x, sc) : 0.f; }
 
 template <int FMT>
 __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
@@ -159,15 +134,44 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
         else
           reinterpret_cast<float *>(sd)[gi] = sc;
       }
-      const float rs = __builtin_amdgcn_rcpf(sc);
+      // Codes from y = x * rcp(sc), within 2 ulp of the IEEE quotient x / sc;
+      // only where that could change a code is the quotient itself taken.
+      const bool zs = !(sc > 0.f);  // zero scale: zero codes
+      const float rs = zs ? 0.f : __builtin_amdgcn_rcpf(sc);
       uint32_t c[8];
+      if constexpr (FMT == kFmtFP8) {
+        // the codes of y(1 - 2^-20) and y(1 + 2^-20) agree only when no
+        // midpoint of the e4m3fn grid (and not the clamp) lies within
+        // 2^-20 |y| of y, which holds the quotient; rounding is monotonic
+        constexpr float kDown = 1.0f - 0x1p-20f, kUp = 1.0f + 0x1p-20f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = x[e] * rs;
-        const bool near = (FMT == kFmtFP8) ? near_e4m3_boundary(y) : near_half_integer(y);
-        if (near) y = __fdiv_rn(x[e], sc);
-        if (!(sc > 0.f)) y = 0.f;
-        c[e] = code_of<FMT>(y);
+        for (int e = 0; e < 8; e += 2) {
+          const float y0 = clamp448(x[e] * rs), y1 = clamp448(x[e + 1] * rs);
+          uint32_t two = e4m3fn_pair(clamp448(y0 * kDown), clamp448(y1 * kDown));
+          if (two != e4m3fn_pair(clamp448(y0 * kUp), clamp448(y1 * kUp)))
+            two = e4m3fn_pair(clamp448(quotient(x[e], sc)), clamp448(quotient(x[e + 1], sc)));
+          if (zs) two = 0u;
+          c[e] = two & 0xFFu;
+          c[e + 1] = two >> 8;
+        }
+      } else {
+        // q = rint(y) is the code's rounding of the IEEE quotient Q' = x / sc
+        // when the residual x - q * sc (one fused multiply-add, rounded once)
+        // puts the exact quotient within 1/2 - kQ 2^-20 of q: Q' differs from
+        // it by at most half an ulp (2^-18 for |Q| < 128, 2^-22 for |Q| < 8),
+        // so Q' is no half-integer tie and rounds to q as well (beyond kQ the
+        // clamp decides).  Otherwise (or for a non-finite value) Q' is taken.
+        const float half = zs ? INFINITY : sc * (0.5f - kQ * 0x1p-20f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float q = __builtin_rintf(x[e] * rs);
+          if (!(fabsf(__builtin_fmaf(-q, sc, x[e])) < half)) q = __builtin_rintf(quotient(x[e], sc));
+          q = fminf(fmaxf(q, -kQ), kQ);
+          if constexpr (FMT == kFmtINT8)
+            c[e] = static_cast<uint32_t>(static_cast<int>(q)) & 0xFFu;
+          else
+            c[e] = static_cast<uint32_t>(static_cast<int>(q) + 8);
+        }
       }
       if constexpr (FMT == kFmtINT4) {
         uint32_t packed = 0;
