@@ -49,8 +49,12 @@
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
 //     one L2; with quantized pools all KV heads of a row share the XCD as
-//     well, so the scale lines they both read come from memory once
-//     (qsa_internal.h, decode_workgroups).
+//     well, so the scale lines they both read come from memory once.  bf16
+//     workgroups, once the library has checked the device's dispatch, take
+//     their pair slot from the XCD they read in XCC_ID rather than from
+//     blockIdx % 8, which keeps the two KV heads of a row on neighbouring
+//     XCDs whichever XCD the dispatcher starts at (qsa_internal.h,
+//     decode_workgroups).
 #include <type_traits>
 
 #include "qsa_internal.h"
@@ -246,7 +250,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 
   // ---- workgroup -> (row b, KV head g, split); the splits of a pair
   // share blockIdx % 8 (the XCD), and with quantized pools so do all KV
-  // heads of a row (decode_workgroups)
+  // heads of a row; with xcc_lead a bf16 workgroup takes slot x of its
+  // group of 8 pairs from the XCD it runs on (decode_workgroups)
   const int wg = blockIdx.x;
   const int local = wg >> 3;
   const int pp = local / nsplit_lead;
