@@ -267,6 +267,41 @@ def test_xcd_placement_is_checked_and_changes_no_output():
     assert all(v == 0 for v in qsa.debug_counters())
 
 
+@pytest.mark.parametrize("fmt,group,sdt", [("fp8", 256, torch.float32), ("int8", 64, torch.float16),
+                                          ("int4", 32, torch.float16)])
+def test_interleaved_scale_views_give_the_same_outputs(fmt, group, sdt):
+    """K and V scales written and read as views of one [slots, 2, Hkv, groups]
+    array (k_scale = [:, 0], v_scale = [:, 1]) instead of two arrays: the
+    store writes the same codes and scales, the decode gives bitwise the same
+    out and lse, and both match the oracle."""
+    lens = [2055, 1, 700, 0, 1500, 2055, 33]
+    case = synth.make_case(lengths=lens, slots=4096, hkv=2, seed=7000 + group, dup_prob=0.05)
+    d = to_device(case)
+    slots, width, ng = 4096, (128 if fmt == "int4" else 256), 256 // group
+    cdt = torch.int8 if fmt == "int8" else torch.uint8
+    loc = torch.arange(slots, dtype=torch.int32, device="cuda")
+    buf = torch.empty(slots, 2, 2, ng, dtype=sdt, device="cuda")
+    res = []
+    for ks, vs in ((torch.empty(slots, 2, ng, dtype=sdt, device="cuda"),
+                    torch.empty(slots, 2, ng, dtype=sdt, device="cuda")), (buf[:, 0], buf[:, 1])):
+        kc = torch.empty(slots, 2, width, dtype=cdt, device="cuda")
+        vc = torch.empty_like(kc)
+        qsa.kv_store(d["k"], d["v"], loc, kc, vc, kv_format=fmt, k_scale=ks, v_scale=vs, group_size=group)
+        o, l = qsa.decode(d["q"], kc, vc, d["sel"], d["cu"], kv_format=fmt, k_scale=ks, v_scale=vs,
+                          group_size=group)
+        torch.cuda.synchronize()
+        res.append((kc, vc, ks, vs, o, l))
+    (k1, v1, ks1, vs1, o1, l1), (k2, v2, ks2, vs2, o2, l2) = res
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(ks1, ks2) and torch.equal(vs1, vs2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    kq, kss = quant.quantize(case.k_pool, fmt, group, "f16" if sdt == torch.float16 else "f32")
+    vq, vss = quant.quantize(case.v_pool, fmt, group, "f16" if sdt == torch.float16 else "f32")
+    o_ref, l_ref = oracle_rows(case.q, kq, vq, case.sel, case.cu, None, fmt=fmt, group=group,
+                               k_scale=kss, v_scale=vss)
+    compare(o2, l2, o_ref, l_ref, case.lengths, label=f"interleaved scales {fmt} g{group}")
+
+
 def test_controls_k_zero_v_zero():
     """K := 0 gives uniform weights (mean of the listed V rows, lse = ln L);
     V := 0 gives exactly zero."""
