@@ -111,16 +111,16 @@ int64_t plan_workgroups(int bs, int hkv, int splits) {
 // formats are bound by per-tile ALU work (dequantization, and for the
 // tiered pool the tier selection), so they run as 8-wave workgroups: two
 // waves per SIMD overlap one wave's dequantization with the other's memory
-// wait, and each wave keeps half as many tiles in flight, so a CU holds the
-// same bytes in flight.  Measured on MI355X (bs=128 / 96 / 64 / 32 TP1,
-// 4 -> 8 waves): fp8 59.8 -> 60.1 / 53.6 -> 48.5 / 36.7 -> 36.4 / 25.8 -> 24.3 us,
-// int8 g64 68.7 -> 65.1 / 64.3 -> 52.1 / 40.6 -> 39.6 / 29.3 -> 26.0 us,
-// int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 -> 27.9 us; bf16
-// is faster with 4.  Keeping the full depth of tiles in flight with 8 waves
-// (twice the bytes per CU) was slower at every measured point (bs=128 TP1
-// fp8 59.3 -> 60.8, int4 55.8 -> 61.0 us).  An 8-wave workgroup takes 151 KB
-// of LDS, so only one fits on a CU: grids of more than 256 workgroups (two
-// per CU) keep 4 waves.
+// wait, and each wave keeps one tile in flight.  Measured on MI355X (bs=128 /
+// 96 / 64 / 32 TP1, 4 -> 8 waves): fp8 59.8 -> 60.1 / 53.6 -> 48.5 / 36.7 ->
+// 36.4 / 25.8 -> 24.3 us, int8 g64 68.7 -> 65.1 / 64.3 -> 52.1 / 40.6 -> 39.6 /
+// 29.3 -> 26.0 us, int4 g32 73.2 -> 58.0 / 71.9 -> 56.0 / 44.7 -> 37.9 / 31.3 ->
+// 27.9 us (two int4 tiles in flight then; one is faster again: bs=128 / 64 /
+// 32 TP1 54.2 -> 52.8 / 35.1 -> 33.9 / 25.8 -> 25.0 us); bf16 is faster with
+// 4.  More tiles in flight with 8 waves was slower at every measured point
+// (bs=128 TP1 fp8 59.3 -> 60.8, int4 55.8 -> 61.0 us).  An 8-wave workgroup
+// takes 151 KB of LDS, so only one fits on a CU: grids of more than 256
+// workgroups (two per CU) keep 4 waves.
 int waves_for(int fmt, int64_t workgroups) {
   const int64_t forced = g_waves.load();
   if (forced == 4 || forced == 8) return static_cast<int>(forced);

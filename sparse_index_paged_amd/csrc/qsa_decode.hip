@@ -230,12 +230,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
-  // tiles in flight: as many as fit the register budget of one bf16 tile
-  // (8 row loads per lane for K and for V), so narrower formats keep as many
-  // bytes in flight per wave as bf16 does -- halved for 8-wave workgroups,
-  // so that a CU holds the same bytes in flight; a tiered pool keeps one
-  // (its owner ids and tier selects take the registers of a second)
-  constexpr int D = TIER ? 1 : ((W > 4 && 8 / NI > 1) ? 4 / NI : 8 / NI);
+  // tiles in flight: with 4-wave workgroups as many as fit the register
+  // budget of one bf16 tile (8 row loads per lane for K and for V), so
+  // narrower formats keep as many bytes in flight per wave as bf16 does;
+  // 8-wave workgroups (two waves per SIMD) and tiered pools keep one (more
+  // was slower for every format: the second wave covers the wait, and a
+  // tiered pool's owner ids and tier selects take the registers)
+  constexpr int D = (TIER || W > 4) ? 1 : 8 / NI;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
