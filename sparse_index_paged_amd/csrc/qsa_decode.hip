@@ -155,6 +155,37 @@ template <> __device__ __forceinline__ uint4 to_bf16x8<kFmtINT4>(uint32_t r) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// int8 codes as exact bf16 in the channel order 0, 2, 4, 6, 1, 3, 5, 7 of
+// int4_offset_bf16x8 (the ring rows of a tiered pool share the LDS tiles
+// with its int4 rows)
+__device__ __forceinline__ uint4 int8_bf16x8_permuted(uint2 r) {
+  auto code = [](uint32_t src, int byte) { return static_cast<float>(static_cast<int8_t>(src >> (8 * byte))); };
+  return make_uint4(pack_bf16_exact(code(r.x, 0), code(r.x, 2)), pack_bf16_exact(code(r.y, 0), code(r.y, 2)),
+                    pack_bf16_exact(code(r.x, 1), code(r.x, 3)), pack_bf16_exact(code(r.y, 1), code(r.y, 3)));
+}
+
+// int4 codes of 8-wave workgroups: nibble n = code + 8
+// becomes the top four of the seven mantissa bits of a bf16 whose exponent
+// is 3 (bits 0x4100 | n << 3), the exact value 8 + n / 2 = 12 + code / 2.
+// Eight codes cost two shift-and-masks and four byte permutes, and come out
+// in the order 0, 2, 4, 6, 1, 3, 5, 7 of their channels.  The kernel stores
+// Q's channels in the same order, stages the scales of such rows doubled
+// (exact), and takes the offset out with the group sums of Q (QK) and of the
+// scaled weights (PV).
+__device__ __forceinline__ uint4 int4_offset_bf16x8(uint32_t r) {
+  const uint32_t ev = (r << 3) & 0x78787878u;  // byte i: nibble 2i << 3
+  const uint32_t od = (r >> 1) & 0x78787878u;  // byte i: nibble 2i+1 << 3
+  constexpr uint32_t kHi = 0x41414141u;        // sign and exponent byte
+  return make_uint4(__builtin_amdgcn_perm(kHi, ev, 0x04010400u), __builtin_amdgcn_perm(kHi, ev, 0x04030402u),
+                    __builtin_amdgcn_perm(kHi, od, 0x04010400u), __builtin_amdgcn_perm(kHi, od, 0x04030402u));
+}
+
+// Q chunk (8 bf16, channels 0..7) in the order of int4_offset_bf16x8
+__device__ __forceinline__ uint4 int4_channel_order(uint4 q) {
+  return make_uint4(__builtin_amdgcn_perm(q.y, q.x, 0x05040100u), __builtin_amdgcn_perm(q.w, q.z, 0x05040100u),
+                    __builtin_amdgcn_perm(q.y, q.x, 0x07060302u), __builtin_amdgcn_perm(q.w, q.z, 0x07060302u));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // LDS rows of the V and Q tiles are padded from 512 to 528 bytes: the
@@ -193,10 +224,11 @@ __device__ __forceinline__ void wave_lds_fence() {
 // the split merge's per-wave weight tables [4][64][16] reuse the start of
 // the buffer.  A workgroup of 8 waves first folds waves 4..7 into 0..3
 // through [4][16 f32x4][64 lanes].
-template <int W> struct Lds {
+template <int W, bool FLAGS> struct Lds {
   static constexpr int kTileB = kTile * kLdsRow;               // one bf16 tile [16][528 B]
   static constexpr int kScaleFloats = kTile * 8;               // up to 8 groups per row
-  static constexpr int kWave = 2 * kTileB + 2 * kScaleFloats * 4;
+  static constexpr int kFlagFloats = FLAGS ? kTile : 0;        // tiered: 1 for an int4 row
+  static constexpr int kWave = 2 * kTileB + (2 * kScaleFloats + kFlagFloats) * 4;
   static constexpr int kLoop = W * kWave;
   static constexpr int kQ = 16 * kLdsRow;
   static_assert(4 * 64 * 16 * 4 <= kLoop, "split-merge weight tables exceed the loop area");
@@ -223,10 +255,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
                       const Params p) {
   using Part = typename Fmt<FMT>::Part;
   using GEO = Geo<FMT>;
-  using LDS = Lds<W>;
-  using Scale = typename std::conditional<SF16, _Float16, float>::type;
   constexpr bool TIER = FMT == kFmtTIERED;
+  // int4 codes (of int4 pools and of the int4 rows of tiered pools) staged
+  // as 12 + code / 2 in permuted channel order (int4_offset_bf16x8) by
+  // 8-wave workgroups; the 4-wave instances, which keep more tiles in
+  // flight, have no registers left for the offsets
+  constexpr bool I4OFF = (FMT == kFmtINT4 || TIER) && W > 4;
+  using LDS = Lds<W, I4OFF && TIER>;
+  using Scale = typename std::conditional<SF16, _Float16, float>::type;
   static_assert(!TIER || (G == 32 && SF16), "tiered pools: f16 scales staged per 32 channels");
+  static_assert(!I4OFF || (G >= 32 && G < kHeadDim), "int4 rows: 2 to 8 channel groups");
   constexpr int kThr = 64 * W;
   constexpr int NG = (FMT == kFmtBF16) ? 0 : kHeadDim / G;   // scale groups per row
   constexpr int NI = GEO::kNI;
@@ -300,6 +338,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   unsigned char *vt = wlds + LDS::kTileB;                            // [16][528 B]
   float *ksc = reinterpret_cast<float *>(wlds + 2 * LDS::kTileB);    // [16][NG]
   float *vsc = ksc + LDS::kScaleFloats;                              // [16][NG]
+  float *i4row = vsc + LDS::kScaleFloats;                            // tiered: [16] 1 = int4 row
 
   // Row addresses.  With A32 (every pool byte within 4 GiB of the pool
   // start, slot ids and strides below 2^24) a row's address is a
@@ -500,7 +539,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int idx = tid * CPT + i;
-      *reinterpret_cast<uint4 *>(qlds + (idx >> 5) * kLdsRow + (idx & 31) * 16) = qv[i];
+      *reinterpret_cast<uint4 *>(qlds + (idx >> 5) * kLdsRow + (idx & 31) * 16) =
+          I4OFF ? int4_channel_order(qv[i]) : qv[i];
     }
   }
   __syncthreads();
@@ -520,6 +560,34 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     if constexpr (QREG) return qreg[kk];
     return as_bf16x8(*reinterpret_cast<const uint4 *>(qlds + r16 * kLdsRow + (4 * kk + qg) * 16));
   };
+  // int4 rows: 12 x the sum of head r16's Q over each channel group (the QK
+  // offset of int4_offset_bf16x8); chunk 4*kk + qg of this lane lies in
+  // group 32*kk / G, and the four lane groups hold the other chunks
+  float qoff[I4OFF ? NG : 1];
+  if constexpr (I4OFF) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) qoff[gi] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 f = qfrag(kk);
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += static_cast<float>(f[i]);
+      qoff[32 * kk / G] += sum;
+    }
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      qoff[gi] += __shfl_xor(qoff[gi], 16);
+      qoff[gi] += __shfl_xor(qoff[gi], 32);
+      qoff[gi] *= 12.0f;
+    }
+  }
+  // int4 rows: running sum over this lane's int4 entries of the weights
+  // times the (doubled) V scale of each channel group (the PV offset),
+  // rescaled with the accumulators
+  float voff[I4OFF ? NG : 1];
+#pragma unroll
+  for (int gi = 0; gi < (I4OFF ? NG : 1); ++gi) voff[gi] = 0.0f;
   // K operand: channel chunk 4*kk + qg of row r16
   const unsigned char *krow = kt + r16 * kLdsRow + (qg % P) * kPartB + (qg / P) * 16;
   auto kfrag = [&](int kk) -> bf16x8 {
@@ -534,17 +602,25 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       const int off = (ldrow + i) * kLdsRow + lchunk * 16;
       if constexpr (TIER) {
         uint4 k0, k1, v0, v1;
+        auto ring8 = [](uint32_t a, uint32_t b) {
+          if constexpr (I4OFF) return int8_bf16x8_permuted(make_uint2(a, b));
+          return to_bf16x8<kFmtINT8>(make_uint2(a, b));
+        };
+        auto pool4 = [](uint32_t a) {
+          if constexpr (I4OFF) return int4_offset_bf16x8(a);
+          return to_bf16x8<kFmtINT4>(a);
+        };
         if (hot[u][i]) {
-          k0 = to_bf16x8<kFmtINT8>(make_uint2(kraw[u][i].x, kraw[u][i].y));
-          k1 = to_bf16x8<kFmtINT8>(make_uint2(kraw[u][i].z, kraw[u][i].w));
-          v0 = to_bf16x8<kFmtINT8>(make_uint2(vraw[u][i].x, vraw[u][i].y));
-          v1 = to_bf16x8<kFmtINT8>(make_uint2(vraw[u][i].z, vraw[u][i].w));
+          k0 = ring8(kraw[u][i].x, kraw[u][i].y);
+          k1 = ring8(kraw[u][i].z, kraw[u][i].w);
+          v0 = ring8(vraw[u][i].x, vraw[u][i].y);
+          v1 = ring8(vraw[u][i].z, vraw[u][i].w);
         } else {
           const bool odd = lchunk & 1;
-          k0 = to_bf16x8<kFmtINT4>(odd ? kraw[u][i].z : kraw[u][i].x);
-          k1 = to_bf16x8<kFmtINT4>(odd ? kraw[u][i].w : kraw[u][i].y);
-          v0 = to_bf16x8<kFmtINT4>(odd ? vraw[u][i].z : vraw[u][i].x);
-          v1 = to_bf16x8<kFmtINT4>(odd ? vraw[u][i].w : vraw[u][i].y);
+          k0 = pool4(odd ? kraw[u][i].z : kraw[u][i].x);
+          k1 = pool4(odd ? kraw[u][i].w : kraw[u][i].y);
+          v0 = pool4(odd ? vraw[u][i].z : vraw[u][i].x);
+          v1 = pool4(odd ? vraw[u][i].w : vraw[u][i].y);
         }
         *reinterpret_cast<uint4 *>(kt + off) = k0;
         *reinterpret_cast<uint4 *>(kt + off + kPartB) = k1;
@@ -555,8 +631,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         for (int c = 0; c < P; ++c) {
           const Part kp = reinterpret_cast<const Part *>(&kraw[u][i])[c];
           const Part vp = reinterpret_cast<const Part *>(&vraw[u][i])[c];
-          *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = to_bf16x8<FMT>(kp);
-          *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = to_bf16x8<FMT>(vp);
+          if constexpr (I4OFF) {
+            *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = int4_offset_bf16x8(kp);
+            *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = int4_offset_bf16x8(vp);
+          } else {
+            *reinterpret_cast<uint4 *>(kt + off + c * kPartB) = to_bf16x8<FMT>(kp);
+            *reinterpret_cast<uint4 *>(vt + off + c * kPartB) = to_bf16x8<FMT>(vp);
+          }
         }
       }
     }
@@ -564,8 +645,20 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       if (lchunk < NG) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          ksc[(ldrow + i) * NG + lchunk] = static_cast<float>(ksr[u][i]);
-          vsc[(ldrow + i) * NG + lchunk] = static_cast<float>(vsr[u][i]);
+          float ks = static_cast<float>(ksr[u][i]), vs = static_cast<float>(vsr[u][i]);
+          if constexpr (I4OFF) {  // rows staged as 12 + code / 2: scales doubled
+            const float f = (TIER && hot[u][i]) ? 1.0f : 2.0f;
+            ks *= f;
+            vs *= f;
+          }
+          ksc[(ldrow + i) * NG + lchunk] = ks;
+          vsc[(ldrow + i) * NG + lchunk] = vs;
+        }
+      }
+      if constexpr (I4OFF && TIER) {
+        if (lchunk == 0) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) i4row[ldrow + i] = hot[u][i] ? 0.0f : 1.0f;
         }
       }
     }
@@ -586,6 +679,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       }
       s = s_even + s_odd;
     }
+    // tiered: which of this lane's entries are int4 rows
+    f32x4 i4f = f32x4{1.f, 1.f, 1.f, 1.f};
+    if constexpr (I4OFF && TIER) i4f = *reinterpret_cast<const f32x4 *>(i4row + 4 * qg);
     if constexpr (NG == 1) {
       const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ksc + 4 * qg);
       s *= k4;
@@ -601,7 +697,11 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
           part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(kk), qfrag(kk), part, 0, 0, 0);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] += ksc[(4 * qg + e) * NG + gi] * part[e];
+        for (int e = 0; e < 4; ++e) {
+          float t = part[e];
+          if constexpr (I4OFF) t = TIER ? fmaf(-i4f[e], qoff[gi], t) : t - qoff[gi];
+          s[e] += ksc[(4 * qg + e) * NG + gi] * t;
+        }
       }
     }
 
@@ -623,6 +723,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     if (__any(alpha != 1.0f)) {
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
+      if constexpr (I4OFF) {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) voff[gi] *= alpha;
+      }
     }
 
     // 4. O^T += V^T . P^T with P as hi + lo bf16
@@ -667,6 +771,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pv[e] = pr[e] * vsc[(4 * qg + e) * NG + gi];
+        if constexpr (I4OFF) {
+          if constexpr (TIER)
+            voff[gi] += (i4f[0] * pv[0] + i4f[1] * pv[1]) + (i4f[2] * pv[2] + i4f[3] * pv[3]);
+          else
+            voff[gi] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        }
         i16x4 hi, lo;
         split_p(pv, hi, lo);
 #pragma unroll
@@ -718,6 +828,39 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         stage(u);
         process(t);
       }
+    }
+  }
+
+  // ---- int4 rows: the accumulators hold sum_j P'_j (12 + code_j / 2) over
+  // them (P' with the doubled V scale) in the permuted channel order; take
+  // out the offset (12 x the weight sum of the channel's group over the
+  // int4 rows, over all four lane groups), then give every lane channels
+  // 16*mt + 4*qg + 0..3 again.  Lane groups 2i and
+  // 2i+1 hold one 8-channel chunk between them, the even channels in the
+  // first and the odd ones in the second; one row swap per pair of
+  // accumulator elements restores the channel order.
+  if constexpr (I4OFF) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      voff[gi] += __shfl_xor(voff[gi], 16);
+      voff[gi] += __shfl_xor(voff[gi], 32);
+      voff[gi] *= 12.0f;
+    }
+    auto swap_rows = [](float a, float b, float &x, float &y) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+      x = __uint_as_float(r[0]);
+      y = __uint_as_float(r[1]);
+    };
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      const float off = voff[16 * mt / G];
+      f32x4 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = acc[mt][e] - off;
+      float o0, o1, o2, o3;
+      swap_rows(a[0], a[2], o0, o1);
+      swap_rows(a[1], a[3], o2, o3);
+      acc[mt] = f32x4{o0, o1, o2, o3};
     }
   }
 
