@@ -74,6 +74,7 @@ constexpr int kHwRegXccId = (3 << 11) | (0 << 6) | 20;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kScaleLog2 = kLog2e / 16.0f;  // softmax scale 1/16 in log2 units
+constexpr float kLazyLog2 = 8.0f;              // weights below 2^8 against a stale max
 
 // ---- per-format gather geometry --------------------------------------------
 // Rows are gathered with fully coalesced 16-byte loads: one wave instruction
@@ -711,16 +712,17 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 #pragma unroll
     for (int e = 0; e < 4; ++e) s2[e] = (jbase + e < nkeys) ? s[e] * kScaleLog2 : -INFINITY;
     const float mx = max_over_groups(fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3])));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float pr[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(s2[e] - m_new);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-    // (once the running maxima settle most tiles leave every head's max
-    // unchanged: alpha == 1 exactly and the rescale is skipped)
-    if (__any(alpha != 1.0f)) {
+    // The running max moves only when some head's tile max exceeds it by
+    // more than kLazyLog2; then every head takes its new max and the state
+    // is rescaled once.  Otherwise the weights are taken against the older
+    // max and may reach 2^kLazyLog2, which the fp32 sums and the hi + lo
+    // split of P carry at the same relative precision.  After the first
+    // tiles almost no tile rescales.
+    if (__any(mx > m_run + kLazyLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) acc[mt] *= alpha;
       if constexpr (I4OFF) {
@@ -728,6 +730,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         for (int gi = 0; gi < NG; ++gi) voff[gi] *= alpha;
       }
     }
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(s2[e] - m_run);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     // 4. O^T += V^T . P^T with P as hi + lo bf16
     auto split_p = [&](const float (&pv)[4], i16x4 &hi, i16x4 &lo) {
