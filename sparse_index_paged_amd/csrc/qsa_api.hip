@@ -218,8 +218,8 @@ bool xcc_dispatch_check(int dev, hipStream_t stream) {
   bool ok = qsa::launch_xcc_probe(0, kN, stream) == hipSuccess &&
             qsa::launch_xcc_probe(2 * kN, 3, stream) == hipSuccess &&
             qsa::launch_xcc_probe(kN, kN, stream) == hipSuccess &&
-            hipStreamSynchronize(stream) == hipSuccess &&
-            qsa::read_xcc_probe(host, 2 * kN) == hipSuccess;
+            qsa::read_xcc_probe(host, 2 * kN, stream) == hipSuccess &&
+            hipStreamSynchronize(stream) == hipSuccess;
   ok = ok && xcc_round_robin(host, kN) && xcc_round_robin(host + kN, kN);
   (void)hipGetLastError();
   return ok;

@@ -37,7 +37,12 @@
 //     of V and its lo parts against the second.  Quantized codes are
 //     converted exactly to bf16; their fp32 scales are applied outside the
 //     MFMA (K scales on the QK partial of each channel group, V scales folded
-//     into P).
+//     into P).  8-wave workgroups stage int4 codes as the exact values
+//     12 + code / 2, one instruction per code, and take the offset out in
+//     fp32 (int4_offset_bf16x8).
+//   * The online softmax keeps a running max per head that moves only when
+//     a tile's max exceeds it by more than 2^8, so the accumulators are
+//     rescaled on a few tiles only.
 //   * Tiered pools (same page, tiered pool bullet): entry j reads ring row
 //     r = sel_j & (R-1) (int8, 64-channel scales) when owner[r] == sel_j,
 //     else its int4 row (32-channel scales).  The owner ids join the
@@ -1226,10 +1231,10 @@ hipError_t launch_xcc_probe(int base, int blocks, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t read_xcc_probe(int32_t *host, int n) {
+hipError_t read_xcc_probe(int32_t *host, int n, hipStream_t stream) {
   if (n < 0 || n > kXccProbeWords) return hipErrorInvalidValue;
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(xcc_probe_out), static_cast<size_t>(n) * sizeof(int32_t), 0,
-                             hipMemcpyDeviceToHost);
+  return hipMemcpyFromSymbolAsync(host, HIP_SYMBOL(xcc_probe_out), static_cast<size_t>(n) * sizeof(int32_t), 0,
+                                  hipMemcpyDeviceToHost, stream);
 }
 
 hipError_t launch_fill_u32(uint32_t *dst, int64_t n, uint32_t value, hipStream_t stream) {

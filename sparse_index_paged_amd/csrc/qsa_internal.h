@@ -158,10 +158,11 @@ hipError_t launch_decode(const Params &p, int fmt, int group, hipStream_t stream
 // Dispatch check probe (no allocation): `blocks` workgroups of 64 threads,
 // workgroup i writing the XCC_ID of its XCD to entry base + i of a
 // kXccProbeWords-entry device array, which read_xcc_probe copies to the host
-// (synchronously, from the current device).
+// in stream order on `stream` (the caller synchronises the stream before
+// reading `host`).
 constexpr int kXccProbeWords = 2 * 1024 + 3;
 hipError_t launch_xcc_probe(int base, int blocks, hipStream_t stream);
-hipError_t read_xcc_probe(int32_t *host, int n);
+hipError_t read_xcc_probe(int32_t *host, int n, hipStream_t stream);
 
 // Launch the quantize + scatter kernel (one wave per (token, kv head)).
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream);

@@ -25,7 +25,7 @@ hipError_t launch_index(const IndexParams &, hipStream_t) { ++g_launches; return
 hipError_t launch_fill_u32(uint32_t *, int64_t, uint32_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_audit(const uint32_t *, int, uint32_t *, hipStream_t) { return hipSuccess; }
 hipError_t launch_xcc_probe(int, int, hipStream_t) { return hipErrorNotSupported; }
-hipError_t read_xcc_probe(int32_t *, int) { return hipErrorNotSupported; }
+hipError_t read_xcc_probe(int32_t *, int, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace qsa
 
 static int g_fail = 0;
