@@ -136,6 +136,56 @@ def test_every_split_count(splits, fmt):
     assert all(v == 0 for v in qsa.debug_counters())
 
 
+def designed_logit_case(seed: int) -> synth.QsaCase:
+    """Rows whose logits follow set sequences.  Row r lists slots r*2055 ..
+    r*2055 + 2054 in order; slot j's K row holds a_r[j] in channel 0 and
+    zeros elsewhere, and head h's query holds 1 + h/24 in channel 0, so the
+    logit of entry j for head h is a_r[j] (1 + h/24) / 16.  In log2 units:
+    row 0 rises by 0.05-0.09 per entry (about 100-185 in all), row 1 is flat
+    and then jumps by 27-54 at entry 1000, row 2 falls from its first entry,
+    row 3 is noise with a spike of 6-11 every 97 entries.  V ~ N(0, 1)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    n = synth.CAPACITY
+    j = np.arange(n, dtype=np.float64)
+    seqs = [0.5 * j,
+            np.where(j < 1000, 0.0, 300.0 + (j % 7)),
+            500.0 - 0.25 * j,
+            rng.normal(0.0, 8.0, n) + np.where(j % 97 == 0, 60.0, 0.0)]
+    bs, hkv = len(seqs), 2
+    k = torch.zeros(bs * n, hkv, 256, dtype=torch.bfloat16)
+    for r, a in enumerate(seqs):
+        k[r * n:(r + 1) * n, :, 0] = torch.from_numpy(a).to(torch.bfloat16)[:, None]
+    v = synth.normal_bf16(rng, (bs * n, hkv, 256))
+    q = torch.zeros(bs, 12 * hkv, 256, dtype=torch.bfloat16)
+    q[:, :, 0] = torch.tensor([1.0 + h / 24 for h in range(12 * hkv)], dtype=torch.bfloat16)
+    sel, cu = synth.pack([np.arange(r * n, (r + 1) * n, dtype=np.int32) for r in range(bs)])
+    return synth.QsaCase(q=q, k_pool=k, v_pool=v, sel=sel, cu=cu, name="designed logits")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int4"])
+@pytest.mark.parametrize("waves,splits", [(4, 1), (8, 1), (0, 0)])
+def test_running_max_sequences(waves, splits, fmt):
+    """The running max of the online softmax moves only once a tile's max
+    exceeds it by more than 2^8; logits that rise slowly through that margin,
+    jump far past it, fall from the start or spike (designed_logit_case),
+    with one wave slice of 514 or 257 entries per wave or the default plan,
+    all match the oracle."""
+    qsa.set_option("waves_per_workgroup", waves)
+    qsa.set_option("splits", splits)
+    case = designed_logit_case(901)
+    label = f"designed logits {fmt} waves={waves} splits={splits}"
+    if fmt == "bf16":
+        run_and_compare(case, label)
+    else:
+        # channel 0 is the only non-zero one of every K row: its group's
+        # code is +-7 and the fp16 scale |a| / 7 carries the logit
+        kc, ks = quant.quantize(case.k_pool, "int4", 32, "f16")
+        vc, vs = quant.quantize(case.v_pool, "int4", 32, "f16")
+        run_and_compare(case, label, quant=("int4", 32, kc, ks, vc, vs), scale_dtype=torch.float16)
+    assert all(c == 0 for c in qsa.debug_counters())
+
+
 EDGE_LENGTHS = [0, 1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 1023, 2054, 2055, 0, 3, 511]
 
 
