@@ -414,7 +414,7 @@ def store_tiered_mode(args):
     rng = np.random.default_rng(2025)
     xk = synth.normal_bf16(rng, (slots, hkv, 256)).cuda()
     xv = synth.normal_bf16(rng, (slots, hkv, 256)).cuda()
-    pool = tiered_pools(xk, xv, r)
+    pool = qsa.TieredPool(tiered_pools(xk, xv, r))
     nb = max(1, slots // n)
     banks = [(xk[i * n:(i + 1) * n], xv[i * n:(i + 1) * n],
               torch.arange(i * n, (i + 1) * n, dtype=torch.int32, device="cuda")) for i in range(min(nb, 4))]
@@ -854,9 +854,10 @@ def main():
     qkw = {}
     tiered = None
     if fmt == "tiered":
-        tiered = tiered_pools(k, v, args.ring_rows)
+        tiered_arrays = tiered_pools(k, v, args.ring_rows)
         del k, v
-        owner_host = tiered["owner"].cpu().numpy()
+        owner_host = tiered_arrays["owner"].cpu().numpy()
+        tiered = qsa.TieredPool(tiered_arrays)  # descriptor built once for every call
     elif fmt != "bf16":
         kc, vc, ks, vs = quantized_pools(k, v, fmt, group, sdt)
         del k, v

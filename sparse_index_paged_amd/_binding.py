@@ -251,9 +251,27 @@ def tiered_pool(*, ring_k, ring_v, ring_k_scale, ring_v_scale, owner, claim, col
     return tp
 
 
-def decode_tiered(q, pool: dict, sel, cu_seqlens, *, out=None, lse=None, stream=None):
-    """Packed QSA decode over a tiered pool (dict with the qsa_tiered_pool
-    fields as torch tensors).  One kernel launch; returns (out, lse)."""
+class TieredPool:
+    """A tiered pool's qsa_tiered_pool descriptor, built once from its
+    tensors (held here, so they stay alive) and passed to decode_tiered /
+    kv_store_tiered in place of the dict, which saves rebuilding the ten
+    tensor descriptors on every call."""
+
+    def __init__(self, pool: dict):
+        self.tensors = {name: pool[name] for name in TIERED_FIELDS}
+        self.desc = tiered_pool(**self.tensors)
+
+
+def _tiered_desc(pool) -> QsaTieredPool:
+    if isinstance(pool, TieredPool):
+        return pool.desc
+    return tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
+
+
+def decode_tiered(q, pool, sel, cu_seqlens, *, out=None, lse=None, stream=None):
+    """Packed QSA decode over a tiered pool (a dict with the qsa_tiered_pool
+    fields as torch tensors, or a TieredPool).  One kernel launch; returns
+    (out, lse)."""
     import torch
     lib = load_library()
     bs, hq = q.shape[0], q.shape[1]
@@ -261,7 +279,7 @@ def decode_tiered(q, pool: dict, sel, cu_seqlens, *, out=None, lse=None, stream=
         out = torch.empty((bs, hq, 256), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((bs, hq), dtype=torch.float32, device=q.device)
-    tp = tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
+    tp = _tiered_desc(pool)
     qd, od, ld = describe(q), describe(out), describe(lse)
     sd, cd = describe(sel), describe(cu_seqlens)
     _check(lib.qsa_decode_tiered(ctypes.byref(qd), ctypes.byref(tp), ctypes.byref(sd),
@@ -270,12 +288,12 @@ def decode_tiered(q, pool: dict, sel, cu_seqlens, *, out=None, lse=None, stream=
     return out, lse
 
 
-def kv_store_tiered(k_new, v_new, loc, pool: dict, *, stream=None):
-    """Write k_new / v_new [n, Hkv, 256] bf16 into a tiered pool: int4 into
-    slot loc[t], int8 into ring row loc[t] & (R-1) with its owner stamp
-    (three kernel launches on `stream`)."""
+def kv_store_tiered(k_new, v_new, loc, pool, *, stream=None):
+    """Write k_new / v_new [n, Hkv, 256] bf16 into a tiered pool (dict or
+    TieredPool): int4 into slot loc[t], int8 into ring row loc[t] & (R-1)
+    with its owner stamp (three kernel launches on `stream`)."""
     lib = load_library()
-    tp = tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
+    tp = _tiered_desc(pool)
     kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
     _check(lib.qsa_kv_store_tiered(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld),
                                    ctypes.byref(tp), _stream_handle(stream)))

@@ -324,3 +324,35 @@ def test_tiered_graph_replay_matches_eager():
     ring, cold = write_history(x, y, [order[4096:written]], ring, cold)
     o_ref, l_ref = oracle_tiered(qbuf.cpu(), ring, cold, sel, cu)
     compare(out, lse, o_ref, l_ref, np.diff(cu), label="graph replay")
+
+
+def test_tiered_pool_descriptor_reused():
+    """A TieredPool (the pool's descriptor built once) gives the dict form's
+    results bit for bit: three rounds of a write then a decode, through each
+    form on twin pools, and the twin pools end equal."""
+    rng = np.random.default_rng(590)
+    slots, hkv, r, bs, n_new = 4096, 2, 256, 6, 48
+    x = synth.normal_bf16(rng, (slots, hkv, 256))
+    y = synth.normal_bf16(rng, (slots, hkv, 256))
+    order = rng.permutation(slots)
+    ring, cold = write_history(x, y, synth.write_batches(rng, order[:2048], 3),
+                               *layout.empty_tiered(r, slots, hkv))
+    dev_a, dev_b = to_dev(ring, cold), to_dev(ring, cold)
+    tp = qsa.TieredPool(dev_b)
+    for step in range(3):
+        loc = torch.from_numpy(rng.choice(slots, n_new, replace=False).astype(np.int32)).cuda()
+        k_new = synth.normal_bf16(rng, (n_new, hkv, 256)).cuda()
+        v_new = synth.normal_bf16(rng, (n_new, hkv, 256)).cuda()
+        qsa.kv_store_tiered(k_new, v_new, loc, dev_a)
+        qsa.kv_store_tiered(k_new, v_new, loc, tp)
+        lens = [2055, 0, 700, 1, 2055, 64]
+        sel, cu = synth.tiered_lists(rng, lens, slots, order[-r:], 0.3, dup_prob=0.05)
+        q = synth.normal_bf16(rng, (bs, 12 * hkv, 256)).cuda()
+        sel_d, cu_d = torch.from_numpy(sel).cuda(), torch.from_numpy(cu).cuda()
+        oa, la = qsa.decode_tiered(q, dev_a, sel_d, cu_d)
+        ob, lb = qsa.decode_tiered(q, tp, sel_d, cu_d)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(la, lb), f"round {step}: outputs differ"
+    for name in dev_a:
+        assert torch.equal(dev_a[name], dev_b[name]), f"pool array {name} differs"
+    assert all(v == 0 for v in qsa.debug_counters())
