@@ -624,8 +624,10 @@ def configs_mode(args):
         out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
         lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
 
+        pool = qsa.KvPool(k, v)
+
         def call(i):
-            qsa.decode(q, k, v, sd[i % 4], cu, out=out, lse=lse)
+            pool.decode(q, sd[i % 4], cu, out=out, lse=lse)
         jobs.append((name, workload, gathered_bytes(case.lengths, case.hkv), call,
                      {"splits": qsa.plan(case.bs, case.hkv)[0]}))
         keep.append((q, k, v, cu, sd, out, lse))
@@ -667,12 +669,12 @@ def configs_mode(args):
         lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
         keep.append((copies, q, cu, sd, out, lse))
         b_kv = gathered_bytes(case.lengths, case.hkv, row_bytes(fmt, group, 4))
+        pools = [qsa.KvPool(k_, v_, kv_format=fmt, k_scale=ks_, v_scale=vs_, group_size=group)
+                 for k_, v_, ks_, vs_ in copies]
+        keep.append(pools)
         for variant, ncopy in (("warm", 1), ("cold", 4)):
-            def call(i, fmt=fmt, group=group, ncopy=ncopy, copies=copies, q=q, cu=cu, sd=sd,
-                     out=out, lse=lse):
-                k_, v_, ks_, vs_ = copies[i % ncopy]
-                qsa.decode(q, k_, v_, sd[i % 4], cu, out=out, lse=lse, kv_format=fmt,
-                           k_scale=ks_, v_scale=vs_, group_size=group)
+            def call(i, ncopy=ncopy, pools=pools, q=q, cu=cu, sd=sd, out=out, lse=lse):
+                pools[i % ncopy].decode(q, sd[i % 4], cu, out=out, lse=lse)
             jobs.append((f"bs64_tp1_{fmt}_{variant}",
                          f"bs=64 TP1 (24Q/2KV) {fmt} pools [131072,2,{FORMATS[fmt][0]}] + f32 scales "
                          f"per {group} channels (written by qsa_kv_store), L~U[256,2055], "
@@ -882,12 +884,13 @@ def main():
     if args.cold and not copies:
         raise SystemExit("--cold needs --pool-copies >= 2 and a single-tier pool")
 
+    # every pool (and pool copy) is passed as a KvPool, whose descriptors are
+    # built once, as a serving loop over persistent pools would
+    fkw = {key: val for key, val in qkw.items() if key in ("kv_format", "group_size")}
+    copy_pools = [qsa.KvPool(kk, vv, k_scale=ks_, v_scale=vs_, **fkw) for kk, vv, ks_, vs_ in copies]
+
     def cold_step(i):
-        kk, vv, ks_, vs_ = copies[i % len(copies)]
-        kw = dict(qkw)
-        if ks_ is not None:
-            kw.update(k_scale=ks_, v_scale=vs_)
-        qsa.decode(q, kk, vv, sels[i % len(sels)], cu, out=out, lse=lse, **kw)
+        copy_pools[i % len(copy_pools)].decode(q, sels[i % len(sels)], cu, out=out, lse=lse)
 
     if tiered is not None:
         def step(i):
@@ -895,8 +898,10 @@ def main():
     elif args.cold:
         step = cold_step
     else:
+        kv_pool = qsa.KvPool(k, v, **qkw)
+
         def step(i):
-            qsa.decode(q, k, v, sels[i % len(sels)], cu, out=out, lse=lse, **qkw)
+            kv_pool.decode(q, sels[i % len(sels)], cu, out=out, lse=lse)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 from ._binding import (  # noqa: F401
     ABI_VERSION,
+    KvPool,
     QsaError,
     TieredPool,
     abi_version,
@@ -42,6 +43,6 @@ __all__ = [
     "decode", "decode_noalloc", "kv_store", "decode_tiered", "kv_store_tiered", "index", "index_reserve", "plan", "workspace_reserve", "workspace_attach",
     "workspace_detach", "workspace_reset", "workspace_release",
     "workspace_bytes", "set_option", "get_option", "debug_counters", "debug_counter_ptr", "debug_audit_counters",
-    "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError", "TieredPool",
+    "debug_device_error", "abi_version", "load_library", "lib_path", "QsaError", "TieredPool", "KvPool",
     "ABI_VERSION",
 ]

@@ -211,6 +211,52 @@ def decode_noalloc(q, k_pool, v_pool, sel, cu_seqlens, *, out, lse, kv_format: s
                   _noalloc=True)
 
 
+class KvPool:
+    """A single-tier K/V pool (and its scales) whose descriptors are built
+    once: decode / decode_noalloc / store through it skip rebuilding them on
+    every call.  The tensors are held here, so they stay alive; they must
+    not be reallocated or reshaped while the KvPool is in use."""
+
+    def __init__(self, k_pool, v_pool, *, kv_format: str = "bf16", k_scale=None, v_scale=None,
+                 group_size: int | None = None):
+        self.k_pool, self.v_pool, self.k_scale, self.v_scale = k_pool, v_pool, k_scale, v_scale
+        self.kv_format = kv_format
+        self._kd = describe(k_pool, kv_format)
+        self._vd = describe(v_pool, kv_format)
+        self._scales = _scales(kv_format, k_scale, v_scale, group_size)
+
+    def decode(self, q, sel, cu_seqlens, *, out=None, lse=None, stream=None, noalloc: bool = False):
+        """qsa_decode (qsa_decode_noalloc with noalloc=True, which needs out
+        and lse) over this pool; returns (out, lse)."""
+        import torch
+        lib = load_library()
+        if out is None or lse is None:
+            if noalloc:
+                raise ValueError("decode with noalloc=True needs out and lse")
+            bs, hq = q.shape[0], q.shape[1]
+            if out is None:
+                out = torch.empty((bs, hq, 256), dtype=torch.bfloat16, device=q.device)
+            if lse is None:
+                lse = torch.empty((bs, hq), dtype=torch.float32, device=q.device)
+        qd, od, ld = describe(q), describe(out), describe(lse)
+        sd, cd = describe(sel), describe(cu_seqlens)
+        entry = lib.qsa_decode_noalloc if noalloc else lib.qsa_decode
+        _check(entry(ctypes.byref(qd), ctypes.byref(self._kd), ctypes.byref(self._vd),
+                     ctypes.byref(self._scales) if self._scales is not None else None,
+                     ctypes.byref(sd), ctypes.byref(cd), ctypes.byref(od), ctypes.byref(ld),
+                     _stream_handle(stream)))
+        return out, lse
+
+    def store(self, k_new, v_new, loc, *, stream=None):
+        """qsa_kv_store of k_new / v_new [n, Hkv, 256] bf16 into this pool."""
+        lib = load_library()
+        kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
+        _check(lib.qsa_kv_store(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld), ctypes.byref(self._kd),
+                                ctypes.byref(self._vd),
+                                ctypes.byref(self._scales) if self._scales is not None else None,
+                                _stream_handle(stream)))
+
+
 def _scales(kv_format, k_scale, v_scale, group_size):
     if kv_format == "bf16":
         return None

@@ -378,3 +378,18 @@ def test_index_contract_rejections(kwargs, match):
     assert re.search(match, msg), msg
     assert msg.startswith("qsa_index")
 
+
+
+def test_kv_pool_checks_before_any_launch():
+    """KvPool needs scales for quantized pools, and its no-allocation decode
+    needs out and lse; both are refused on the host."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    k = torch.zeros(16, 2, 256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="need k_scale and v_scale"):
+        qsa.KvPool(k, k, kv_format="fp8")
+    pool = qsa.KvPool(torch.zeros(16, 2, 256, dtype=torch.bfloat16),
+                      torch.zeros(16, 2, 256, dtype=torch.bfloat16))
+    q = torch.zeros(1, 24, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="needs out and lse"):
+        pool.decode(q, torch.zeros(1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32), noalloc=True)

@@ -442,3 +442,45 @@ def test_pools_beyond_32bit_offsets():
     compare(out, lse, o_ref, l_ref, case.lengths, label="64-bit addressing")
     del kb, vb
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt,group", [("bf16", 256), ("fp8", 256), ("int4", 32)])
+def test_kv_pool_descriptor_reused(fmt, group):
+    """A KvPool (descriptors of the pools and scales built once) gives the
+    plain calls' results bit for bit: a store of new tokens into twin pools,
+    then qsa_decode and qsa_decode_noalloc through both forms."""
+    rng = np.random.default_rng(611)
+    case = synth.make_case(lengths=[2055, 0, 300, 1, 1500], slots=4096, hkv=2, seed=612, dup_prob=0.1)
+    new_k = synth.normal_bf16(rng, (64, 2, 256)).cuda()
+    new_v = synth.normal_bf16(rng, (64, 2, 256)).cuda()
+    loc = torch.from_numpy(rng.choice(4096, 64, replace=False).astype(np.int32)).cuda()
+    kw = {}
+    if fmt == "bf16":
+        pools = [(case.k_pool.cuda(), case.v_pool.cuda(), None, None) for _ in range(2)]
+    else:
+        kc, ks = quant.quantize(case.k_pool, fmt, group, "f16")
+        vc, vs = quant.quantize(case.v_pool, fmt, group, "f16")
+        mk = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        f16 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.float16).cuda()
+        pools = [(mk(kc), mk(vc), f16(ks), f16(vs)) for _ in range(2)]
+        kw = dict(kv_format=fmt, group_size=group)
+    ka, va, ksa, vsa = pools[0]
+    kb, vb, ksb, vsb = pools[1]
+    sc_a = dict(k_scale=ksa, v_scale=vsa) if fmt != "bf16" else {}
+    pool = qsa.KvPool(kb, vb, k_scale=ksb, v_scale=vsb, **kw)
+    qsa.kv_store(new_k, new_v, loc, ka, va, **kw, **sc_a)
+    pool.store(new_k, new_v, loc)
+    q = case.q.cuda()
+    sel, cu = torch.from_numpy(case.sel).cuda(), torch.from_numpy(case.cu).cuda()
+    oa, la = qsa.decode(q, ka, va, sel, cu, **kw, **sc_a)
+    ob, lb = pool.decode(q, sel, cu)
+    out = torch.empty_like(ob)
+    lse = torch.empty_like(lb)
+    oc, lc = pool.decode(q, sel, cu, out=out, lse=lse, noalloc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(la, lb)
+    assert torch.equal(oa, oc) and torch.equal(la, lc)
+    for a, b in zip(pools[0], pools[1]):
+        if a is not None:
+            assert torch.equal(a, b)
+    assert all(v == 0 for v in qsa.debug_counters())
