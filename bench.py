@@ -749,6 +749,56 @@ def configs_mode(args):
                               "by_bs": table}), flush=True)
 
 
+def splits_mode(args):
+    """Every forced split count (1-12 and 16) at each --sweep-bs batch size,
+    both layouts, over the bench workload's lists (4 rotating banks), eager:
+    one JSON line per (layout, bs) with the time of each count, the plan's
+    count and what the plan loses against the fastest measured count."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    import synth
+    torch.cuda.set_device(0)
+    case = synth.case_bs128_tp1_saturated()
+    slots = case.k_pool.shape[0]
+    sels = [case.sel]
+    for i in range(1, 4):
+        rng = np.random.default_rng(103_000 + i)
+        sels.append(synth.pack([synth.draw_indices(rng, n, slots) for n in case.lengths])[0])
+    q, k, v = case.q.cuda(), case.k_pool.cuda(), case.v_pool.cuda()
+    cu = torch.from_numpy(case.cu).cuda()
+    sd = [torch.from_numpy(s_).cuda() for s_ in sels]
+    qsa.workspace_reserve(128, 24, 2)
+    counts = list(range(1, 13)) + [16]
+    for hkv in (2, 1):
+        pool = qsa.KvPool(k, v) if hkv == 2 else qsa.KvPool(k[:, :1], v[:, :1])
+        for bs in (int(x) for x in args.sweep_bs.split(",") if x):
+            hq = 12 * hkv
+            qq, cub = q[:bs, :hq].contiguous(), cu[:bs + 1].contiguous()
+            out = torch.empty(bs, hq, 256, dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(bs, hq, dtype=torch.float32, device="cuda")
+            qsa.set_option("splits", 0)
+            plan = qsa.plan(bs, hkv)[0]
+            us = {}
+            try:
+                for n in counts:
+                    qsa.set_option("splits", n)
+
+                    def run():
+                        for i in range(100):
+                            pool.decode(qq, sd[i % 4], cub, out=out, lse=lse)
+                    run()
+                    us[n] = round(time_calls(run, 100, 3)[0], 3)
+            finally:
+                qsa.set_option("splits", 0)
+            best = min(us, key=us.get)
+            print(json.dumps({"mode": "splits", "layout": "TP1" if hkv == 2 else "TP2", "bs": bs,
+                              "plan": plan, "us_by_splits": us, "fastest": best,
+                              "plan_loss_us": round(us[plan] - us[best], 3) if plan in us else None,
+                              "workload": "bf16 pools [262144, Hkv, 256], 2055 uniform entries per row, "
+                                          "4 rotating index banks, 100 eager calls x 3 repeats"}),
+                  flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -763,7 +813,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
-    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather"],
+    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather", "splits"],
                     default="decode")
     ap.add_argument("--ctx", type=int, default=8192, help="index mode: context tokens per row")
     ap.add_argument("--compress", type=int, default=4, help="index mode: compression ratio")
@@ -792,6 +842,11 @@ def main():
     ap.add_argument("--no-probe", action="store_true", help="decode: skip the bare-gather ceiling")
     ap.add_argument("--only", default=None,
                     help="configs mode: comma-separated substrings of the configuration names to run")
+    ap.add_argument("--pool-layout", choices=["slot-major", "head-major"], default="slot-major",
+                    help="decode, bf16: pools stored [slots][Hkv][256] (the pages' layout) or each KV "
+                         "head's rows contiguous, passed as the same [slots, Hkv, 256] view by strides")
+    ap.add_argument("--sweep-bs", default="1,2,3,4,6,8,12,16,20,24,28,32,40,48,56,64,72,80,96,112,128",
+                    help="splits mode: batch sizes")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -815,6 +870,9 @@ def main():
         return
     if args.mode == "gather":
         gather_mode(args)
+        return
+    if args.mode == "splits":
+        splits_mode(args)
         return
 
     import numpy as np
@@ -851,6 +909,11 @@ def main():
     k = case.k_pool.cuda()
     v = case.v_pool.cuda()
     fmt = args.kv_format
+    if args.pool_layout == "head-major":
+        if fmt != "bf16":
+            raise SystemExit("--pool-layout head-major applies to bf16 pools")
+        k = k.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        v = v.permute(1, 0, 2).contiguous().permute(1, 0, 2)
     group = args.group or FORMATS.get(fmt, (0, 0, 32))[2]
     sdt = torch.float16 if args.scale_dtype == "f16" else torch.float32
     qkw = {}
@@ -1035,6 +1098,7 @@ def main():
             "index_banks": len(sels), "splits": splits, "workgroups": wgs,
             "pool_copies_timed": len(copies) if args.cold else 1,
             **({"ring_rows": args.ring_rows, "hot_share": hot_share} if tiered is not None else {}),
+            **({"pool_layout": "head-major"} if args.pool_layout == "head-major" else {}),
             "gathered_kv_bytes_per_call": b_kv, "counters_at_rest": counters_ok,
         },
         "roofline": {
