@@ -26,6 +26,7 @@ one line per measured workload configuration (see configs_mode).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -749,6 +750,84 @@ def configs_mode(args):
                               "by_bs": table}), flush=True)
 
 
+def phases_mode(args):
+    """Per-workgroup phase breakdown of decode calls, from the phase stamps
+    of the measurement build libqsa_stamps.so (include/qsa_stamps.h): the
+    bench workload's lists at --bs / --hkv over bf16 pools, --warmup calls
+    without stamps, then --steps stamped calls.  For each stamped call the
+    median and the slowest workgroup of every phase; the line reports the
+    medians of those over the calls, in us (stamps tick at 100 MHz)."""
+    import torch
+    import synth
+    from sparse_index_paged_amd import _binding as B
+    lib = B.load_stamps_library()
+    torch.cuda.set_device(0)
+    case = synth.case_bs128_tp1_saturated(bs=args.bs, hkv=args.hkv)
+    slots = case.k_pool.shape[0]
+    sels = [case.sel]
+    for i in range(1, 4):
+        rng = np.random.default_rng(103_000 + i)
+        sels.append(synth.pack([synth.draw_indices(rng, n, slots) for n in case.lengths])[0])
+    q, k, v = case.q.cuda(), case.k_pool.cuda(), case.v_pool.cuda()
+    cu = torch.from_numpy(case.cu).cuda()
+    sd = [torch.from_numpy(s_).cuda() for s_ in sels]
+    out = torch.empty(case.bs, case.hq, 256, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(case.bs, case.hq, dtype=torch.float32, device="cuda")
+    ns, nw = ctypes.c_int(), ctypes.c_int()
+    if lib.qsa_plan(case.bs, case.hkv, ctypes.byref(ns), ctypes.byref(nw)) != 0:
+        raise RuntimeError(lib.qsa_last_error().decode())
+    stamps = torch.zeros(nw.value * 8, dtype=torch.int64, device="cuda")
+    qd, kd, vd = B.describe(q), B.describe(k), B.describe(v)
+    cd, od, ld = B.describe(cu), B.describe(out), B.describe(lse)
+    sdd = [B.describe(x) for x in sd]
+    stream = B._stream_handle(None)
+
+    def call(i, stamped):
+        lib.qsa_debug_set_phase_stamps(stamps.data_ptr() if stamped else None,
+                                       stamps.numel() if stamped else 0)
+        if lib.qsa_decode(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), None,
+                          ctypes.byref(sdd[i % 4]), ctypes.byref(cd), ctypes.byref(od),
+                          ctypes.byref(ld), stream) != 0:
+            raise RuntimeError(lib.qsa_last_error().decode())
+
+    for i in range(args.warmup):
+        call(i, False)
+    torch.cuda.synchronize()
+    keys = ("start_skew", "cu_seqlens", "first_rows", "loop", "wave_merge", "arrival",
+            "last_split_merge", "end")
+    per_call = {k_: [] for k_ in keys}
+    spans = []
+    for i in range(args.steps):
+        stamps.zero_()
+        call(i, True)
+        torch.cuda.synchronize()
+        st = stamps.view(nw.value, 8).cpu().numpy().astype(np.float64) * 0.01  # us
+        act = st[:, 1] > 0
+        s_ = st[act]
+        t0 = st[st[:, 0] > 0, 0].min()
+        end = np.where(s_[:, 6] > 0, s_[:, 6], s_[:, 5])
+        split = s_[:, 5] > 0
+        last = split & (s_[:, 6] > 0)
+        tiled = s_[:, 2] > 0
+        ph = {"start_skew": s_[:, 0] - t0, "cu_seqlens": s_[:, 1] - s_[:, 0],
+              "first_rows": s_[tiled, 2] - s_[tiled, 1], "loop": s_[tiled, 3] - s_[tiled, 2],
+              "wave_merge": s_[:, 4] - s_[:, 3], "arrival": (s_[split, 5] - s_[split, 4]),
+              "last_split_merge": (s_[last, 6] - s_[last, 5]), "end": end - t0}
+        for k_ in keys:
+            x = ph[k_]
+            per_call[k_].append((float(np.median(x)), float(np.max(x))) if x.size else (0.0, 0.0))
+        spans.append(float(end.max() - t0))
+    rec = {"mode": "phases", "bs": case.bs, "hkv": case.hkv, "splits": ns.value, "workgroups": nw.value,
+           "stamped_calls": args.steps,
+           "span_us": round(float(np.median(spans)), 2),
+           "phases_us": {k_: {"median_wg": round(float(np.median([a for a, _ in v_])), 2),
+                              "slowest_wg": round(float(np.median([b_ for _, b_ in v_])), 2)}
+                         for k_, v_ in per_call.items()},
+           "workload": f"bench lists at bs={case.bs} hkv={case.hkv} (2055 entries per row), bf16 pools "
+                       f"[262144,{case.hkv},256], libqsa_stamps.so"}
+    print(json.dumps(rec), flush=True)
+
+
 def splits_mode(args):
     """Every forced split count (1-12 and 16) at each --sweep-bs batch size,
     both layouts, over the bench workload's lists (4 rotating banks), eager:
@@ -813,7 +892,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
-    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather", "splits"],
+    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather", "splits",
+                                       "phases"],
                     default="decode")
     ap.add_argument("--ctx", type=int, default=8192, help="index mode: context tokens per row")
     ap.add_argument("--compress", type=int, default=4, help="index mode: compression ratio")
@@ -873,6 +953,9 @@ def main():
         return
     if args.mode == "splits":
         splits_mode(args)
+        return
+    if args.mode == "phases":
+        phases_mode(args)
         return
 
     import numpy as np

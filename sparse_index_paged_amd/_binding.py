@@ -67,7 +67,31 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is missing: build it with "
                           "`python -m sparse_index_paged_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+_stamps_lib = None
+
+
+def load_stamps_library():
+    """The measurement build libqsa_stamps.so (include/qsa_stamps.h): the
+    same API with per-workgroup phase stamps in the decode kernel, loaded
+    beside libqsa.so with its own library state."""
+    global _stamps_lib
+    if _stamps_lib is None:
+        path = os.path.join(os.path.dirname(_LIB_PATH), "libqsa_stamps.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m sparse_index_paged_amd.build`")
+        lib = _configure(ctypes.CDLL(path))
+        lib.qsa_debug_set_phase_stamps.restype = ctypes.c_int
+        lib.qsa_debug_set_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        _stamps_lib = lib
+    return _stamps_lib
+
+
+def _configure(lib):
+    """Argument and result types of every qsa.h call."""
     P = ctypes.POINTER
     T = P(QsaTensor)
     lib.qsa_decode.restype = ctypes.c_int
@@ -114,7 +138,6 @@ def load_library():
     lib.qsa_debug_device_error.argtypes = [P(ctypes.c_uint32), ctypes.c_void_p]
     lib.qsa_abi_version.restype = ctypes.c_int
     lib.qsa_abi_version.argtypes = []
-    _lib = lib
     return lib
 
 

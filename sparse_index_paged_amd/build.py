@@ -81,10 +81,28 @@ def build(verbose: bool = False, sanitize: bool = False) -> str:
         sys.stderr.write("\n".join(noise) + "\n")
     os.replace(tmp, LIB)
     build_probe(verbose)
+    build_stamps(verbose)
     return LIB
 
 
 PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
+STAMPS_LIB = os.path.join(PKG, "libqsa_stamps.so")
+
+
+def build_stamps(verbose: bool = False) -> str:
+    """Build the measurement build libqsa_stamps.so: the same sources with the
+    decode kernel's per-workgroup phase stamps (include/qsa_stamps.h)."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = STAMPS_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-DQSA_PHASE_STAMPS", "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libqsa_stamps.so")
+    os.replace(tmp, STAMPS_LIB)
+    return STAMPS_LIB
 
 
 def build_probe(verbose: bool = False) -> str:

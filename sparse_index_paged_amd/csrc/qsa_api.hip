@@ -15,6 +15,9 @@
 #include <mutex>
 
 #include "../../include/qsa.h"
+#ifdef QSA_PHASE_STAMPS
+#include "../../include/qsa_stamps.h"
+#endif
 #include "qsa_internal.h"
 
 namespace {
@@ -239,6 +242,20 @@ int xcc_lanes_for(hipStream_t stream) {
   }
   return g_xcc_state[dev] == 2 ? 1 : 0;
 }
+
+// ---- phase stamps (the measurement build libqsa_stamps.so only) ----------
+#ifdef QSA_PHASE_STAMPS
+std::atomic<uint64_t *> g_stamps{nullptr};
+std::atomic<int64_t> g_stamp_words{0};
+// A launch writes its stamps when the buffer holds kStampSlots words per
+// workgroup of its grid.
+void stamp_launch(qsa::Params *p, int fmt) {
+  const int64_t need = qsa::decode_workgroups(fmt, p->bs, p->hkv, p->nsplit) * qsa::kStampSlots;
+  p->stamps = g_stamp_words.load() >= need ? g_stamps.load() : nullptr;
+}
+#else
+inline void stamp_launch(qsa::Params *, int) {}
+#endif
 
 // Index of the private workspace bound to `stream` on `dev`, or -1 (the
 // caller holds g_ws_mutex).
@@ -886,6 +903,7 @@ qsa_status qsa_decode(const qsa_tensor *q, const qsa_tensor *k_pool, const qsa_t
   if (st != QSA_OK) return st;
   if ((st = attach_workspace(fn, stream, &p)) != QSA_OK) return st;
   p.xcc_lanes = xcc_lanes_for(stream);
+  stamp_launch(&p, pd.fmt);
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -914,6 +932,7 @@ qsa_status qsa_decode_noalloc(const qsa_tensor *q, const qsa_tensor *k_pool,
   p.ctr = reinterpret_cast<uint32_t *>(base + kScratchPartFloats * sizeof(float));
   p.err = p.ctr + kCtrWords;
   p.xcc_lanes = xcc_lanes_for(stream);
+  stamp_launch(&p, pd.fmt);
   const hipError_t e = qsa::launch_decode(p, pd.fmt, pd.group, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -962,6 +981,7 @@ qsa_status qsa_decode_tiered(const qsa_tensor *q, const qsa_tiered_pool *pool,
   p.a32 = tiered_fits_32(pool, td, &p) ? 1 : 0;
   p.waves = waves_for(qsa::kFmtTIERED, qsa::decode_workgroups(qsa::kFmtTIERED, p.bs, p.hkv, p.nsplit));
   p.xcc_lanes = xcc_lanes_for(stream);
+  stamp_launch(&p, qsa::kFmtTIERED);
   const hipError_t e = qsa::launch_decode(p, qsa::kFmtTIERED, 32, stream);
   if (e != hipSuccess) return fail(QSA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -1274,5 +1294,13 @@ qsa_status qsa_debug_device_error(uint32_t *host_word, hipStream_t stream) {
     return fail(QSA_ERR_HIP, "qsa_debug_device_error: copy failed");
   return ok();
 }
+
+#ifdef QSA_PHASE_STAMPS
+int qsa_debug_set_phase_stamps(void *buf, int64_t words) {
+  g_stamps = static_cast<uint64_t *>(buf);
+  g_stamp_words = buf != nullptr && words > 0 ? words : 0;
+  return 0;
+}
+#endif
 
 }  // extern "C"

@@ -71,6 +71,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family
+// chips, and the cache-policy operand that sets sc1 (device-scope coherent)
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCachePolicySc1 = 16;
 
 // s_getreg_b32 operand for the XCC_ID hardware register (hwreg 20, bits
 // 0..3): the XCD the wave runs on
@@ -242,6 +248,18 @@ template <int W, bool FLAGS> struct Lds {
   static constexpr int kBytes = (kLoop + kQ) > kFold ? (kLoop + kQ) : kFold;
 };
 
+// Phase stamp k of this workgroup (the measurement build only; see
+// kStampSlots).  s_memrealtime reads the constant 100 MHz clock; the stamp
+// is written with a vector store.
+__device__ __forceinline__ void phase_stamp(const Params &p, int tid, int k) {
+#ifdef QSA_PHASE_STAMPS
+  if (tid == 0 && p.stamps != nullptr)
+    p.stamps[static_cast<int64_t>(blockIdx.x) * kStampSlots + k] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)p, (void)tid, (void)k;
+#endif
+}
+
 __device__ void write_nan_rows(const Params &p, int b, int g, int tid, int nthreads) {
   const __bf16 nan = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0x7FC0u));
   for (int i = tid; i < kGqa * kHeadDim; i += nthreads)
@@ -315,6 +333,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     g = pair8 - b * hkv_lead;
   }
   const int pair = b * hkv_lead + g;
+  phase_stamp(p, tid, 0);
 
   // ---- live row length from device cu_seqlens
   const int c0 = cu_lead[b];
@@ -330,6 +349,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   int n_active = (L + msk_lead - 1) / msk_lead;
   n_active = n_active < 1 ? 1 : (n_active > nsplit_lead ? nsplit_lead : n_active);
   if (split >= n_active) return;
+  phase_stamp(p, tid, 1);
 
   // ---- this wave's contiguous slice of the list
   const int nw = n_active * W;
@@ -814,6 +834,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     for (int u = 0; u < D; ++u) {
       const int t = t0 + u;
       stage(u);
+      if (t == 0) phase_stamp(p, tid, 2);
       if constexpr (TIER) {
         // owner ids of tile t+2D from its slot ids fetched D steps ago; the
         // same slot ids are fetched again (cache hits) for the row issue D
@@ -837,10 +858,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       const int t = t0 + u;
       if (t < ntile) {
         stage(u);
+        if (t == 0) phase_stamp(p, tid, 2);
         process(t);
       }
     }
   }
+
+  phase_stamp(p, tid, 3);
 
   // ---- int4 rows: the accumulators hold sum_j P'_j (12 + code_j / 2) over
   // them (P' with the doubled V scale) in the permuted channel order; take
@@ -977,6 +1001,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     }
   }
 
+  phase_stamp(p, tid, 4);
   if (n_active == 1) {
     if (wv < 4) {
       const float invj = recip(sw);
@@ -984,31 +1009,36 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       for (int k = 0; k < 3; ++k) store_out(4 * k + wv, o[k], bcast(invj, 4 * k + wv));
       if (wv == 0 && lane < kGqa) lrow[lane * p.l_sh] = lse_of(Mw, sw);
     }
+    phase_stamp(p, tid, 6);
     return;
   }
 
   // ---- split partial, then the last arriver merges all splits in order.
   // A partial is m[16], l[16] (log2 domain) and the unnormalised
-  // accumulator laid out [head][4][64 lanes], so every store and load of a
-  // wave covers 256 contiguous bytes.  Partials are written and read with
-  // device-scope (sc1) accesses, which are coherent across XCDs without
-  // writing back or invalidating whole L2 caches; each wave waits for its
-  // stores to be acknowledged before the workgroup barrier, and one
-  // device-scope atomic per workgroup counts the arrivals.  The split that
-  // sees count n_active - 1 is the last one.
+  // accumulator laid out [head][64 lanes][4], so a lane moves its 4 values
+  // of a head as one 16-byte access and a wave covers 1 KB contiguous.
+  // Partials are written and read with device-scope (sc1) accesses -- m and
+  // l as relaxed agent-scope atomics, the accumulators as sc1 buffer loads
+  // and stores -- which are coherent across XCDs without writing back or
+  // invalidating whole L2 caches; each wave waits for its stores to be
+  // acknowledged before the workgroup barrier, and one device-scope atomic
+  // per workgroup counts the arrivals.  The split that sees count
+  // n_active - 1 is the last one.
   auto st = [](float *ptr, float x) { __hip_atomic_store(ptr, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   const float *pbase = p.part + static_cast<int64_t>(pair) * nsplit_lead * kPartFloats;
+  // byte offset of lane `lane`'s 4 accumulator values of head h in a partial
+  auto acc_off = [&](int h) { return (32 + (h * 64 + lane) * 4) * static_cast<int>(sizeof(float)); };
   if (wv < 4) {
     float *part = p.part + (static_cast<int64_t>(pair) * nsplit_lead + split) * kPartFloats;
     if (wv == 0 && lane < 16) {
       st(part + lane, Mw);
       st(part + 16 + lane, sw);
     }
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(part, 0, kPartFloats * sizeof(float), kBufferWord3);
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st(part + 32 + ((4 * k + wv) * 4 + i) * 64 + lane, o[k][i]);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[k]), rs, acc_off(4 * k + wv), 0, kCachePolicySc1);
   }
   // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained); as a builtin, the
   // compiler's own wait tracking knows that no load is outstanding after it
@@ -1019,15 +1049,16 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     s_last = (prev == static_cast<uint32_t>(n_active - 1)) ? 1 : 0;
   }
   __syncthreads();
+  phase_stamp(p, tid, 5);
   if (!s_last || wv >= 4) return;
 
   // (a) m and l of every split: lane j = 16 s' + h of round r holds split
   // 4r + s' (at most 64 splits = 16 rounds; rounds past the last split
   // re-read the last split and are masked), then the accumulators of the
-  // first 8 splits.  Round 0 always exists and is straight-line code; the
+  // first kBatch splits.  Round 0 always exists and is straight-line code; the
   // other rounds sit behind one branch, so the common case of at most 4
   // splits issues all its loads back to back.
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 12;  // splits whose accumulators are loaded in one round trip
   const int nround = (n_active + 3) >> 2;
   float mr[16], lr[16];
   {
@@ -1045,17 +1076,21 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       }
     }
   }
-  const float *pacc = pbase + 32 + wv * 4 * 64 + lane;
-  auto acc_ld = [&](int s, int k, int i) { return ld(pacc + s * kPartFloats + (16 * k + i) * 64); };
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(pbase), 0,
+                                                    nsplit_lead * kPartFloats * static_cast<int>(sizeof(float)),
+                                                    kBufferWord3);
+  auto acc_ld = [&](int s, int k) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rp, s * kPartFloats * static_cast<int>(sizeof(float)) + acc_off(4 * k + wv),
+                                         0, kCachePolicySc1));
+  };
   // (a split's registers are only written and read when the split exists)
   f32x4 a[kBatch][3];
 #pragma unroll
   for (int u = 0; u < kBatch; ++u)
     if (u < n_active) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[u][k][i] = acc_ld(u, k, i);
+      for (int k = 0; k < 3; ++k) a[u][k] = acc_ld(u, k);
     }
 
   // (b) per head: merged max, each split's weight (into this wave's LDS
@@ -1116,9 +1151,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
     for (int u = 0; u < kBatch; ++u)
       if (s0 + u < n_active) {
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a[u][k][i] = acc_ld(s0 + u, k, i);
+        for (int k = 0; k < 3; ++k) a[u][k] = acc_ld(s0 + u, k);
       }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
@@ -1132,6 +1165,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   for (int k = 0; k < 3; ++k) store_out(4 * k + wv, acc_o[k], bcast(invj, 4 * k + wv));
   if (wv == 0 && lane < kGqa) lrow[lane * p.l_sh] = lse_of(M, ssum);
   if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  phase_stamp(p, tid, 6);
 }
 
 // XCC_ID of every workgroup of the dispatch check's probe launches

@@ -93,7 +93,18 @@ struct Params {
   float *part;              // [npairs][nsplit][kPartFloats]
   uint32_t *ctr;            // [npairs], zero at rest
   uint32_t *err;            // sticky error word
+#ifdef QSA_PHASE_STAMPS
+  uint64_t *stamps;         // [grid][kStampSlots] wall-clock stamps, or null
+#endif
 };
+
+// Phase stamps (measurement build libqsa_stamps.so only): per workgroup,
+// thread 0 writes the 100 MHz wall clock at kernel entry, once cu_seqlens
+// has arrived, once its first tile's rows have arrived, at the end of its
+// loop, after the workgroup's wave merge, after the split arrival count, and
+// when it has written the output (slots 0..6; slots it does not reach keep
+// the value the host put there).
+constexpr int kStampSlots = 8;
 
 // One quantize + scatter call: rows t of k_new / v_new go to pool slot loc[t].
 struct StoreParams {
