@@ -71,12 +71,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Buffer resource word 3 for raw (untyped) buffer accesses on gfx9-family
-// chips, and the cache-policy operand that sets sc1 (device-scope coherent)
-constexpr int kBufferWord3 = 0x00020000;
-constexpr int kCachePolicySc1 = 16;
 
 // s_getreg_b32 operand for the XCC_ID hardware register (hwreg 20, bits
 // 0..3): the XCD the wave runs on
@@ -1015,30 +1010,26 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 
   // ---- split partial, then the last arriver merges all splits in order.
   // A partial is m[16], l[16] (log2 domain) and the unnormalised
-  // accumulator laid out [head][64 lanes][4], so a lane moves its 4 values
-  // of a head as one 16-byte access and a wave covers 1 KB contiguous.
-  // Partials are written and read with device-scope (sc1) accesses -- m and
-  // l as relaxed agent-scope atomics, the accumulators as sc1 buffer loads
-  // and stores -- which are coherent across XCDs without writing back or
-  // invalidating whole L2 caches; each wave waits for its stores to be
-  // acknowledged before the workgroup barrier, and one device-scope atomic
-  // per workgroup counts the arrivals.  The split that sees count
-  // n_active - 1 is the last one.
+  // accumulator laid out [head][4][64 lanes], so every store and load of a
+  // wave covers 256 contiguous bytes.  Partials are written and read with
+  // device-scope (sc1) accesses, which are coherent across XCDs without
+  // writing back or invalidating whole L2 caches; each wave waits for its
+  // stores to be acknowledged before the workgroup barrier, and one
+  // device-scope atomic per workgroup counts the arrivals.  The split that
+  // sees count n_active - 1 is the last one.
   auto st = [](float *ptr, float x) { __hip_atomic_store(ptr, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   auto ld = [](const float *ptr) { return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   const float *pbase = p.part + static_cast<int64_t>(pair) * nsplit_lead * kPartFloats;
-  // byte offset of lane `lane`'s 4 accumulator values of head h in a partial
-  auto acc_off = [&](int h) { return (32 + (h * 64 + lane) * 4) * static_cast<int>(sizeof(float)); };
   if (wv < 4) {
     float *part = p.part + (static_cast<int64_t>(pair) * nsplit_lead + split) * kPartFloats;
     if (wv == 0 && lane < 16) {
       st(part + lane, Mw);
       st(part + 16 + lane, sw);
     }
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(part, 0, kPartFloats * sizeof(float), kBufferWord3);
 #pragma unroll
     for (int k = 0; k < 3; ++k)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o[k]), rs, acc_off(4 * k + wv), 0, kCachePolicySc1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st(part + 32 + ((4 * k + wv) * 4 + i) * 64 + lane, o[k][i]);
   }
   // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained); as a builtin, the
   // compiler's own wait tracking knows that no load is outstanding after it
@@ -1076,13 +1067,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
       }
     }
   }
-  const auto rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(pbase), 0,
-                                                    nsplit_lead * kPartFloats * static_cast<int>(sizeof(float)),
-                                                    kBufferWord3);
+  const float *pacc = pbase + 32 + wv * 4 * 64 + lane;
   auto acc_ld = [&](int s, int k) {
-    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rp, s * kPartFloats * static_cast<int>(sizeof(float)) + acc_off(4 * k + wv),
-                                         0, kCachePolicySc1));
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = ld(pacc + s * kPartFloats + (16 * k + i) * 64);
+    return r;
   };
   // (a split's registers are only written and read when the split exists)
   f32x4 a[kBatch][3];
