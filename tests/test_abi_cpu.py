@@ -393,3 +393,15 @@ def test_kv_pool_checks_before_any_launch():
     q = torch.zeros(1, 24, 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="needs out and lse"):
         pool.decode(q, torch.zeros(1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32), noalloc=True)
+
+
+def test_stamps_build_exports_the_api_and_its_call():
+    """libqsa_stamps.so (include/qsa_stamps.h) exports everything qsa.h
+    declares plus qsa_debug_set_phase_stamps, which libqsa.so does not."""
+    path = os.path.join(os.path.dirname(qsa.lib_path()), "libqsa_stamps.so")
+    nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r"\bT (qsa_\w+)", nm))
+    assert exported == set(_declared_functions()) | {"qsa_debug_set_phase_stamps"}
+    lib = B.load_stamps_library()
+    assert lib.qsa_debug_set_phase_stamps(None, 0) == 0
