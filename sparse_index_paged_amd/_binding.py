@@ -259,6 +259,17 @@ class KvPool:
         self._kd = describe(k_pool, kv_format)
         self._vd = describe(v_pool, kv_format)
         self._scales = _scales(kv_format, k_scale, v_scale, group_size)
+        self._held = [(k_pool, self._kd.data), (v_pool, self._vd.data)]
+        if self._scales is not None:
+            self._held += [(k_scale, self._scales.k_scale.data), (v_scale, self._scales.v_scale.data)]
+
+    def check(self):
+        """Raise if a held tensor no longer has the storage its descriptor
+        names (reallocated by resize_ or set_): a stale descriptor would send
+        the kernels to freed memory."""
+        for t, ptr in self._held:
+            if (t.data_ptr() or 16) != ptr:
+                raise ValueError("KvPool: a pool tensor was reallocated; build a new KvPool")
 
     def decode(self, q, sel, cu_seqlens, *, out=None, lse=None, stream=None, noalloc: bool = False):
         """qsa_decode (qsa_decode_noalloc with noalloc=True, which needs out
@@ -273,6 +284,7 @@ class KvPool:
                 out = torch.empty((bs, hq, 256), dtype=torch.bfloat16, device=q.device)
             if lse is None:
                 lse = torch.empty((bs, hq), dtype=torch.float32, device=q.device)
+        self.check()
         qd, od, ld = describe(q), describe(out), describe(lse)
         sd, cd = describe(sel), describe(cu_seqlens)
         entry = lib.qsa_decode_noalloc if noalloc else lib.qsa_decode
@@ -285,6 +297,7 @@ class KvPool:
     def store(self, k_new, v_new, loc, *, stream=None):
         """qsa_kv_store of k_new / v_new [n, Hkv, 256] bf16 into this pool."""
         lib = load_library()
+        self.check()
         kd, vd, ld = describe(k_new), describe(v_new), describe(loc)
         _check(lib.qsa_kv_store(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(ld), ctypes.byref(self._kd),
                                 ctypes.byref(self._vd),
@@ -341,10 +354,20 @@ class TieredPool:
     def __init__(self, pool: dict):
         self.tensors = {name: pool[name] for name in TIERED_FIELDS}
         self.desc = tiered_pool(**self.tensors)
+        self._held = [(t, getattr(self.desc, name).data) for name, t in self.tensors.items()]
+
+    def check(self):
+        """Raise if a held tensor no longer has the storage its descriptor
+        names (reallocated by resize_ or set_): a stale descriptor would send
+        the kernels to freed memory."""
+        for t, ptr in self._held:
+            if (t.data_ptr() or 16) != ptr:
+                raise ValueError("TieredPool: a pool tensor was reallocated; build a new TieredPool")
 
 
 def _tiered_desc(pool) -> QsaTieredPool:
     if isinstance(pool, TieredPool):
+        pool.check()
         return pool.desc
     return tiered_pool(**{name: pool[name] for name in TIERED_FIELDS})
 

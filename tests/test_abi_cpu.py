@@ -405,3 +405,38 @@ def test_stamps_build_exports_the_api_and_its_call():
     assert exported == set(_declared_functions()) | {"qsa_debug_set_phase_stamps"}
     lib = B.load_stamps_library()
     assert lib.qsa_debug_set_phase_stamps(None, 0) == 0
+
+
+def test_pool_objects_refuse_reallocated_tensors():
+    """KvPool / TieredPool keep descriptors built once; a held tensor whose
+    storage was replaced (resize_) is refused on the host before any call."""
+    import torch
+    import sparse_index_paged_amd as qsa
+    k = torch.zeros(16, 2, 256, dtype=torch.bfloat16)
+    v = torch.zeros(16, 2, 256, dtype=torch.bfloat16)
+    pool = qsa.KvPool(k, v)
+    pool.check()
+    k.resize_(4096, 2, 256)
+    with pytest.raises(ValueError, match="reallocated"):
+        pool.check()
+    ks = torch.ones(16, 2, 1)
+    qp = qsa.KvPool(torch.zeros(16, 2, 256, dtype=torch.uint8), torch.zeros(16, 2, 256, dtype=torch.uint8),
+                    kv_format="fp8", k_scale=ks, v_scale=ks.clone())
+    qp.check()
+    ks.resize_(8192, 2, 1)
+    with pytest.raises(ValueError, match="reallocated"):
+        qp.check()
+    r, slots = 64, 256
+    arrays = dict(ring_k=torch.zeros(r, 2, 256, dtype=torch.int8), ring_v=torch.zeros(r, 2, 256, dtype=torch.int8),
+                  ring_k_scale=torch.zeros(r, 2, 4, dtype=torch.float16),
+                  ring_v_scale=torch.zeros(r, 2, 4, dtype=torch.float16),
+                  owner=torch.zeros(r, dtype=torch.int32), claim=torch.zeros(r, dtype=torch.int32),
+                  cold_k=torch.zeros(slots, 2, 128, dtype=torch.uint8),
+                  cold_v=torch.zeros(slots, 2, 128, dtype=torch.uint8),
+                  cold_k_scale=torch.zeros(slots, 2, 8, dtype=torch.float16),
+                  cold_v_scale=torch.zeros(slots, 2, 8, dtype=torch.float16))
+    tp = qsa.TieredPool(arrays)
+    tp.check()
+    arrays["owner"].resize_(1 << 16)
+    with pytest.raises(ValueError, match="reallocated"):
+        tp.check()
