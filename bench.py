@@ -229,6 +229,8 @@ def probe_lib():
         lib.qsa_probe_gather.restype = ctypes.c_int
         lib.qsa_probe_gather.argtypes = [P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, I64, I64, I64,
                                          P, I64, P]
+        lib.qsa_probe_line_reads.restype = ctypes.c_int
+        lib.qsa_probe_line_reads.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_uint32, P, I64, P]
         _PROBE = lib
     return _PROBE
 
@@ -320,6 +322,48 @@ def gather_mode(args):
                       flush=True)
         del pools
         torch.cuda.empty_cache()
+
+
+LINE_POLICIES = ("plain", "non-temporal", "atomic, agent scope", "atomic, system scope")
+
+
+def line_reads_mode(args):
+    """Random 4-byte reads of 128-byte lines that no other read touches (the
+    scale reads of a quantized pool) under each load form of
+    qsa_probe_line_reads, over a 2 GiB buffer (eight times the Infinity
+    Cache): us per launch and reads per second; the bytes the L2 fetches
+    per read come from the TCC read-request counters of a profiled run.
+    One JSON line per load form."""
+    import ctypes
+    import torch
+    if probe_lib() is None:
+        raise SystemExit("libqsa_probe.so is not built")
+    torch.cuda.set_device(0)
+    lib = probe_lib()
+    buf_bytes = 2 << 30
+    buf = torch.zeros(buf_bytes // 4, dtype=torch.float32, device="cuda")
+    n_reads = 4096 * 1024
+    sink = torch.zeros(n_reads // 1024, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for pol, name in enumerate(LINE_POLICIES):
+        def call(i, pol=pol):
+            rc = lib.qsa_probe_line_reads(buf.data_ptr(), buf_bytes, n_reads, pol, 7 + i,
+                                          sink.data_ptr(), sink.numel(), stream)
+            if rc != 0:
+                raise RuntimeError(f"qsa_probe_line_reads failed ({rc})")
+        for i in range(2):
+            call(1000 + i)
+        torch.cuda.synchronize()
+
+        def run():
+            for i in range(args.steps):
+                call(i)
+        us = time_calls(run, args.steps, args.repeats)[0]
+        print(json.dumps({"mode": "line-reads", "load": name, "policy": pol, "reads": n_reads,
+                          "us_per_launch": round(us, 3),
+                          "Greads_per_s": round(n_reads / (us * 1e-6) / 1e9, 2),
+                          "line_GBps_if_128B": round(n_reads * 128 / (us * 1e-6) / 1e9, 1),
+                          "buffer_bytes": buf_bytes}), flush=True)
 
 
 def copy_mode(args):
@@ -892,7 +936,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy reference rate")
-    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather", "splits",
+    ap.add_argument("--mode", choices=["decode", "copy", "store", "index", "configs", "gather", "line-reads", "splits",
                                        "phases"],
                     default="decode")
     ap.add_argument("--ctx", type=int, default=8192, help="index mode: context tokens per row")
@@ -948,6 +992,8 @@ def main():
     if args.mode == "configs":
         configs_mode(args)
         return
+    if args.mode == "line-reads":
+        return line_reads_mode(args)
     if args.mode == "gather":
         gather_mode(args)
         return

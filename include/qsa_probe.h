@@ -16,6 +16,20 @@
  * workgroups).  Slot ids outside [0, slots) read slot 0.  One kernel launch
  * on `stream`; returns 0, 1 for bad arguments (nothing launched), 2 when
  * the launch failed.
+ *
+ * qsa_probe_line_reads makes n_reads reads of 4 bytes, each of the first
+ * word of a pseudo-random 128-byte line of buf[0 .. buf_bytes) (buf
+ * 128-byte aligned, at most 2^32 lines), one request per 16-lane group
+ * and read, under one load form: policy 0 plain, 1 non-temporal, 2 relaxed
+ * agent-scope atomic, 3 relaxed system-scope atomic.  It stands for the
+ * scale reads of a quantized pool (page "feat(qsa): quantized KV pools
+ * with dequant-on-gather (fp8/int8/int4)", part 4: a slot's scales live in
+ * arrays of their own, so each listed slot's scale is a small read of a
+ * line the row read does not touch).  n_reads must be a positive multiple
+ * of 1024 (one workgroup per 1024 reads); workgroup i writes a fold of
+ * what it read to sink[i] (sink_words >= n_reads / 1024).  seed varies the
+ * lines.  One kernel launch on `stream`; returns 0, 1 for bad arguments
+ * (nothing launched), 2 when the launch failed.
  */
 #ifndef QSA_PROBE_H_
 #define QSA_PROBE_H_
@@ -32,6 +46,9 @@ int qsa_probe_gather(const void *k_pool, const void *v_pool, int64_t slot_stride
                      int64_t head_stride, int hkv, int row_bytes, const int32_t *sel,
                      int64_t n_sel, int64_t slots, int64_t per_wave, uint32_t *sink,
                      int64_t sink_words, hipStream_t stream);
+
+int qsa_probe_line_reads(const void *buf, int64_t buf_bytes, int64_t n_reads, int policy,
+                         uint32_t seed, uint32_t *sink, int64_t sink_words, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -106,7 +106,8 @@ def build_stamps(verbose: bool = False) -> str:
 
 
 def build_probe(verbose: bool = False) -> str:
-    """Build the measurement helper libqsa_probe.so (the bare gather)."""
+    """Build the measurement helper libqsa_probe.so (the bare gather and the
+    random line reads)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = PROBE_LIB + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, os.path.join(CSRC, "qsa_probe.hip")]

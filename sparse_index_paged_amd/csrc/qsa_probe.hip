@@ -67,6 +67,51 @@ __global__ void __launch_bounds__(256) probe_gather_kernel(const uint8_t *__rest
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
+// Random single-line reads: each 16-lane group reads the first 4 bytes of
+// kLineIters pseudo-random 128-byte lines of buf (one request per group and
+// read; lines from a 32-bit integer hash of (group, iteration, seed), taken
+// modulo the line count, so every address is inside buf).  POL picks the
+// load form: 0 plain, 1 non-temporal, 2 relaxed agent-scope atomic, 3
+// relaxed system-scope atomic.  What it answers: how many bytes the L2
+// fetches from memory for one small read of a line no other read touches --
+// the case of a quantized pool's scale read -- and whether a load form
+// changes that.
+constexpr int kLineIters = 64;
+
+__device__ __forceinline__ uint32_t line_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+
+template <int POL>
+__global__ void __launch_bounds__(256) probe_line_reads_kernel(const float *__restrict__ buf,
+                                                               uint32_t nlines, uint32_t seed,
+                                                               uint32_t *sink) {
+  const uint32_t grp = (blockIdx.x * 256u + threadIdx.x) >> 4;
+  float s = 0.f;
+#pragma unroll 8
+  for (int it = 0; it < kLineIters; ++it) {
+    const uint32_t line = line_hash(grp * 977u + static_cast<uint32_t>(it) * 0x9e3779b9u + seed) % nlines;
+    const float *ptr = buf + static_cast<uint64_t>(line) * 32u;
+    float x;
+    if constexpr (POL == 0) x = *ptr;
+    else if constexpr (POL == 1) x = __builtin_nontemporal_load(ptr);
+    else if constexpr (POL == 2) x = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else x = __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    s += x;
+  }
+  uint32_t x = __float_as_uint(s);
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 }  // namespace
 
 extern "C" int qsa_probe_gather(const void *k_pool, const void *v_pool, int64_t slot_stride,
@@ -92,6 +137,28 @@ extern "C" int qsa_probe_gather(const void *k_pool, const void *v_pool, int64_t 
     case 256: hipLaunchKernelGGL(probe_gather_kernel<16>, grid, block, 0, stream, k, v, slot_stride, head_stride, hkv, sel, n_sel, s32, per_wave, sink); break;
     case 128: hipLaunchKernelGGL(probe_gather_kernel<8>, grid, block, 0, stream, k, v, slot_stride, head_stride, hkv, sel, n_sel, s32, per_wave, sink); break;
     default: return 1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int qsa_probe_line_reads(const void *buf, int64_t buf_bytes, int64_t n_reads, int policy,
+                                    uint32_t seed, uint32_t *sink, int64_t sink_words,
+                                    hipStream_t stream) {
+  // one workgroup = 16 groups of 16 lanes, kLineIters reads each
+  constexpr int64_t kReadsPerBlock = 16 * kLineIters;
+  if (buf == nullptr || sink == nullptr || policy < 0 || policy > 3) return 1;
+  if (buf_bytes < 128 || buf_bytes / 128 > 0xFFFFFFFF || (reinterpret_cast<uintptr_t>(buf) & 127)) return 1;
+  if (n_reads < kReadsPerBlock || n_reads % kReadsPerBlock != 0) return 1;
+  const int64_t blocks = n_reads / kReadsPerBlock;
+  if (blocks > sink_words || blocks > 0x7FFFFFFF) return 1;
+  const auto *f = static_cast<const float *>(buf);
+  const uint32_t nlines = static_cast<uint32_t>(buf_bytes / 128);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  switch (policy) {
+    case 0: hipLaunchKernelGGL(probe_line_reads_kernel<0>, grid, block, 0, stream, f, nlines, seed, sink); break;
+    case 1: hipLaunchKernelGGL(probe_line_reads_kernel<1>, grid, block, 0, stream, f, nlines, seed, sink); break;
+    case 2: hipLaunchKernelGGL(probe_line_reads_kernel<2>, grid, block, 0, stream, f, nlines, seed, sink); break;
+    default: hipLaunchKernelGGL(probe_line_reads_kernel<3>, grid, block, 0, stream, f, nlines, seed, sink); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

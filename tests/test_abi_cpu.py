@@ -440,3 +440,28 @@ def test_pool_objects_refuse_reallocated_tensors():
     arrays["owner"].resize_(1 << 16)
     with pytest.raises(ValueError, match="reallocated"):
         tp.check()
+
+
+def test_probe_library_exports_what_its_header_declares():
+    """libqsa_probe.so (measurement helpers, include/qsa_probe.h) exports
+    exactly the calls its header declares, and its argument checks reject
+    bad calls on the host without a device."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qsa_probe.h")).read(), flags=re.S)
+    declared = set(re.findall(r"\b(qsa_probe_[a-z_]+)\s*\(", text))
+    assert declared == {"qsa_probe_gather", "qsa_probe_line_reads"}
+    path = os.path.join(os.path.dirname(qsa.lib_path()), "libqsa_probe.so")
+    nm = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                        check=True).stdout
+    assert set(re.findall(r"\bT (qsa_\w+)", nm)) == declared
+    lib = ctypes.CDLL(path)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.qsa_probe_line_reads
+    f.restype = ctypes.c_int
+    f.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_uint32, P, I64, P]
+    fake = ctypes.c_void_p(1 << 20)  # 128-byte aligned, never dereferenced on these paths
+    assert f(None, 1 << 20, 1024, 0, 1, fake, 1, None) == 1          # no buffer
+    assert f(fake, 1 << 20, 1024, 4, 1, fake, 1, None) == 1          # unknown load form
+    assert f(fake, 1 << 20, 1000, 0, 1, fake, 1, None) == 1          # not a multiple of 1024
+    assert f(fake, 1 << 20, 4096, 0, 1, fake, 3, None) == 1          # sink too small
+    assert f(fake, 64, 1024, 0, 1, fake, 1, None) == 1               # less than one line
+    assert f(ctypes.c_void_p((1 << 20) + 4), 1 << 20, 1024, 0, 1, fake, 1, None) == 1  # misaligned
