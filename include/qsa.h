@@ -394,8 +394,10 @@ qsa_status qsa_plan(int bs, int hkv, int *splits, int *workgroups);
 qsa_status qsa_set_option(const char *name, int64_t value);
 qsa_status qsa_get_option(const char *name, int64_t *value);
 
-/* Device pointer and count of the split counters (uint32, zero between
- * calls) of the workspace `stream` uses, for audits after a launch.  The
+/* Device pointer and count of the split-counter words (uint32, zero
+ * between calls) of the workspace `stream` uses, for audits after a launch.
+ * The counter of (row b, KV head g) is word (b * Hkv + g) * 32: one counter
+ * per 128-byte line, the words between them stay zero.  The
  * counters are the ones of page "fix(qsa): restore SM121 correctness with
  * Humanize and Kernel Design Agent", section "Optimized kernel": the final
  * split of a (row, KV head) resets its counter in the same launch, so every

@@ -175,7 +175,7 @@ struct DeviceWorkspaces {
 std::mutex g_ws_mutex;
 DeviceWorkspaces g_ws[kMaxDevices];
 
-constexpr int64_t kCtrWords = static_cast<int64_t>(qsa::kMaxBs) * 2;
+constexpr int64_t kCtrWords = static_cast<int64_t>(qsa::kMaxBs) * 2 * qsa::kCtrStride;
 
 int64_t part_floats_needed(int max_bs, int hkv) {
   int64_t worst = 0;

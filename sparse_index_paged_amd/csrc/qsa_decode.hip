@@ -1036,7 +1036,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(p.ctr + pair * kCtrStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == static_cast<uint32_t>(n_active - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -1154,7 +1154,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 #pragma unroll
   for (int k = 0; k < 3; ++k) store_out(4 * k + wv, acc_o[k], bcast(invj, 4 * k + wv));
   if (wv == 0 && lane < kGqa) lrow[lane * p.l_sh] = lse_of(M, ssum);
-  if (tid == 0) __hip_atomic_store(p.ctr + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(p.ctr + pair * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   phase_stamp(p, tid, 6);
 }
 

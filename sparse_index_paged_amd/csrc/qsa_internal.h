@@ -11,6 +11,9 @@ constexpr int kHeadDim = 256;
 constexpr int kGqa = 12;          // Q heads per KV head
 constexpr int kMaxSel = 2055;     // list entries per row
 constexpr int kMaxBs = 128;
+// Arrival counters sit one per 128-byte line: the device-scope adds of the
+// splits of different pairs then never meet at one line.
+constexpr int kCtrStride = 32;
 constexpr int kTile = 16;         // list entries per wave iteration
 
 // One split partial: m[16] and l[16] (log2 domain, 12 used) then the
@@ -91,7 +94,7 @@ struct Params {
   int min_split_keys;       // entries per split before another is used
   int xcc_lanes;            // bf16 placement from the workgroup's own XCD (decode_workgroups)
   float *part;              // [npairs][nsplit][kPartFloats]
-  uint32_t *ctr;            // [npairs], zero at rest
+  uint32_t *ctr;            // pair i's counter at ctr[i * kCtrStride], zero at rest
   uint32_t *err;            // sticky error word
 #ifdef QSA_PHASE_STAMPS
   uint64_t *stamps;         // [grid][kStampSlots] wall-clock stamps, or null
