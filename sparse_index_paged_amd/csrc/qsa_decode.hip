@@ -50,7 +50,9 @@
 //     of tile t+2D, rows of tile t+D.  Every lane dequantizes 16 channels of
 //     either tier into the same LDS place (an int4 lane loads the aligned
 //     16 bytes holding its 8 bytes), and the scales are staged per 32
-//     channels (a ring scale twice).
+//     channels (a ring scale twice).  With two waves per SIMD a wave raises
+//     its priority while it stages a tile and issues the next loads, so the
+//     dependent chain of slot ids, owner ids and rows advances first.
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
 //     one L2; with quantized pools all KV heads of a row share the XCD as
@@ -294,6 +296,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   // was slower for every format: the second wave covers the wait, and a
   // tiered pool's owner ids and tier selects take the registers)
   constexpr int D = (TIER || W > 4) ? 1 : 8 / NI;
+  constexpr bool kPrioStage = TIER && W > 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
@@ -828,6 +831,12 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int t = t0 + u;
+      // tiered pools, two waves per SIMD (8-wave workgroups): the wave that
+      // converts its rows and issues the next loads goes first.  Its row
+      // loads end a chain of dependent loads (slot ids, then owner ids, then
+      // rows), and this lets the chain advance before the other wave's
+      // products; the tile's own products then yield.
+      if constexpr (kPrioStage) __builtin_amdgcn_s_setprio(2);
       stage(u);
       if (t == 0) phase_stamp(p, tid, 2);
       if constexpr (TIER) {
@@ -842,6 +851,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         issue(u, snext[u]);
         fetch_slots(t + 2 * D, snext[u]);
       }
+      if constexpr (kPrioStage) __builtin_amdgcn_s_setprio(0);
       if (t < ntile) process(t);
     }
   }
