@@ -50,9 +50,13 @@
 //     of tile t+2D, rows of tile t+D.  Every lane dequantizes 16 channels of
 //     either tier into the same LDS place (an int4 lane loads the aligned
 //     16 bytes holding its 8 bytes), and the scales are staged per 32
-//     channels (a ring scale twice).  With two waves per SIMD a wave raises
-//     its priority while it stages a tile and issues the next loads, so the
-//     dependent chain of slot ids, owner ids and rows advances first.
+//     channels (a ring scale twice).
+//   * Wave priorities with two waves per SIMD: a tiered wave raises its
+//     priority while it stages a tile and issues the next loads, so the
+//     dependent chain of slot ids, owner ids and rows advances first.  An
+//     int4 wave raises its priority for the tile's products instead, so
+//     their dependent chain goes first and the other wave's unpacking
+//     fills the gaps.
 //   * All splits of one (row, KV head) are given workgroup ids congruent mod
 //     8, so they are dispatched to the same XCD and their partials stay in
 //     one L2; with quantized pools all KV heads of a row share the XCD as
@@ -296,7 +300,9 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   // was slower for every format: the second wave covers the wait, and a
   // tiered pool's owner ids and tier selects take the registers)
   constexpr int D = (TIER || W > 4) ? 1 : 8 / NI;
+  // wave priorities with two waves per SIMD (8-wave workgroups), see the loop
   constexpr bool kPrioStage = TIER && W > 4;
+  constexpr bool kPrioProcess = FMT == kFmtINT4 && !TIER && W > 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
@@ -852,7 +858,13 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         fetch_slots(t + 2 * D, snext[u]);
       }
       if constexpr (kPrioStage) __builtin_amdgcn_s_setprio(0);
+      // int4 pools, two waves per SIMD: a tile's products go first.  Their
+      // chain of dependent steps (QK products, group scales, softmax, P
+      // splits, PV products) then keeps moving, and the other wave's
+      // unpacking, which depends on nothing in flight, fills the gaps.
+      if constexpr (kPrioProcess) __builtin_amdgcn_s_setprio(1);
       if (t < ntile) process(t);
+      if constexpr (kPrioProcess) __builtin_amdgcn_s_setprio(0);
     }
   }
   // the last group: its rows are in flight already and nothing more is
