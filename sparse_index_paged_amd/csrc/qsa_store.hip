@@ -41,7 +41,17 @@
 namespace qsa {
 namespace {
 
-constexpr int kRowsPerWave = 4;
+// Rows (token, KV head) per wave: one for quantized pools without a ring
+// (the most waves in flight); two for bf16 rows and for ring writes.  A
+// ring write needs both KV heads of a token in one wave, because the
+// token's claim is tested for both before either clears it (rows 2t and
+// 2t + 1 share a wave when the count is even).  Every store to a pool is
+// non-temporal: the rows are not read back by this launch, and streaming
+// them past the L2 measured faster for every format.
+template <int FMT>
+constexpr int store_rows_per_wave(bool ring) {
+  return (FMT == kFmtBF16 || ring) ? 2 : 1;
+}
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
@@ -57,7 +67,7 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.
 // x / sc rounded once (the IEEE quotient), 0 for a zero scale
 __device__ __forceinline__ float quotient(float x, float sc) { return sc > 0.f ? __fdiv_rn(x, sc) : 0.f; }
 
-template <int FMT>
+template <int FMT, int kRowsPerWave>
 __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -109,7 +119,10 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
     }
     uint8_t *dst = is_v ? p.vp + s * p.vp_ss + h * p.vp_sh : p.kp + s * p.kp_ss + h * p.kp_sh;
     if constexpr (FMT == kFmtBF16) {
-      reinterpret_cast<uint4 *>(dst)[l] = raw[i];
+      __builtin_nontemporal_store(raw[i].x, reinterpret_cast<uint32_t *>(dst) + 4 * l);
+      __builtin_nontemporal_store(raw[i].y, reinterpret_cast<uint32_t *>(dst) + 4 * l + 1);
+      __builtin_nontemporal_store(raw[i].z, reinterpret_cast<uint32_t *>(dst) + 4 * l + 2);
+      __builtin_nontemporal_store(raw[i].w, reinterpret_cast<uint32_t *>(dst) + 4 * l + 3);
     } else {
       const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
       float x[8];
@@ -130,9 +143,9 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
         uint8_t *sd = is_v ? p.vs + s * p.vs_ss + h * p.vs_sh : p.ks + s * p.ks_ss + h * p.ks_sh;
         const int gi = l / lpg;
         if (p.scale_f16)
-          reinterpret_cast<_Float16 *>(sd)[gi] = static_cast<_Float16>(sc);
+          __builtin_nontemporal_store(static_cast<_Float16>(sc), reinterpret_cast<_Float16 *>(sd) + gi);
         else
-          reinterpret_cast<float *>(sd)[gi] = sc;
+          __builtin_nontemporal_store(sc, reinterpret_cast<float *>(sd) + gi);
       }
       // Codes from y = x * rcp(sc), within 2 ulp of the IEEE quotient x / sc;
       // only where that could change a code is the quotient itself taken.
@@ -177,12 +190,13 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) packed |= c[e] << (4 * e);
-        reinterpret_cast<uint32_t *>(dst)[l] = packed;
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(dst) + l);
       } else {
         uint2 out;
         out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
         out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-        reinterpret_cast<uint2 *>(dst)[l] = out;
+        __builtin_nontemporal_store(out.x, reinterpret_cast<uint32_t *>(dst) + 2 * l);
+        __builtin_nontemporal_store(out.y, reinterpret_cast<uint32_t *>(dst) + 2 * l + 1);
       }
     }
   }
@@ -206,16 +220,25 @@ hipError_t launch_claim(const StoreParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT>
+void launch_store_fmt(const StoreParams &p, int64_t rows, hipStream_t stream) {
+  const bool ring = p.claim != nullptr;
+  const int64_t per_block = 4 * store_rows_per_wave<FMT>(ring);
+  const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
+  if (store_rows_per_wave<FMT>(ring) == 2)
+    hipLaunchKernelGGL((qsa_store_kernel<FMT, 2>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((qsa_store_kernel<FMT, 1>), grid, dim3(256), 0, stream, p);
+}
+
 hipError_t launch_store(const StoreParams &p, int fmt, hipStream_t stream) {
   const int64_t rows = p.n * p.hkv;
   if (rows <= 0) return hipSuccess;
-  const int64_t per_block = 4 * kRowsPerWave;
-  const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
   switch (fmt) {
-    case kFmtBF16: hipLaunchKernelGGL(qsa_store_kernel<kFmtBF16>, grid, dim3(256), 0, stream, p); break;
-    case kFmtFP8: hipLaunchKernelGGL(qsa_store_kernel<kFmtFP8>, grid, dim3(256), 0, stream, p); break;
-    case kFmtINT8: hipLaunchKernelGGL(qsa_store_kernel<kFmtINT8>, grid, dim3(256), 0, stream, p); break;
-    case kFmtINT4: hipLaunchKernelGGL(qsa_store_kernel<kFmtINT4>, grid, dim3(256), 0, stream, p); break;
+    case kFmtBF16: launch_store_fmt<kFmtBF16>(p, rows, stream); break;
+    case kFmtFP8: launch_store_fmt<kFmtFP8>(p, rows, stream); break;
+    case kFmtINT8: launch_store_fmt<kFmtINT8>(p, rows, stream); break;
+    case kFmtINT4: launch_store_fmt<kFmtINT4>(p, rows, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
