@@ -51,7 +51,7 @@
 //     either tier into the same LDS place (an int4 lane loads the aligned
 //     16 bytes holding its 8 bytes), and the scales are staged per 32
 //     channels (a ring scale twice).
-//   * Wave priorities with two waves per SIMD: a tiered wave raises its
+//   * Wave priorities for two waves on a SIMD: a tiered wave raises its
 //     priority while it stages a tile and issues the next loads, so the
 //     dependent chain of slot ids, owner ids and rows advances first.  An
 //     int4 wave raises its priority for the tile's products instead, so
@@ -300,9 +300,10 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
   // was slower for every format: the second wave covers the wait, and a
   // tiered pool's owner ids and tier selects take the registers)
   constexpr int D = (TIER || W > 4) ? 1 : 8 / NI;
-  // wave priorities with two waves per SIMD (8-wave workgroups), see the loop
-  constexpr bool kPrioStage = TIER && W > 4;
-  constexpr bool kPrioProcess = FMT == kFmtINT4 && !TIER && W > 4;
+  // wave priorities, which order two waves of a SIMD (8-wave workgroups, or
+  // two 4-wave workgroups on a CU); see the loop
+  constexpr bool kPrioStage = TIER;
+  constexpr bool kPrioProcess = FMT == kFmtINT4 && !TIER;
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS::kBytes];
   __shared__ int s_last;
@@ -837,8 +838,8 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int t = t0 + u;
-      // tiered pools, two waves per SIMD (8-wave workgroups): the wave that
-      // converts its rows and issues the next loads goes first.  Its row
+      // tiered pools, two waves on a SIMD: the wave that converts its rows
+      // and issues the next loads goes first.  Its row
       // loads end a chain of dependent loads (slot ids, then owner ids, then
       // rows), and this lets the chain advance before the other wave's
       // products; the tile's own products then yield.
@@ -858,7 +859,7 @@ __global__ void __launch_bounds__(64 * W, 8 / W)
         fetch_slots(t + 2 * D, snext[u]);
       }
       if constexpr (kPrioStage) __builtin_amdgcn_s_setprio(0);
-      // int4 pools, two waves per SIMD: a tile's products go first.  Their
+      // int4 pools, two waves on a SIMD: a tile's products go first.  Their
       // chain of dependent steps (QK products, group scales, softmax, P
       // splits, PV products) then keeps moving, and the other wave's
       // unpacking, which depends on nothing in flight, fills the gaps.
