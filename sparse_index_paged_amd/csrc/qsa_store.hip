@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
   const bool is_v = lane >= 32;
   const int l = lane & 31;
 
-  // ---- all loads of the wave's rows first (with a ring, also the claims:
+  // ---- all loads of the wave's rows first (with a ring, the claims first:
   // every claim this wave tests is read before it clears any)
   uint4 raw[kRowsPerWave];
   int64_t slot[kRowsPerWave];
@@ -90,9 +90,28 @@ __global__ void __launch_bounds__(256) qsa_store_kernel(const StoreParams p) {
       const int h = static_cast<int>(row - t * p.hkv);
       slot[i] = p.loc_i64 ? static_cast<const int64_t *>(p.loc)[t]
                           : static_cast<int64_t>(static_cast<const int32_t *>(p.loc)[t]);
-      const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
-      raw[i] = reinterpret_cast<const uint4 *>(src)[l];
-      if (ring) claim[i] = p.claim[static_cast<uint32_t>(slot[i]) & p.ring_mask];
+      if (ring) {
+        claim[i] = p.claim[static_cast<uint32_t>(slot[i]) & p.ring_mask];
+      } else {
+        const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
+        raw[i] = reinterpret_cast<const uint4 *>(src)[l];
+      }
+    }
+  }
+  // a ring write reads only the rows of the tokens that hold their claim
+  // (one token per ring row): the others' rows are never loaded
+  if (ring) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t row = row0 + i;
+      if (row < nrows) {
+        const int64_t t = (p.hkv == 2) ? (row >> 1) : row;
+        const int h = static_cast<int>(row - t * p.hkv);
+        if (claim[i] == static_cast<int32_t>(t + 1)) {
+          const __bf16 *src = is_v ? p.v + t * p.v_st + h * p.v_sh : p.k + t * p.k_st + h * p.k_sh;
+          raw[i] = reinterpret_cast<const uint4 *>(src)[l];
+        }
+      }
     }
   }
 
