@@ -22,11 +22,13 @@
 // the owner table and clears its claim (so the claim table is zero again
 // when the call ends).
 //
-// Mapping: a wave handles 4 consecutive (token, kv head) rows; lanes 0..31
-// work on the K rows and lanes 32..63 on the V rows, 8 channels (one
-// 16-byte load) per lane, and all loads of the 4 rows are issued before the
-// first row is processed.  The absmax of a group of G channels is a
-// butterfly over G/8 lanes.
+// Mapping: a wave handles one (token, kv head) row of a quantized pool, or
+// two consecutive rows for bf16 pools and ring writes
+// (store_rows_per_wave).  Lanes 0..31 work on the K row and lanes 32..63 on
+// the V row, 8 channels (one 16-byte load) per lane, and all loads of the
+// wave's rows are issued before the first row is processed.  The absmax of
+// a group of G channels is a butterfly over G/8 lanes.  Codes, scales and
+// bf16 rows go to the pools with non-temporal stores.
 //
 // x / scale must be the correctly rounded fp32 quotient, because the codes
 // round it once more.  The quotient is first taken as x * rcp(scale)
